@@ -1,0 +1,181 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule library (libgdn.so).
+ *
+ * The method: the Gated DeltaNet recurrence (Yang, Kautz, Hatamizadeh, "Gated
+ * Delta Networks", ICLR 2025), whose kernels the pages name gated_delta_rule_*
+ * (ssm_gdn_tc_route.rs, module doc and the spine entry constants):
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t,
+ *
+ * with alpha_t = exp(log_g_t) (log_g <= 0), no scale on q, and S_t a dv x dk
+ * matrix per (sequence, v-head).  States cross this ABI as h = S^T: dk rows of
+ * dv fp32 values, row-major ("dk*dv fp32 per head", ssm_gdn_woa.rs, the
+ * shared-memory size of the verify launch).  V-head vh reads k-head
+ * vh / (Hv / Hk) (ssm_ba_gates_hopper.rs, the v-head grouping of its index model).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (the caller allocates them; the
+ *    library never allocates, frees or synchronises).  h_table/hi_tables are
+ *    device arrays of device pointers.
+ *  - Shapes and pointers are validated on the host before anything is
+ *    launched; a refusal returns a named status (gdn_status_string) and
+ *    launches nothing.  A refused fast path is never silent: either the
+ *    generic kernel runs and gdn_last_route() names it, or an error returns.
+ *  - Work is enqueued on `stream` and the call returns without waiting.
+ *  - Floating-point inputs are read as given; bf16 values are widened exactly.
+ *  - Entry points are reentrant and thread-safe; gdn_last_route() is
+ *    thread-local.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of q/k/v (io_dtype) and of the output (out_dtype). */
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Return codes.  0 = success; every refusal has its own code and text. */
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,          /* a required pointer is NULL */
+    GDN_ERR_SHAPE = 2,         /* B < 1, T < 0, a head count, dk, dv or chunk < 1 */
+    GDN_ERR_HEAD_GROUPS = 3,   /* Hv is not a multiple of Hk */
+    GDN_ERR_DIM_LIMIT = 4,     /* dk or dv > 128, or chunk > 64: no kernel here takes it */
+    GDN_ERR_DTYPE = 5,         /* unknown dtype code */
+    GDN_ERR_WORKSPACE = 6,     /* workspace smaller than gdn_prefill_workspace_bytes() */
+    GDN_ERR_STASH = 7,         /* stash_seq_floats smaller than gdn_stash_seq_floats() */
+    GDN_ERR_K_ROWS = 8,        /* k_rows is not 4 */
+    GDN_ERR_STRIDE = 9,        /* a row stride shorter than the heads it must hold */
+    GDN_ERR_UNSUPPORTED = 10,  /* a documented branch that this library does not build */
+    GDN_ERR_HIP = 11           /* the HIP runtime refused a launch (text: gdn_last_route()) */
+} gdn_status;
+
+/* Static text naming a status.  Never NULL. */
+const char* gdn_status_string(int status);
+
+/* Thread-local text of the last call on this thread: the kernel entry that
+ * was launched (or would be, for the *_plan functions), its grid, block and
+ * LDS bytes, or the reason for a refusal.  Never NULL; valid until the next
+ * call on the same thread. */
+const char* gdn_last_route(void);
+
+/* ------------------------------------------------------------------------ */
+/* Chunked prefill.
+ *
+ * The pages' "state spine" (ssm_gdn_tc_route.rs, doc of the spine entry
+ * constants): sequences are cut into chunks of `chunk` tokens; inside a chunk
+ * the delta rule is solved in closed form (WY/UT form: T = (I + A)^-1 with
+ * A = strict_lower(diag(beta) (Gamma o K K^T)), U = T diag(beta) V,
+ * W = T diag(beta gamma) K) and the fp32 state walks the chunks in order,
+ * h <- gamma_L h + K~^T (U - W h) ("h stays f32", same page, the route line
+ * of the tensor-core spine), while each chunk's outputs are
+ * O = diag(gamma) Q h + (lower_incl(Q K^T) o Gamma)(U - W h).
+ *
+ * Layouts (row-major, element strides implied by the shapes):
+ *   dense  (cu_seqlens == NULL): q, k [B][T][Hk][dk];  v, out [B][T][Hv][dv];
+ *                                log_g, beta [B][T][Hv]
+ *   packed (cu_seqlens != NULL): the B sequences' rows concatenated, T = total
+ *                                rows: q, k [T][Hk][dk]; v, out [T][Hv][dv];
+ *                                log_g, beta [T][Hv]; cu_seqlens: device int32
+ *                                [B+1], cu[0] = 0, non-decreasing, cu[B] = T
+ *                                (values outside [0, T] are clamped into it).
+ *   h0, h_final: [B][Hv][dk][dv] fp32.  h0 == NULL means zero states;
+ *   h_final == NULL means the final states are not written; h0 == h_final is
+ *   allowed (updated in place).  q, k, v: io_dtype; out: out_dtype; log_g
+ *   (natural log of the decay, <= 0) and beta: fp32.
+ *   Precondition: within any chunk the sum of log_g stays above -80.
+ *
+ * Kernels: io_dtype == GDN_BF16 with dk == dv == 128 and chunk == 64 runs the
+ * bf16-MFMA spine (fp32 state and accumulators).  Every other accepted shape
+ * runs the generic fp32-arithmetic chunked kernel (dk, dv <= 128, chunk <= 64).
+ * gdn_last_route() names the one that ran.
+ * workspace: device scratch of at least gdn_prefill_workspace_bytes() bytes
+ * (may be NULL when that is 0).
+ */
+size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                                   int io_dtype);
+
+int gdn_chunk_prefill(const void* q, const void* k, const void* v,
+                      const float* log_g, const float* beta,
+                      const float* h0, void* out, float* h_final,
+                      int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                      const int32_t* cu_seqlens, int io_dtype, int out_dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Validation and kernel choice of gdn_chunk_prefill without launching
+ * anything: same return codes; gdn_last_route() holds the route.  Pointers are
+ * only compared with NULL. */
+int gdn_chunk_prefill_plan(const void* q, const void* k, const void* v,
+                           const float* log_g, const float* beta,
+                           const float* h0, void* out, float* h_final,
+                           int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                           const int32_t* cu_seqlens, int io_dtype, int out_dtype,
+                           void* workspace, size_t workspace_bytes);
+
+/* ------------------------------------------------------------------------ */
+/* K = 4 write-on-accept decode verify, its fold, and the engaged word
+ * (ssm_gdn_woa.rs: docs of gdn_decode_wy4_woa, gdn_wy4_fold and
+ * gdn_wy4_flag_clear).  Protocol, on one stream: gdn_flag_clear, then
+ * gdn_decode_verify_k4 (writes outputs and the stash, marks the word, writes
+ * NO state), then the caller writes na_tab, then gdn_fold (if the word is
+ * set, applies the first na_tab[b] stashed rows to each state, reading and
+ * writing it once).
+ *
+ * Verify rows: row r (0..3) of sequence b is global row b*4 + r.
+ *   q, k : row at q + (b*4 + r)*qk_stride, k-head kh at + kh*dk   (io_dtype)
+ *   v    : row at v + (b*4 + r)*v_stride,  v-head vh at + vh*dv   (io_dtype)
+ *   gate, beta: fp32 at (b*4 + r)*gb_stride + vh; gate is log-space like log_g
+ *   out  : dense [B][4][Hv][dv] (out_dtype)
+ *   h_table[b]: device pointer to sequence b's states [Hv][dk][dv] fp32
+ *   stash: sequence b at stash + b*stash_seq_floats; per v-head vh, at
+ *          vh*(4*dv + 4 + kfl) floats: delta [4][dv] fp32, G [4] fp32 (the
+ *          within-verify cumulative log decay), then the 4 keys [4][dk] as
+ *          kfl = 4*dk floats (fp32 io) or 2*dk floats of packed bf16 bits (bf16
+ *          io).  The fold receives no q/k/v/gate, so the stash carries them.
+ *   engaged_flag: one device uint32; verify sets it to 1.
+ * Fold:
+ *   na_tab: device int32 [B], accepted rows per sequence, clamped to 0..4;
+ *           na = 0 leaves the state's bytes unchanged.
+ *   hi_tables / slab_entries: the restore branch of a non-write-on-accept
+ *           verify (word not set).  Not built here: hi_tables must be NULL,
+ *           and with the word clear the fold changes nothing.
+ *   k_rows: must be 4.
+ */
+size_t gdn_stash_seq_floats(int Hv, int dk, int dv, int k_rows, int io_dtype);
+
+int gdn_flag_clear(uint32_t* engaged_flag, hipStream_t stream);
+
+int gdn_decode_verify_k4(float* const* h_table, const void* q, const void* k, const void* v,
+                         const float* gate, const float* beta, void* out, float* stash,
+                         int B, int Hk, int Hv, int dk, int dv,
+                         int qk_stride, int v_stride, int gb_stride, int stash_seq_floats,
+                         uint32_t* engaged_flag, int io_dtype, int out_dtype, hipStream_t stream);
+
+int gdn_fold(float* const* h_table, const float* stash, const int32_t* na_tab,
+             float* const* hi_tables, int slab_entries, const uint32_t* engaged_flag,
+             int k_rows, int B, int Hk, int Hv, int dk, int dv, int stash_seq_floats,
+             int io_dtype, hipStream_t stream);
+
+/* Validation of the two calls above without launching (same return codes). */
+int gdn_decode_verify_k4_plan(float* const* h_table, const void* q, const void* k,
+                              const void* v, const float* gate, const float* beta, void* out,
+                              float* stash, int B, int Hk, int Hv, int dk, int dv,
+                              int qk_stride, int v_stride, int gb_stride, int stash_seq_floats,
+                              uint32_t* engaged_flag, int io_dtype, int out_dtype);
+
+int gdn_fold_plan(float* const* h_table, const float* stash, const int32_t* na_tab,
+                  float* const* hi_tables, int slab_entries, const uint32_t* engaged_flag,
+                  int k_rows, int B, int Hk, int Hv, int dk, int dv, int stash_seq_floats,
+                  int io_dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

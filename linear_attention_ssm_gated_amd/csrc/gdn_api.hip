@@ -1,0 +1,298 @@
+// C ABI of libgdn.so (declared in include/gdn.h): host-side validation that
+// names every refusal, the kernel choice, the route line, and the launches.
+//
+// The route line follows the pages' rule that a log must name the entry that
+// actually launched, with its geometry (ssm_gdn_tc_route.rs, the route-line
+// functions and their tests), and that a fast path refused by a shape guard
+// names the guard (ssm_ba_gates_hopper.rs, doc of its reject function).
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+namespace {
+
+thread_local char t_route[512] = "no call yet";
+
+void set_route(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void set_route(const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(t_route, sizeof(t_route), fmt, ap);
+    va_end(ap);
+}
+
+int refuse(int status, const char* who, const char* why)
+{
+    set_route("%s refused: %s (%s)", who, gdn_status_string(status), why);
+    return status;
+}
+
+bool bad_dtype(int d) { return d != GDN_F32 && d != GDN_BF16; }
+
+void route_geometry(const gdn::Geometry& g, const char* note)
+{
+    set_route("%s grid=[%u,%u,%u] block=%u lds=%uB%s%s", g.entry, g.grid[0], g.grid[1], g.grid[2],
+              g.block, g.lds_bytes, note && *note ? " " : "", note ? note : "");
+}
+
+// Validation shared by gdn_chunk_prefill and its plan.  On success *mfma tells
+// which kernel runs and *why names the guard that sent it to the generic one.
+int check_prefill(const gdn::PrefillArgs& a, bool* mfma, const char** why)
+{
+    const char* who = "gdn_chunk_prefill";
+    if (bad_dtype(a.io_dtype) || bad_dtype(a.out_dtype))
+        return refuse(GDN_ERR_DTYPE, who, "io_dtype/out_dtype must be GDN_F32 or GDN_BF16");
+    if (a.B < 1 || a.T < 0 || a.Hk < 1 || a.Hv < 1 || a.dk < 1 || a.dv < 1 || a.chunk < 1)
+        return refuse(GDN_ERR_SHAPE, who, "need B, Hk, Hv, dk, dv, chunk >= 1 and T >= 0");
+    if (a.B > 65535)
+        return refuse(GDN_ERR_SHAPE, who, "B > 65535 (grid y limit)");
+    if (a.Hv % a.Hk != 0)
+        return refuse(GDN_ERR_HEAD_GROUPS, who, "Hv must be a multiple of Hk");
+    if (a.dk > 128 || a.dv > 128 || a.chunk > 64)
+        return refuse(GDN_ERR_DIM_LIMIT, who, "dk, dv <= 128 and chunk <= 64");
+    if (a.T > 0 && (!a.q || !a.k || !a.v || !a.log_g || !a.beta || !a.out))
+        return refuse(GDN_ERR_NULL, who, "q, k, v, log_g, beta and out are required when T > 0");
+    const size_t need = gdn_prefill_workspace_bytes(a.B, a.T, a.Hk, a.Hv, a.dk, a.dv, a.chunk, a.io_dtype);
+    if (need > 0 && (!a.workspace || a.workspace_bytes < need))
+        return refuse(GDN_ERR_WORKSPACE, who, "workspace smaller than gdn_prefill_workspace_bytes()");
+    *why = "";
+    if (a.io_dtype != GDN_BF16) *why = "(generic: io dtype is f32; the MFMA spine takes bf16)";
+    else if (a.dk != 128 || a.dv != 128) *why = "(generic: the MFMA spine takes dk = dv = 128)";
+    else if (a.chunk != 64) *why = "(generic: the MFMA spine takes chunk = 64)";
+    *mfma = gdn::prefill_mfma_accepts(a) && !**why;
+    if (!*mfma && !**why) *why = "(generic: MFMA spine not built)";
+    return GDN_OK;
+}
+
+int check_verify(const gdn::VerifyArgs& a)
+{
+    const char* who = "gdn_decode_verify_k4";
+    if (bad_dtype(a.io_dtype) || bad_dtype(a.out_dtype))
+        return refuse(GDN_ERR_DTYPE, who, "io_dtype/out_dtype must be GDN_F32 or GDN_BF16");
+    if (!a.h_table || !a.stash || !a.engaged_flag)
+        return refuse(GDN_ERR_NULL, who, "null table/stash/flag");
+    if (!a.q || !a.k || !a.v || !a.gate || !a.beta || !a.out)
+        return refuse(GDN_ERR_NULL, who, "q, k, v, gate, beta and out are required");
+    if (a.B < 1 || a.Hk < 1 || a.Hv < 1 || a.dk < 1 || a.dv < 1)
+        return refuse(GDN_ERR_SHAPE, who, "need B, Hk, Hv, dk, dv >= 1");
+    if (a.B > 65535) return refuse(GDN_ERR_SHAPE, who, "B > 65535 (grid y limit)");
+    if (a.Hv % a.Hk != 0) return refuse(GDN_ERR_HEAD_GROUPS, who, "Hv must be a multiple of Hk");
+    if (a.dk > 128 || a.dv > 128 || a.dv % 4 != 0)
+        return refuse(GDN_ERR_DIM_LIMIT, who, "dk <= 128, dv <= 128 and dv a multiple of 4");
+    if ((long)a.qk_stride < (long)a.Hk * a.dk || (long)a.v_stride < (long)a.Hv * a.dv ||
+        (long)a.gb_stride < (long)a.Hv)
+        return refuse(GDN_ERR_STRIDE, who, "a row stride is shorter than its row");
+    if ((size_t)a.stash_seq_floats < gdn_stash_seq_floats(a.Hv, a.dk, a.dv, 4, a.io_dtype))
+        return refuse(GDN_ERR_STASH, who, "stash_seq_floats < gdn_stash_seq_floats()");
+    return GDN_OK;
+}
+
+int check_fold(const gdn::FoldArgs& a, float* const* hi_tables, int k_rows)
+{
+    const char* who = "gdn_fold";
+    if (bad_dtype(a.io_dtype)) return refuse(GDN_ERR_DTYPE, who, "io_dtype must be GDN_F32 or GDN_BF16");
+    if (k_rows != 4) return refuse(GDN_ERR_K_ROWS, who, "k_rows must be 4");
+    if (hi_tables)
+        return refuse(GDN_ERR_UNSUPPORTED, who, "the restore branch of a non-write-on-accept verify is not built; pass hi_tables = NULL");
+    if (!a.h_table || !a.stash || !a.na_tab || !a.engaged_flag)
+        return refuse(GDN_ERR_NULL, who, "null table/stash/na_tab/flag");
+    if (a.B < 1 || a.Hk < 1 || a.Hv < 1 || a.dk < 1 || a.dv < 1)
+        return refuse(GDN_ERR_SHAPE, who, "need B, Hk, Hv, dk, dv >= 1");
+    if (a.B > 65535) return refuse(GDN_ERR_SHAPE, who, "B > 65535 (grid y limit)");
+    if (a.Hv % a.Hk != 0) return refuse(GDN_ERR_HEAD_GROUPS, who, "Hv must be a multiple of Hk");
+    if (a.dk > 128 || a.dv > 128 || a.dv % 4 != 0)
+        return refuse(GDN_ERR_DIM_LIMIT, who, "dk <= 128, dv <= 128 and dv a multiple of 4");
+    if ((size_t)a.stash_seq_floats < gdn_stash_seq_floats(a.Hv, a.dk, a.dv, 4, a.io_dtype))
+        return refuse(GDN_ERR_STASH, who, "stash_seq_floats < gdn_stash_seq_floats()");
+    return GDN_OK;
+}
+
+int launched(hipError_t e)
+{
+    if (e == hipSuccess) return GDN_OK;
+    size_t n = strlen(t_route);
+    snprintf(t_route + n, sizeof(t_route) - n, " -- launch failed: %s", hipGetErrorString(e));
+    return GDN_ERR_HIP;
+}
+
+gdn::PrefillArgs make_prefill(const void* q, const void* k, const void* v, const float* log_g,
+                              const float* beta, const float* h0, void* out, float* h_final, int B,
+                              int T, int Hk, int Hv, int dk, int dv, int chunk,
+                              const int32_t* cu_seqlens, int io_dtype, int out_dtype,
+                              void* workspace, size_t workspace_bytes)
+{
+    gdn::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta; a.h0 = h0; a.out = out;
+    a.h_final = h_final; a.B = B; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv;
+    a.chunk = chunk; a.cu_seqlens = cu_seqlens; a.io_dtype = io_dtype; a.out_dtype = out_dtype;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(int status)
+{
+    switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: a size is out of range";
+    case GDN_ERR_HEAD_GROUPS: return "GDN_ERR_HEAD_GROUPS: Hv is not a multiple of Hk";
+    case GDN_ERR_DIM_LIMIT: return "GDN_ERR_DIM_LIMIT: dk, dv or chunk beyond what any kernel takes";
+    case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unknown dtype code";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace too small";
+    case GDN_ERR_STASH: return "GDN_ERR_STASH: stash_seq_floats too small";
+    case GDN_ERR_K_ROWS: return "GDN_ERR_K_ROWS: k_rows must be 4";
+    case GDN_ERR_STRIDE: return "GDN_ERR_STRIDE: a row stride is shorter than its row";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: branch not built";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP: the HIP runtime refused a launch";
+    default: return "unknown gdn status";
+    }
+}
+
+const char* gdn_last_route(void) { return t_route; }
+
+size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                                   int io_dtype)
+{
+    (void)B; (void)T; (void)Hk; (void)Hv; (void)dk; (void)dv; (void)chunk; (void)io_dtype;
+    return 0;  // both prefill kernels keep their intermediates on chip
+}
+
+int gdn_chunk_prefill_plan(const void* q, const void* k, const void* v, const float* log_g,
+                           const float* beta, const float* h0, void* out, float* h_final, int B,
+                           int T, int Hk, int Hv, int dk, int dv, int chunk,
+                           const int32_t* cu_seqlens, int io_dtype, int out_dtype,
+                           void* workspace, size_t workspace_bytes)
+{
+    gdn::PrefillArgs a = make_prefill(q, k, v, log_g, beta, h0, out, h_final, B, T, Hk, Hv, dk, dv,
+                                      chunk, cu_seqlens, io_dtype, out_dtype, workspace,
+                                      workspace_bytes);
+    bool mfma = false;
+    const char* why = "";
+    int st = check_prefill(a, &mfma, &why);
+    if (st != GDN_OK) return st;
+    route_geometry(mfma ? gdn::prefill_mfma_geometry(a) : gdn::prefill_generic_geometry(a), why);
+    return GDN_OK;
+}
+
+int gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* log_g,
+                      const float* beta, const float* h0, void* out, float* h_final, int B, int T,
+                      int Hk, int Hv, int dk, int dv, int chunk, const int32_t* cu_seqlens,
+                      int io_dtype, int out_dtype, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream)
+{
+    gdn::PrefillArgs a = make_prefill(q, k, v, log_g, beta, h0, out, h_final, B, T, Hk, Hv, dk, dv,
+                                      chunk, cu_seqlens, io_dtype, out_dtype, workspace,
+                                      workspace_bytes);
+    bool mfma = false;
+    const char* why = "";
+    int st = check_prefill(a, &mfma, &why);
+    if (st != GDN_OK) return st;
+    route_geometry(mfma ? gdn::prefill_mfma_geometry(a) : gdn::prefill_generic_geometry(a), why);
+    return launched(mfma ? gdn::launch_prefill_mfma(a, stream) : gdn::launch_prefill_generic(a, stream));
+}
+
+size_t gdn_stash_seq_floats(int Hv, int dk, int dv, int k_rows, int io_dtype)
+{
+    if (Hv < 1 || dk < 1 || dv < 1 || k_rows != 4) return 0;
+    return (size_t)Hv * gdn::stash_head_floats(dk, dv, io_dtype == GDN_BF16 ? 1 : 0);
+}
+
+int gdn_flag_clear(uint32_t* engaged_flag, hipStream_t stream)
+{
+    if (!engaged_flag) return refuse(GDN_ERR_NULL, "gdn_flag_clear", "null flag");
+    route_geometry(gdn::flag_clear_geometry(), "");
+    return launched(gdn::launch_flag_clear(engaged_flag, stream));
+}
+
+static gdn::VerifyArgs make_verify(float* const* h_table, const void* q, const void* k, const void* v,
+                                   const float* gate, const float* beta, void* out, float* stash,
+                                   int B, int Hk, int Hv, int dk, int dv, int qk_stride,
+                                   int v_stride, int gb_stride, int stash_seq_floats,
+                                   uint32_t* engaged_flag, int io_dtype, int out_dtype)
+{
+    gdn::VerifyArgs a;
+    a.h_table = h_table; a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta; a.out = out;
+    a.stash = stash; a.B = B; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.qk_stride = qk_stride;
+    a.v_stride = v_stride; a.gb_stride = gb_stride; a.stash_seq_floats = stash_seq_floats;
+    a.engaged_flag = engaged_flag; a.io_dtype = io_dtype; a.out_dtype = out_dtype;
+    return a;
+}
+
+int gdn_decode_verify_k4_plan(float* const* h_table, const void* q, const void* k, const void* v,
+                              const float* gate, const float* beta, void* out, float* stash, int B,
+                              int Hk, int Hv, int dk, int dv, int qk_stride, int v_stride,
+                              int gb_stride, int stash_seq_floats, uint32_t* engaged_flag,
+                              int io_dtype, int out_dtype)
+{
+    gdn::VerifyArgs a = make_verify(h_table, q, k, v, gate, beta, out, stash, B, Hk, Hv, dk, dv,
+                                    qk_stride, v_stride, gb_stride, stash_seq_floats, engaged_flag,
+                                    io_dtype, out_dtype);
+    int st = check_verify(a);
+    if (st != GDN_OK) return st;
+    route_geometry(gdn::verify_geometry(a), "");
+    return GDN_OK;
+}
+
+int gdn_decode_verify_k4(float* const* h_table, const void* q, const void* k, const void* v,
+                         const float* gate, const float* beta, void* out, float* stash, int B,
+                         int Hk, int Hv, int dk, int dv, int qk_stride, int v_stride, int gb_stride,
+                         int stash_seq_floats, uint32_t* engaged_flag, int io_dtype, int out_dtype,
+                         hipStream_t stream)
+{
+    gdn::VerifyArgs a = make_verify(h_table, q, k, v, gate, beta, out, stash, B, Hk, Hv, dk, dv,
+                                    qk_stride, v_stride, gb_stride, stash_seq_floats, engaged_flag,
+                                    io_dtype, out_dtype);
+    int st = check_verify(a);
+    if (st != GDN_OK) return st;
+    route_geometry(gdn::verify_geometry(a), "");
+    return launched(gdn::launch_verify(a, stream));
+}
+
+static gdn::FoldArgs make_fold(float* const* h_table, const float* stash, const int32_t* na_tab,
+                               const uint32_t* engaged_flag, int B, int Hk, int Hv, int dk, int dv,
+                               int stash_seq_floats, int io_dtype)
+{
+    gdn::FoldArgs a;
+    a.h_table = h_table; a.stash = stash; a.na_tab = na_tab; a.engaged_flag = engaged_flag;
+    a.B = B; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.stash_seq_floats = stash_seq_floats;
+    a.io_dtype = io_dtype;
+    return a;
+}
+
+int gdn_fold_plan(float* const* h_table, const float* stash, const int32_t* na_tab,
+                  float* const* hi_tables, int slab_entries, const uint32_t* engaged_flag,
+                  int k_rows, int B, int Hk, int Hv, int dk, int dv, int stash_seq_floats,
+                  int io_dtype)
+{
+    (void)slab_entries;
+    gdn::FoldArgs a = make_fold(h_table, stash, na_tab, engaged_flag, B, Hk, Hv, dk, dv,
+                                stash_seq_floats, io_dtype);
+    int st = check_fold(a, hi_tables, k_rows);
+    if (st != GDN_OK) return st;
+    route_geometry(gdn::fold_geometry(a), "");
+    return GDN_OK;
+}
+
+int gdn_fold(float* const* h_table, const float* stash, const int32_t* na_tab,
+             float* const* hi_tables, int slab_entries, const uint32_t* engaged_flag, int k_rows,
+             int B, int Hk, int Hv, int dk, int dv, int stash_seq_floats, int io_dtype,
+             hipStream_t stream)
+{
+    (void)slab_entries;
+    gdn::FoldArgs a = make_fold(h_table, stash, na_tab, engaged_flag, B, Hk, Hv, dk, dv,
+                                stash_seq_floats, io_dtype);
+    int st = check_fold(a, hi_tables, k_rows);
+    if (st != GDN_OK) return st;
+    route_geometry(gdn::fold_geometry(a), "");
+    return launched(gdn::launch_fold(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,262 @@
+// K = 4 write-on-accept decode verify, its post-verdict fold, and the clear of
+// the engaged word (ssm_gdn_woa.rs: docs of gdn_decode_wy4_woa, gdn_wy4_fold
+// and gdn_wy4_flag_clear).
+//
+// Verify, per (v-head, sequence): the 4 draft rows are one chunk of the
+// chunked form with L = 4 and start state h0 = *(h_table[b]) + vh*dk*dv:
+//   p_s = h0^T k_s,  y_r = h0^T q_r                       (8 reductions over dk)
+//   G = cumsum(gate), A_rs = beta_r exp(G_r - G_s) k_r.k_s (s < r)
+//   Delta = (I + A)^-1 diag(beta) (V - diag(exp(G)) P)     (4x4 forward solve)
+//   o_r = exp(G_r) y_r + sum_{s<=r} exp(G_r - G_s) (q_r.k_s) Delta_s
+// It writes the outputs and stashes Delta, G and the keys; it writes no state.
+// Fold: h <- exp(G_{na-1}) h0 + sum_{s<na} exp(G_{na-1} - G_s) k_s Delta_s^T,
+// the state after the first na rows, reading and writing the state once.
+//
+// Both kernels are HBM-bound (about 4 flop per state byte): the state is
+// streamed once with 16-byte coalesced loads, a 64-lane wave covering two
+// 512-byte row segments, and the verify's dk reductions are split over 8 row
+// slices per workgroup and finished through LDS.
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSlices = 8;      // dk row slices per workgroup
+constexpr int kColGroups = 32;  // float4 column groups per slice (dv <= 128)
+constexpr int kMaxD = 128;
+constexpr int kRows = 4;
+
+template <typename TIn>
+__device__ __forceinline__ void load_key_row(float* dst, const TIn* src, int n, int tid) {
+    for (int i = tid; i < n; i += kThreads) dst[i] = Elem<TIn>::load(src + i);
+}
+
+template <typename TIn, typename TOut>
+__global__ void __launch_bounds__(kThreads)
+gdn_verify_k4_kernel(float* const* __restrict__ h_table, const TIn* __restrict__ q,
+                     const TIn* __restrict__ k, const TIn* __restrict__ v,
+                     const float* __restrict__ gate, const float* __restrict__ beta,
+                     TOut* __restrict__ out, float* __restrict__ stash, int Hk, int Hv, int dk,
+                     int dv, int qk_stride, int v_stride, int gb_stride, int stash_seq_floats,
+                     uint32_t* __restrict__ engaged_flag)
+{
+    __shared__ float sk[kRows][kMaxD];
+    __shared__ float sq[kRows][kMaxD];
+    __shared__ float sv[kRows][kMaxD];
+    __shared__ float4 part[kSlices][2 * kRows][kColGroups];  // partial p_s, y_r
+    __shared__ float sG[kRows], sBeta[kRows], sA[kRows][kRows], sQK[kRows][kRows];
+
+    const int tid = threadIdx.x;
+    const int vh = blockIdx.x;
+    const int b = blockIdx.y;
+    const int kh = vh / (Hv / Hk);
+
+    for (int r = 0; r < kRows; ++r) {
+        const size_t row = (size_t)b * kRows + r;
+        load_key_row(sk[r], k + row * qk_stride + (size_t)kh * dk, dk, tid);
+        load_key_row(sq[r], q + row * qk_stride + (size_t)kh * dk, dk, tid);
+        load_key_row(sv[r], v + row * v_stride + (size_t)vh * dv, dv, tid);
+    }
+    if (tid < kRows) {
+        const size_t off = ((size_t)b * kRows + tid) * gb_stride + vh;
+        sG[tid] = gate[off];
+        sBeta[tid] = beta[off];
+    }
+    __syncthreads();
+
+    // Partial reductions over this thread's dk slice, 4 columns at a time.
+    const float* h0 = h_table[b] + (size_t)vh * dk * dv;
+    const int cg = tid % kColGroups;
+    const int sl = tid / kColGroups;
+    const int ncg = dv / 4;
+    if (cg < ncg) {
+        float4 acc[2 * kRows];
+#pragma unroll
+        for (int m = 0; m < 2 * kRows; ++m) acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = sl; i < dk; i += kSlices) {
+            const float4 h = *reinterpret_cast<const float4*>(h0 + (size_t)i * dv + 4 * cg);
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                const float kk = sk[r][i], qq = sq[r][i];
+                acc[r].x += h.x * kk; acc[r].y += h.y * kk; acc[r].z += h.z * kk; acc[r].w += h.w * kk;
+                acc[kRows + r].x += h.x * qq; acc[kRows + r].y += h.y * qq;
+                acc[kRows + r].z += h.z * qq; acc[kRows + r].w += h.w * qq;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 2 * kRows; ++m) part[sl][m][cg] = acc[m];
+    }
+    // Scalars of the 4x4 chunk: cumulative decay, A and Q K^T.
+    if (tid < 16) {
+        const int r = tid / 4, s = tid % 4;
+        float kk = 0.f, qk = 0.f;
+        if (s <= r)
+            for (int i = 0; i < dk; ++i) { kk += sk[r][i] * sk[s][i]; qk += sq[r][i] * sk[s][i]; }
+        sA[r][s] = kk;   // raw k_r.k_s for now
+        sQK[r][s] = qk;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float acc = 0.f;
+        for (int r = 0; r < kRows; ++r) { acc += sG[r]; sG[r] = acc; }
+        for (int r = 0; r < kRows; ++r)
+            for (int s = 0; s < kRows; ++s) {
+                const float gam = s <= r ? __expf(sG[r] - sG[s]) : 0.f;
+                sA[r][s] = s < r ? sBeta[r] * gam * sA[r][s] : 0.f;
+                sQK[r][s] = gam * sQK[r][s];
+            }
+    }
+    __syncthreads();
+
+    // One thread per dv column: finish the reductions, solve, write.
+    float* st = stash + (size_t)b * stash_seq_floats + (size_t)vh * stash_head_floats(dk, dv, sizeof(TIn) == 2);
+    for (int j = tid; j < dv; j += kThreads) {
+        float p[kRows], y[kRows];
+        for (int r = 0; r < kRows; ++r) { p[r] = 0.f; y[r] = 0.f; }
+        const int g = j / 4, c = j % 4;
+        for (int s2 = 0; s2 < kSlices; ++s2)
+            for (int r = 0; r < kRows; ++r) {
+                const float4 a = part[s2][r][g], w = part[s2][kRows + r][g];
+                p[r] += c == 0 ? a.x : c == 1 ? a.y : c == 2 ? a.z : a.w;
+                y[r] += c == 0 ? w.x : c == 1 ? w.y : c == 2 ? w.z : w.w;
+            }
+        float d[kRows];
+        for (int r = 0; r < kRows; ++r) {
+            float x = sBeta[r] * (sv[r][j] - __expf(sG[r]) * p[r]);
+            for (int m = 0; m < r; ++m) x -= sA[r][m] * d[m];
+            d[r] = x;
+        }
+        for (int r = 0; r < kRows; ++r) {
+            float o = __expf(sG[r]) * y[r];
+            for (int s = 0; s <= r; ++s) o += sQK[r][s] * d[s];
+            Elem<TOut>::store(out + (((size_t)b * kRows + r) * Hv + vh) * dv + j, o);
+            st[r * dv + j] = d[r];
+        }
+    }
+    if (tid < kRows) st[kRows * dv + tid] = sG[tid];
+    float* sk_out = st + kRows * dv + kRows;
+    if (sizeof(TIn) == 2) {
+        // keys as packed bf16 bits, exactly as read
+        uint16_t* kb = reinterpret_cast<uint16_t*>(sk_out);
+        for (int e = tid; e < kRows * dk; e += kThreads) {
+            const int r = e / dk, i = e % dk;
+            kb[e] = *reinterpret_cast<const uint16_t*>(k + ((size_t)b * kRows + r) * qk_stride + (size_t)kh * dk + i);
+        }
+    } else {
+        for (int e = tid; e < kRows * dk; e += kThreads) sk_out[e] = sk[e / dk][e % dk];
+    }
+    if (vh == 0 && b == 0 && tid == 0) engaged_flag[0] = 1u;
+}
+
+template <bool kBf16Keys>
+__global__ void __launch_bounds__(kThreads)
+gdn_fold_k4_kernel(float* const* __restrict__ h_table, const float* __restrict__ stash,
+                   const int32_t* __restrict__ na_tab, const uint32_t* __restrict__ engaged_flag,
+                   int dk, int dv, int stash_seq_floats)
+{
+    __shared__ float sk[kRows][kMaxD];
+    __shared__ float sd[kRows][kMaxD];
+    __shared__ float sc[kRows + 1];
+
+    if (engaged_flag[0] == 0u) return;   // the write-on-accept verify did not run
+    const int vh = blockIdx.x;
+    const int b = blockIdx.y;
+    const int na = min(max(na_tab[b], 0), kRows);
+    if (na == 0) return;                 // nothing accepted: the state is left as it is
+    const int tid = threadIdx.x;
+    const float* st = stash + (size_t)b * stash_seq_floats + (size_t)vh * stash_head_floats(dk, dv, kBf16Keys);
+    for (int e = tid; e < na * dv; e += kThreads) sd[e / dv][e % dv] = st[e];
+    const float* sk_in = st + kRows * dv + kRows;
+    for (int e = tid; e < na * dk; e += kThreads) {
+        float x;
+        if (kBf16Keys) x = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sk_in)[e]);
+        else x = sk_in[e];
+        sk[e / dk][e % dk] = x;
+    }
+    if (tid <= na) {
+        const float gl = st[kRows * dv + na - 1];
+        sc[tid] = tid < na ? __expf(gl - st[kRows * dv + tid]) : __expf(gl);
+    }
+    __syncthreads();
+
+    float* h = h_table[b] + (size_t)vh * dk * dv;
+    const int ncg = dv / 4;
+    const float gam = sc[na];
+    for (int e = tid; e < dk * ncg; e += kThreads) {
+        const int i = e / ncg, c4 = (e % ncg) * 4;
+        float4 x = *reinterpret_cast<float4*>(h + (size_t)i * dv + c4);
+        x.x *= gam; x.y *= gam; x.z *= gam; x.w *= gam;
+        for (int s = 0; s < na; ++s) {
+            const float ks = sc[s] * sk[s][i];
+            x.x += ks * sd[s][c4]; x.y += ks * sd[s][c4 + 1];
+            x.z += ks * sd[s][c4 + 2]; x.w += ks * sd[s][c4 + 3];
+        }
+        *reinterpret_cast<float4*>(h + (size_t)i * dv + c4) = x;
+    }
+}
+
+__global__ void __launch_bounds__(64) gdn_flag_clear_kernel(uint32_t* flag)
+{
+    if (threadIdx.x == 0) flag[0] = 0u;
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_verify_typed(const VerifyArgs& a, hipStream_t s)
+{
+    hipLaunchKernelGGL((gdn_verify_k4_kernel<TIn, TOut>), dim3(a.Hv, a.B), dim3(kThreads), 0, s,
+                       a.h_table, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.gate, a.beta,
+                       (TOut*)a.out, a.stash, a.Hk, a.Hv, a.dk, a.dv, a.qk_stride, a.v_stride,
+                       a.gb_stride, a.stash_seq_floats, a.engaged_flag);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+Geometry verify_geometry(const VerifyArgs& a)
+{
+    Geometry g{"gdn_verify_k4_kernel", {(unsigned)a.Hv, (unsigned)a.B, 1u}, kThreads,
+               (unsigned)(sizeof(float) * 3 * kRows * kMaxD + sizeof(float4) * kSlices * 2 * kRows * kColGroups +
+                          sizeof(float) * (2 * kRows + 2 * kRows * kRows))};
+    return g;
+}
+
+Geometry fold_geometry(const FoldArgs& a)
+{
+    Geometry g{"gdn_fold_k4_kernel", {(unsigned)a.Hv, (unsigned)a.B, 1u}, kThreads,
+               (unsigned)(sizeof(float) * (2 * kRows * kMaxD + kRows + 1))};
+    return g;
+}
+
+Geometry flag_clear_geometry()
+{
+    Geometry g{"gdn_flag_clear_kernel", {1u, 1u, 1u}, 64u, 0u};
+    return g;
+}
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t s)
+{
+    if (a.io_dtype == 0 && a.out_dtype == 0) return launch_verify_typed<float, float>(a, s);
+    if (a.io_dtype == 0 && a.out_dtype == 1) return launch_verify_typed<float, uint16_t>(a, s);
+    if (a.io_dtype == 1 && a.out_dtype == 0) return launch_verify_typed<uint16_t, float>(a, s);
+    return launch_verify_typed<uint16_t, uint16_t>(a, s);
+}
+
+hipError_t launch_fold(const FoldArgs& a, hipStream_t s)
+{
+    if (a.io_dtype == 1)
+        hipLaunchKernelGGL((gdn_fold_k4_kernel<true>), dim3(a.Hv, a.B), dim3(kThreads), 0, s,
+                           a.h_table, a.stash, a.na_tab, a.engaged_flag, a.dk, a.dv, a.stash_seq_floats);
+    else
+        hipLaunchKernelGGL((gdn_fold_k4_kernel<false>), dim3(a.Hv, a.B), dim3(kThreads), 0, s,
+                           a.h_table, a.stash, a.na_tab, a.engaged_flag, a.dk, a.dv, a.stash_seq_floats);
+    return hipGetLastError();
+}
+
+hipError_t launch_flag_clear(uint32_t* flag, hipStream_t s)
+{
+    hipLaunchKernelGGL(gdn_flag_clear_kernel, dim3(1), dim3(64), 0, s, flag);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,103 @@
+// Internal declarations shared by the HIP sources of libgdn.so.  Not part of
+// the C ABI (include/gdn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Arguments of one prefill call after host validation.
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_g;
+    const float* beta;
+    const float* h0;
+    void* out;
+    float* h_final;
+    int B, T, Hk, Hv, dk, dv, chunk;
+    const int32_t* cu_seqlens;
+    int io_dtype, out_dtype;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+struct VerifyArgs {
+    float* const* h_table;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* gate;
+    const float* beta;
+    void* out;
+    float* stash;
+    int B, Hk, Hv, dk, dv;
+    int qk_stride, v_stride, gb_stride, stash_seq_floats;
+    uint32_t* engaged_flag;
+    int io_dtype, out_dtype;
+};
+
+struct FoldArgs {
+    float* const* h_table;
+    const float* stash;
+    const int32_t* na_tab;
+    const uint32_t* engaged_flag;
+    int B, Hk, Hv, dk, dv, stash_seq_floats;
+    int io_dtype;
+};
+
+// Launch geometry a launcher reports for the route line.
+struct Geometry {
+    const char* entry;
+    unsigned grid[3];
+    unsigned block;
+    unsigned lds_bytes;
+};
+
+// Kernel choice and geometry of a prefill call (no launch).
+bool prefill_mfma_accepts(const PrefillArgs& a);
+Geometry prefill_generic_geometry(const PrefillArgs& a);
+Geometry prefill_mfma_geometry(const PrefillArgs& a);
+Geometry verify_geometry(const VerifyArgs& a);
+Geometry fold_geometry(const FoldArgs& a);
+Geometry flag_clear_geometry();
+
+hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
+hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
+hipError_t launch_flag_clear(uint32_t* flag, hipStream_t s);
+
+// Per-v-head stash floats of the 4-row verify (delta, G, keys).
+__host__ __device__ inline size_t stash_head_floats(int dk, int dv, int io_dtype) {
+    return (size_t)4 * dv + 4 + (io_dtype == 1 ? (size_t)2 * dk : (size_t)4 * dk);
+}
+
+// ---- element helpers ------------------------------------------------------
+// bf16 is carried as its 16 raw bits; widening is exact.
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float load(const float* p) { return *p; }
+    __device__ __forceinline__ static void store(float* p, float x) { *p = x; }
+};
+template <> struct Elem<uint16_t> {
+    __device__ __forceinline__ static float load(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+    __device__ __forceinline__ static void store(uint16_t* p, float x) { *p = f32_to_bf16_bits(x); }
+};
+
+}  // namespace gdn

@@ -1,0 +1,178 @@
+"""GPU parity and bookkeeping of the K = 4 write-on-accept verify and its fold.
+
+States sit in separately allocated slots, allocated in shuffled order and
+interleaved with spare slots that are not in the pointer table.  Checks:
+  * outputs of all 4 rows against the fp64 oracle (fp32 outputs <= 1e-4,
+    bf16 outputs within bf16 rounding, 4e-3);
+  * verify writes no state (bitwise) and sets the engaged word;
+  * after the fold, each state equals the oracle's state after its first na
+    rows (<= 1e-4 of max|state|); na = 0 states and spare slots are bitwise
+    unchanged;
+  * one-hot keys with no decay and beta = 1 make the accepted rows
+    identifiable: exactly rows 0..na-1 of each state change, bit for bit;
+  * with the word cleared (no verify since the clear) the fold changes nothing;
+  * repeated runs are bitwise identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_ssm_gated_amd as gdn
+import oracle
+import synth
+from gpu_common import dev, rel_err, say
+
+pytestmark = pytest.mark.gpu
+K = 4
+
+
+class Setup:
+    def __init__(self, inp, io, out_dtype, qk_pad=0, stash_pad=0):
+        d = dev()
+        st = inp["states"]
+        self.B, self.Hv, self.dk, self.dv = st.shape
+        self.Hk = inp["q"].shape[2]
+        B, Hv, dk, dv, Hk = self.B, self.Hv, self.dk, self.dv, self.Hk
+        self.io = io
+        # separately allocated states, in shuffled order, with spare slots between
+        self.slots = [None] * B
+        self.spares = []
+        for idx in inp["slot_perm"].tolist():
+            self.spares.append(torch.full((Hv, dk, dv), -7.25, device=d))
+            self.slots[idx] = st[idx].to(d).clone()
+        self.h_table = torch.tensor([s.data_ptr() for s in self.slots], dtype=torch.int64, device=d)
+        # rows with padded strides
+        self.qk_stride = Hk * dk + qk_pad
+        self.v_stride = Hv * dv + qk_pad
+        self.gb_stride = Hv + qk_pad
+
+        def rows(x, width, stride, dtype):
+            buf = torch.zeros((B * K, stride), dtype=dtype)
+            buf[:, :width] = x.reshape(B * K, width).to(dtype)
+            return buf.to(d)
+
+        self.q = rows(inp["q"], Hk * dk, self.qk_stride, io)
+        self.k = rows(inp["k"], Hk * dk, self.qk_stride, io)
+        self.v = rows(inp["v"], Hv * dv, self.v_stride, io)
+        self.gate = rows(inp["gate"], Hv, self.gb_stride, torch.float32)
+        self.beta = rows(inp["beta"], Hv, self.gb_stride, torch.float32)
+        self.out = torch.empty((B, K, Hv, dv), dtype=out_dtype, device=d)
+        self.io_code = gdn.GDN_BF16 if io == torch.bfloat16 else gdn.GDN_F32
+        self.ssf = gdn.gdn_stash_seq_floats(Hv, dk, dv, K, self.io_code) + stash_pad
+        self.stash = torch.full((B * self.ssf,), float("nan"), device=d)
+        self.flag = torch.full((1,), 7, dtype=torch.int32, device=d)
+        self.na = inp["na"].to(d)
+
+    def states(self):
+        return torch.stack([s for s in self.slots]).cpu()
+
+    def clear(self):
+        gdn.gdn_flag_clear(self.flag)
+
+    def verify(self):
+        return gdn.gdn_decode_verify_k4(self.h_table, self.q, self.k, self.v, self.gate, self.beta,
+                                        self.out, self.stash, self.B, self.Hk, self.Hv, self.dk,
+                                        self.dv, self.qk_stride, self.v_stride, self.gb_stride,
+                                        self.ssf, self.flag)
+
+    def fold(self):
+        return gdn.gdn_fold(self.h_table, self.stash, self.na, None, 0, self.flag, K, self.B,
+                            self.Hk, self.Hv, self.dk, self.dv, self.ssf, self.io_code)
+
+
+def oracle_decode(inp):
+    return oracle.decode(inp["states"], inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"])
+
+
+@pytest.mark.parametrize("io,out_dtype,tol,pad", [
+    (torch.bfloat16, torch.float32, 1e-4, 0),
+    (torch.bfloat16, torch.bfloat16, 4e-3, 0),
+    (torch.float32, torch.float32, 1e-4, 0),
+    (torch.bfloat16, torch.float32, 1e-4, 24),
+])
+def test_verify_fold_workload(io, out_dtype, tol, pad):
+    w = synth.WORKLOADS["verify_k4_b16"]
+    inp = synth.decode_inputs(w.B, K, w.Hk, w.Hv, w.dk, w.dv, io=io, seed=w.seed)
+    say("verify_k4_b16", io, out_dtype, "pad", pad)
+    s = Setup(inp, io, out_dtype, qk_pad=pad, stash_pad=pad)
+    before = s.states()
+    spares_before = [x.cpu() for x in s.spares]
+    s.clear()
+    torch.cuda.synchronize()
+    assert int(s.flag.item()) == 0
+    route = s.verify()
+    torch.cuda.synchronize()
+    assert route.startswith("gdn_verify_k4_kernel grid=[48,16,1]"), route
+    assert int(s.flag.item()) == 1, "verify marks the engaged word"
+    assert torch.equal(s.states(), before), "verify writes no state"
+    ro, after = oracle_decode(inp)
+    assert rel_err(s.out, ro) <= tol
+    s.fold()
+    torch.cuda.synchronize()
+    got = s.states()
+    na = inp["na"].numpy()
+    for b in range(s.B):
+        if na[b] == 0:
+            assert torch.equal(got[b], before[b]), f"na=0 state {b} must keep its bytes"
+        else:
+            assert rel_err(got[b], after[b, na[b]]) <= 1e-4, f"sequence {b} na={na[b]}"
+    for x, y in zip(s.spares, spares_before):
+        assert torch.equal(x.cpu(), y), "a slot outside the table changed"
+
+
+def test_fold_without_verify_is_a_no_op():
+    inp = synth.decode_inputs(4, K, 2, 4, 128, 128, seed=21)
+    say("fold with the word clear")
+    s = Setup(inp, torch.bfloat16, torch.float32)
+    s.na.fill_(4)
+    s.stash.fill_(1.0)
+    before = s.states()
+    s.clear()
+    s.fold()
+    torch.cuda.synchronize()
+    assert torch.equal(s.states(), before)
+
+
+def test_one_hot_rows_bookkeeping():
+    """gate = 0, beta = 1, key s = e_s: the fold of na rows moves exactly state
+    rows 0..na-1 (the others are multiplied by exp(0) = 1 and get 0 * delta)."""
+    B, Hk, Hv, dk, dv = 5, 1, 2, 128, 128
+    inp = synth.decode_inputs(B, K, Hk, Hv, dk, dv, seed=22)
+    k = torch.zeros(B, K, Hk, dk)
+    for s_ in range(K):
+        k[:, s_, :, s_] = 1.0
+    inp["k"] = k.to(torch.bfloat16)
+    inp["gate"] = torch.zeros(B, K, Hv)
+    inp["beta"] = torch.ones(B, K, Hv)
+    inp["v"] = (inp["v"].float() + 3.0).to(torch.bfloat16)  # make every delta nonzero
+    say("one-hot bookkeeping")
+    s = Setup(inp, torch.bfloat16, torch.float32)
+    before = s.states()
+    s.clear()
+    s.verify()
+    s.fold()
+    torch.cuda.synchronize()
+    got = s.states()
+    for b in range(B):
+        na = int(inp["na"][b])
+        changed = (got[b] != before[b]).any(dim=-1)  # [Hv, dk]
+        for vh in range(Hv):
+            rows = torch.nonzero(changed[vh]).flatten().tolist()
+            assert rows == list(range(na)), (b, vh, na, rows)
+
+
+def test_verify_fold_deterministic():
+    w = synth.WORKLOADS["verify_k4_b16"]
+    inp = synth.decode_inputs(w.B, K, w.Hk, w.Hv, w.dk, w.dv, seed=w.seed)
+    say("decode determinism")
+    res = []
+    for _ in range(2):
+        s = Setup(inp, torch.bfloat16, torch.bfloat16)
+        s.clear()
+        s.verify()
+        s.fold()
+        torch.cuda.synchronize()
+        res.append((s.out.cpu(), s.stash.cpu(), s.states()))
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))

@@ -1,0 +1,155 @@
+"""Host-side checks of the C ABI, no GPU needed.
+
+The library must load, export every entry point include/gdn.h declares, and
+refuse each bad argument with its own named status before launching anything
+(the *_plan entry points run the same validation as the launching ones and
+stop there).  Pointers below are dummies: the plan functions only compare them
+with NULL.
+"""
+import os
+import re
+
+import pytest
+
+import linear_attention_ssm_gated_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+X = 0x1000  # non-NULL dummy pointer
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.fail("libgdn.so is not built (run __graft_entry__.build())")
+    return gdn.library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in gdn.h but not exported"
+    assert set(names) == set(gdn.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings_are_distinct(lib):
+    texts = [gdn.status_string(s) for s in range(12)]
+    assert len(set(texts)) == 12
+    for s, t in enumerate(texts):
+        assert t.startswith(gdn._STATUS[s]), (s, t)
+    assert gdn.status_string(99) == "unknown gdn status"
+
+
+def prefill_plan(lib, **kw):
+    a = dict(q=X, k=X, v=X, log_g=X, beta=X, h0=None, out=X, h_final=X, B=1, T=128, Hk=16, Hv=48,
+             dk=128, dv=128, chunk=64, cu=None, io=1, od=1, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.gdn_chunk_prefill_plan(a["q"], a["k"], a["v"], a["log_g"], a["beta"], a["h0"],
+                                      a["out"], a["h_final"], a["B"], a["T"], a["Hk"], a["Hv"],
+                                      a["dk"], a["dv"], a["chunk"], a["cu"], a["io"], a["od"],
+                                      a["ws"], a["ws_bytes"])
+
+
+def test_prefill_routes(lib):
+    assert prefill_plan(lib) == 0
+    r = gdn.last_route()
+    assert r.startswith("gdn_prefill_"), r
+    assert "grid=[" in r and "block=" in r and "lds=" in r
+    # fp32 I/O goes to the generic kernel and the line says why
+    assert prefill_plan(lib, io=0, od=0, dk=32, dv=32, chunk=32, Hk=1, Hv=1) == 0
+    r = gdn.last_route()
+    assert r.startswith("gdn_prefill_generic_kernel") and "io dtype is f32" in r, r
+    assert "grid=[1,1,1]" in r
+    # bf16 with an odd head size: generic, naming the dk/dv guard
+    assert prefill_plan(lib, dk=64, dv=96) == 0
+    r = gdn.last_route()
+    assert r.startswith("gdn_prefill_generic_kernel") and "dk = dv = 128" in r, r
+    assert "grid=[144,1,1]" in r  # 48 v-heads x 3 column slices of 32
+    assert prefill_plan(lib, chunk=32) == 0
+    assert "chunk = 64" in gdn.last_route()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(io=2), 5), (dict(od=-1), 5),
+    (dict(B=0), 2), (dict(T=-1), 2), (dict(Hk=0), 2), (dict(dk=0), 2), (dict(chunk=0), 2),
+    (dict(B=70000), 2),
+    (dict(Hk=5), 3),
+    (dict(dk=129), 4), (dict(dv=256), 4), (dict(chunk=65), 4),
+    (dict(q=None), 1), (dict(out=None), 1), (dict(beta=None), 1),
+])
+def test_prefill_refusals(lib, kw, status):
+    assert prefill_plan(lib, **kw) == status
+    r = gdn.last_route()
+    assert "refused" in r and gdn._STATUS[status] in r, r
+
+
+def test_prefill_empty_needs_no_pointers(lib):
+    assert prefill_plan(lib, T=0, q=None, k=None, v=None, log_g=None, beta=None, out=None) == 0
+
+
+def test_workspace_and_stash_sizes(lib):
+    assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 128, 128, 64, 1) == 0
+    # per v-head: delta 4*dv, G 4, keys 4*dk bf16 (2*dk floats) or fp32 (4*dk floats)
+    assert gdn.gdn_stash_seq_floats(48, 128, 128, 4, 1) == 48 * (4 * 128 + 4 + 2 * 128)
+    assert gdn.gdn_stash_seq_floats(48, 128, 128, 4, 0) == 48 * (4 * 128 + 4 + 4 * 128)
+    assert gdn.gdn_stash_seq_floats(48, 128, 128, 3, 1) == 0
+
+
+def verify_plan(lib, **kw):
+    a = dict(ht=X, q=X, k=X, v=X, gate=X, beta=X, out=X, stash=X, B=16, Hk=16, Hv=48, dk=128,
+             dv=128, qks=16 * 128, vs=48 * 128, gbs=48, ssf=48 * (512 + 4 + 256), flag=X, io=1, od=1)
+    a.update(kw)
+    return lib.gdn_decode_verify_k4_plan(a["ht"], a["q"], a["k"], a["v"], a["gate"], a["beta"],
+                                         a["out"], a["stash"], a["B"], a["Hk"], a["Hv"], a["dk"],
+                                         a["dv"], a["qks"], a["vs"], a["gbs"], a["ssf"], a["flag"],
+                                         a["io"], a["od"])
+
+
+def test_verify_plan(lib):
+    assert verify_plan(lib) == 0
+    r = gdn.last_route()
+    assert r.startswith("gdn_verify_k4_kernel grid=[48,16,1] block=256"), r
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ht=None), 1), (dict(stash=None), 1), (dict(flag=None), 1), (dict(q=None), 1),
+    (dict(B=0), 2), (dict(Hk=7), 3), (dict(dv=130), 4), (dict(dv=126), 4),
+    (dict(qks=100), 9), (dict(vs=48 * 128 - 1), 9), (dict(gbs=47), 9),
+    (dict(ssf=100), 7), (dict(io=3), 5),
+])
+def test_verify_refusals(lib, kw, status):
+    assert verify_plan(lib, **kw) == status
+    assert "refused" in gdn.last_route()
+
+
+def fold_plan(lib, **kw):
+    a = dict(ht=X, stash=X, na=X, hi=None, slab=0, flag=X, k_rows=4, B=16, Hk=16, Hv=48, dk=128,
+             dv=128, ssf=48 * (512 + 4 + 256), io=1)
+    a.update(kw)
+    return lib.gdn_fold_plan(a["ht"], a["stash"], a["na"], a["hi"], a["slab"], a["flag"],
+                             a["k_rows"], a["B"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["ssf"], a["io"])
+
+
+def test_fold_plan(lib):
+    assert fold_plan(lib) == 0
+    assert gdn.last_route().startswith("gdn_fold_k4_kernel grid=[48,16,1] block=256")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_rows=3), 8), (dict(hi=X), 10), (dict(na=None), 1), (dict(ht=None), 1),
+    (dict(ssf=10), 7), (dict(Hv=47), 3), (dict(io=9), 5),
+])
+def test_fold_refusals(lib, kw, status):
+    assert fold_plan(lib, **kw) == status
+    assert "refused" in gdn.last_route()
+
+
+def test_flag_clear_refuses_null(lib):
+    assert lib.gdn_flag_clear(None, None) == 1
