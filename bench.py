@@ -138,6 +138,9 @@ def bench_prefill(w, args, torch):
         g["hf"] = torch.empty((w.B, w.Hv, w.dk, w.dv), dtype=torch.float32, device=d)
         sets.append(g)
     T_arg = N if inp["cu_seqlens"] is not None else w.T
+    ws_n = gdn.gdn_prefill_workspace_bytes(w.B, T_arg, w.Hk, w.Hv, w.dk, w.dv, w.chunk, gdn.GDN_BF16,
+                                           packed=inp["cu_seqlens"] is not None)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=d)
     stream = torch.cuda.current_stream()
     route = []
 
@@ -145,7 +148,7 @@ def bench_prefill(w, args, torch):
         g = sets[i]
         r = gdn.gdn_chunk_prefill(g["q"], g["k"], g["v"], g["log_g"], g["beta"], g["h0"], g["out"],
                                   g["hf"], w.B, T_arg, w.Hk, w.Hv, w.dk, w.dv, w.chunk,
-                                  cu_seqlens=g["cu_seqlens"], stream=stream)
+                                  cu_seqlens=g["cu_seqlens"], workspace=ws, stream=stream)
         if not route:
             route.append(r)
 

@@ -44,7 +44,7 @@ typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 typedef enum gdn_status {
     GDN_OK = 0,
     GDN_ERR_NULL = 1,          /* a required pointer is NULL */
-    GDN_ERR_SHAPE = 2,         /* B < 1, T < 0, a head count, dk, dv or chunk < 1 */
+    GDN_ERR_SHAPE = 2,         /* B < 1, T < 0, a head count, dk, dv or chunk < 1; B or Hv > 65535 */
     GDN_ERR_HEAD_GROUPS = 3,   /* Hv is not a multiple of Hk */
     GDN_ERR_DIM_LIMIT = 4,     /* dk or dv > 128, or chunk > 64: no kernel here takes it */
     GDN_ERR_DTYPE = 5,         /* unknown dtype code */
@@ -96,10 +96,15 @@ const char* gdn_last_route(void);
  * runs the generic fp32-arithmetic chunked kernel (dk, dv <= 128, chunk <= 64).
  * gdn_last_route() names the one that ran.
  * workspace: device scratch of at least gdn_prefill_workspace_bytes() bytes
- * (may be NULL when that is 0).
+ * (may be NULL when that is 0), asked with the same B, T, shapes and io_dtype,
+ * and packed = (cu_seqlens != NULL).  The MFMA route keeps T = (I + A)^-1 and
+ * P = lower_incl(Gamma o Q K^T) of every (chunk, v-head) there as bf16 (16 KiB
+ * each) plus a chunk table of packed sequences; the generic route needs none.
+ * The library reads and writes the workspace only inside the call's stream
+ * order; its contents need no initialisation.
  */
 size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
-                                   int io_dtype);
+                                   int io_dtype, int packed);
 
 int gdn_chunk_prefill(const void* q, const void* k, const void* v,
                       const float* log_g, const float* beta,

@@ -31,7 +31,7 @@ P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 SIGNATURES = {
     "gdn_status_string": (ctypes.c_char_p, [I]),
     "gdn_last_route": (ctypes.c_char_p, []),
-    "gdn_prefill_workspace_bytes": (Z, [I, I, I, I, I, I, I, I]),
+    "gdn_prefill_workspace_bytes": (Z, [I, I, I, I, I, I, I, I, I]),
     "gdn_chunk_prefill": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, I, I, P, Z, P]),
     "gdn_chunk_prefill_plan": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, I, I, P, Z]),
     "gdn_stash_seq_floats": (Z, [I, I, I, I, I]),
@@ -108,8 +108,8 @@ def _stream(stream):
 
 # ---- entry points, same names as the C ABI --------------------------------
 
-def gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, io_dtype) -> int:
-    return library().gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, io_dtype)
+def gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, io_dtype, packed=False) -> int:
+    return library().gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, io_dtype, int(bool(packed)))
 
 
 def gdn_chunk_prefill(q, k, v, log_g, beta, h0, out, h_final, B, T, Hk, Hv, dk, dv, chunk,
@@ -168,7 +168,8 @@ def chunk_prefill(q, k, v, log_g, beta, h0=None, cu_seqlens=None, chunk=64, out_
     Hv, dv = v.shape[-2], v.shape[-1]
     out = torch.empty(v.shape, dtype=out_dtype or v.dtype, device=v.device)
     hf = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=v.device) if want_state else None
-    ws_n = gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, _dtype_code(q))
+    ws_n = gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, _dtype_code(q),
+                                       packed=cu_seqlens is not None)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=v.device) if ws_n else None
     route = gdn_chunk_prefill(q, k, v, log_g, beta, h0, out, hf, B, T, Hk, Hv, dk, dv, chunk,
                               cu_seqlens=cu_seqlens, workspace=ws, stream=stream)

@@ -48,15 +48,16 @@ int check_prefill(const gdn::PrefillArgs& a, bool* mfma, const char** why)
         return refuse(GDN_ERR_DTYPE, who, "io_dtype/out_dtype must be GDN_F32 or GDN_BF16");
     if (a.B < 1 || a.T < 0 || a.Hk < 1 || a.Hv < 1 || a.dk < 1 || a.dv < 1 || a.chunk < 1)
         return refuse(GDN_ERR_SHAPE, who, "need B, Hk, Hv, dk, dv, chunk >= 1 and T >= 0");
-    if (a.B > 65535)
-        return refuse(GDN_ERR_SHAPE, who, "B > 65535 (grid y limit)");
+    if (a.B > 65535 || a.Hv > 65535)
+        return refuse(GDN_ERR_SHAPE, who, "B or Hv > 65535 (grid y limit)");
     if (a.Hv % a.Hk != 0)
         return refuse(GDN_ERR_HEAD_GROUPS, who, "Hv must be a multiple of Hk");
     if (a.dk > 128 || a.dv > 128 || a.chunk > 64)
         return refuse(GDN_ERR_DIM_LIMIT, who, "dk, dv <= 128 and chunk <= 64");
     if (a.T > 0 && (!a.q || !a.k || !a.v || !a.log_g || !a.beta || !a.out))
         return refuse(GDN_ERR_NULL, who, "q, k, v, log_g, beta and out are required when T > 0");
-    const size_t need = gdn_prefill_workspace_bytes(a.B, a.T, a.Hk, a.Hv, a.dk, a.dv, a.chunk, a.io_dtype);
+    const size_t need = gdn_prefill_workspace_bytes(a.B, a.T, a.Hk, a.Hv, a.dk, a.dv, a.chunk,
+                                                    a.io_dtype, a.cu_seqlens != nullptr);
     if (need > 0 && (!a.workspace || a.workspace_bytes < need))
         return refuse(GDN_ERR_WORKSPACE, who, "workspace smaller than gdn_prefill_workspace_bytes()");
     *why = "";
@@ -159,10 +160,13 @@ const char* gdn_status_string(int status)
 const char* gdn_last_route(void) { return t_route; }
 
 size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
-                                   int io_dtype)
+                                   int io_dtype, int packed)
 {
-    (void)B; (void)T; (void)Hk; (void)Hv; (void)dk; (void)dv; (void)chunk; (void)io_dtype;
-    return 0;  // both prefill kernels keep their intermediates on chip
+    if (B < 1 || T < 0 || Hk < 1 || Hv < 1) return 0;
+    gdn::PrefillArgs a{};
+    a.io_dtype = io_dtype; a.dk = dk; a.dv = dv; a.chunk = chunk;
+    if (!gdn::prefill_mfma_accepts(a)) return 0;  // the generic kernel keeps everything in LDS
+    return gdn::prefill_mfma_workspace_bytes(B, T, Hv, packed != 0);
 }
 
 int gdn_chunk_prefill_plan(const void* q, const void* k, const void* v, const float* log_g,

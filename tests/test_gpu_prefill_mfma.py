@@ -1,0 +1,134 @@
+"""GPU parity of the bf16 MFMA chunked prefill (dk = dv = 128, chunk 64)
+against the fp64 oracle: max|d|/max|ref| <= 2e-2 on outputs and final states
+(bf16 MFMA operands, fp32 accumulators and state).
+
+Full-size workloads run through the same entry point and launch
+configuration bench.py times: the 1168-token and 4576-token calls are checked
+on every v-head; the packed 8-sequence workload on a sample of v-heads.
+Edge cases: sequences of 1, 63, 64, 65 and 130 tokens, empty packed
+sequences, fp32 outputs, in-place states.  Bitwise properties: repeated runs,
+a state carried across a chunk-aligned split, and packed vs separate runs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_ssm_gated_amd as gdn
+import synth
+from gpu_common import dev, gpu_prefill, oracle_prefill, rel_err, say
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+ROUTE = "gdn_wy_prep_kernel+gdn_spine_kernel"
+
+
+def check(inp, out, hf, heads=None):
+    ro, rh = oracle_prefill(inp, heads=heads)
+    eo = rel_err(out, ro, heads=heads)
+    eh = rel_err(hf, rh, heads=heads, head_axis=1)
+    say(f"  out err {eo:.3e}  state err {eh:.3e}")
+    assert eo <= TOL
+    assert eh <= TOL
+    return eo, eh
+
+
+@pytest.mark.parametrize("name", ["prefill_t1168", "prefill_t4576_h0"])
+def test_full_workload_all_heads(name):
+    w = synth.WORKLOADS[name]
+    inp = synth.workload_inputs(w)
+    say(name)
+    out, hf, route = gpu_prefill(inp, w.chunk)
+    assert route.startswith(ROUTE), route
+    check(inp, out, hf)
+
+
+def test_packed_workload_sampled_heads():
+    w = synth.WORKLOADS["varlen_b8"]
+    inp = synth.workload_inputs(w)
+    say("varlen_b8", inp["cu_seqlens"].tolist())
+    out, hf, route = gpu_prefill(inp, w.chunk)
+    assert route.startswith(ROUTE), route
+    check(inp, out, hf, heads=[0, 17, 47])
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130])
+def test_short_and_ragged(T):
+    inp = synth.prefill_inputs(2, T, 1, 3, 128, 128, h0=True, seed=100 + T)
+    say("ragged", T)
+    out, hf, route = gpu_prefill(inp, 64)
+    assert route.startswith(ROUTE)
+    check(inp, out, hf)
+
+
+def test_packed_with_empty_and_short_sequences():
+    lens = [1, 0, 64, 65, 200, 0]
+    inp = synth.prefill_inputs(len(lens), 0, 2, 4, 128, 128, h0=True, seed=31, lengths=lens)
+    say("packed edge", lens)
+    out, hf, _ = gpu_prefill(inp, 64)
+    check(inp, out, hf)
+    for b in (1, 5):
+        assert torch.equal(hf[b].cpu(), inp["h0"][b]), "an empty sequence keeps its state"
+
+
+def test_fp32_output_and_no_initial_state():
+    inp = synth.prefill_inputs(1, 300, 2, 6, 128, 128, h0=False, seed=32)
+    say("fp32 out")
+    out, hf, _ = gpu_prefill(inp, 64, out_dtype=torch.float32)
+    assert out.dtype == torch.float32
+    check(inp, out, hf)
+
+
+def test_in_place_state():
+    inp = synth.prefill_inputs(2, 150, 1, 3, 128, 128, h0=True, seed=33)
+    g = {k: (v.to(dev()) if torch.is_tensor(v) else v) for k, v in inp.items()}
+    h = g["h0"].clone()
+    out = torch.empty_like(g["v"])
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(2, 150, 1, 3, 128, 128, 64, gdn.GDN_BF16),
+                     dtype=torch.uint8, device=dev())
+    say("in place")
+    gdn.gdn_chunk_prefill(g["q"], g["k"], g["v"], g["log_g"], g["beta"], h, out, h,
+                          2, 150, 1, 3, 128, 128, 64, workspace=ws)
+    torch.cuda.synchronize()
+    check(inp, out, h)
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def test_deterministic():
+    inp = synth.prefill_inputs(1, 700, 2, 6, 128, 128, h0=True, seed=34)
+    say("determinism")
+    o1, h1, _ = gpu_prefill(inp, 64)
+    o2, h2, _ = gpu_prefill(inp, 64)
+    assert torch.equal(_bits(o1), _bits(o2)) and torch.equal(_bits(h1), _bits(h2))
+
+
+def test_state_carry_is_bitwise_at_chunk_boundary():
+    T1, T2 = 128, 150
+    inp = synth.prefill_inputs(1, T1 + T2, 2, 6, 128, 128, h0=True, seed=35)
+    part = lambda sl: {k: (v[:, sl].contiguous() if k in ("q", "k", "v", "log_g", "beta") else v)
+                       for k, v in inp.items()}
+    say("carry")
+    o, h, _ = gpu_prefill(inp, 64)
+    o1, h1, _ = gpu_prefill(part(slice(0, T1)), 64)
+    o2, h2, _ = gpu_prefill(part(slice(T1, None)), 64, h0=h1)
+    assert torch.equal(_bits(torch.cat([o1, o2], dim=1)), _bits(o))
+    assert torch.equal(_bits(h2), _bits(h))
+
+
+def test_packed_equals_separate_bitwise():
+    lens = [70, 129, 5]
+    inp = synth.prefill_inputs(len(lens), 0, 1, 3, 128, 128, h0=True, seed=36, lengths=lens)
+    say("packed vs separate")
+    out, hf, _ = gpu_prefill(inp, 64)
+    cu = inp["cu_seqlens"].tolist()
+    for b, L in enumerate(lens):
+        sl = slice(cu[b], cu[b + 1])
+        one = {k: (v[sl].unsqueeze(0).contiguous() if k in ("q", "k", "v", "log_g", "beta") else v)
+               for k, v in inp.items()}
+        one["h0"] = inp["h0"][b : b + 1]
+        one["cu_seqlens"] = None
+        o, h, _ = gpu_prefill(one, 64)
+        assert torch.equal(_bits(o[0]), _bits(out[sl])), b
+        assert torch.equal(_bits(h[0]), _bits(hf[b])), b

@@ -49,7 +49,7 @@ def test_status_strings_are_distinct(lib):
 
 def prefill_plan(lib, **kw):
     a = dict(q=X, k=X, v=X, log_g=X, beta=X, h0=None, out=X, h_final=X, B=1, T=128, Hk=16, Hv=48,
-             dk=128, dv=128, chunk=64, cu=None, io=1, od=1, ws=None, ws_bytes=0)
+             dk=128, dv=128, chunk=64, cu=None, io=1, od=1, ws=X, ws_bytes=1 << 40)
     a.update(kw)
     return lib.gdn_chunk_prefill_plan(a["q"], a["k"], a["v"], a["log_g"], a["beta"], a["h0"],
                                       a["out"], a["h_final"], a["B"], a["T"], a["Hk"], a["Hv"],
@@ -60,8 +60,8 @@ def prefill_plan(lib, **kw):
 def test_prefill_routes(lib):
     assert prefill_plan(lib) == 0
     r = gdn.last_route()
-    assert r.startswith("gdn_prefill_"), r
-    assert "grid=[" in r and "block=" in r and "lds=" in r
+    assert r.startswith("gdn_wy_prep_kernel+gdn_spine_kernel grid=[192,1,1] block=128"), r
+    assert "lds=" in r
     # fp32 I/O goes to the generic kernel and the line says why
     assert prefill_plan(lib, io=0, od=0, dk=32, dv=32, chunk=32, Hk=1, Hv=1) == 0
     r = gdn.last_route()
@@ -83,6 +83,7 @@ def test_prefill_routes(lib):
     (dict(Hk=5), 3),
     (dict(dk=129), 4), (dict(dv=256), 4), (dict(chunk=65), 4),
     (dict(q=None), 1), (dict(out=None), 1), (dict(beta=None), 1),
+    (dict(ws=None), 6), (dict(ws_bytes=1000), 6), (dict(Hv=70000, Hk=70000), 2),
 ])
 def test_prefill_refusals(lib, kw, status):
     assert prefill_plan(lib, **kw) == status
@@ -95,7 +96,15 @@ def test_prefill_empty_needs_no_pointers(lib):
 
 
 def test_workspace_and_stash_sizes(lib):
-    assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 128, 128, 64, 1) == 0
+    # MFMA route: a 256-byte chunk table, then T and P (2 x 64 x 64 bf16) per (chunk, v-head)
+    assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 128, 128, 64, 1) == 256 + 72 * 48 * 16384
+    assert gdn.gdn_prefill_workspace_bytes(2, 100, 16, 48, 128, 128, 64, 1) == 256 + 2 * 2 * 48 * 16384
+    # packed: ceil(T / 64) + B chunks at most
+    assert gdn.gdn_prefill_workspace_bytes(8, 39168, 16, 48, 128, 128, 64, 1, packed=True) == \
+        256 + (612 + 8) * 48 * 16384
+    # generic route needs none
+    assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 128, 128, 64, 0) == 0
+    assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 64, 64, 64, 1) == 0
     # per v-head: delta 4*dv, G 4, keys 4*dk bf16 (2*dk floats) or fp32 (4*dk floats)
     assert gdn.gdn_stash_seq_floats(48, 128, 128, 4, 1) == 48 * (4 * 128 + 4 + 2 * 128)
     assert gdn.gdn_stash_seq_floats(48, 128, 128, 4, 0) == 48 * (4 * 128 + 4 + 4 * 128)
