@@ -151,6 +151,8 @@ __device__ __forceinline__ void load_rows_128(uint16_t* dst, const uint16_t* src
 }
 
 // ---------------------------------------------------------------------------
+// One workgroup per (chunk, k-head): K K^T and Q K^T once, then for each
+// v-head of the group its decay, A, T and P.
 __global__ void __launch_bounds__(256)
 gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const float* __restrict__ log_g, const float* __restrict__ beta,
@@ -158,27 +160,31 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_base,
                    int nc_dense)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t sK[C * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[C * LDK];
-    __shared__ __attribute__((aligned(16))) float sA[C * LDF];
-    __shared__ __attribute__((aligned(16))) float sT[C * LDF];
-    __shared__ __attribute__((aligned(16))) uint16_t sP[C * LDC];
+    // K and Q (bf16) while the Grams are formed; afterwards the same bytes
+    // hold A and T (fp32) of the v-head being solved.
+    __shared__ __attribute__((aligned(16))) unsigned char sRaw[2 * C * LDK * sizeof(uint16_t)];
+    __shared__ __attribute__((aligned(16))) float sKK[C * LDF];
+    __shared__ __attribute__((aligned(16))) float sQK[C * LDF];
     __shared__ float sG[C], sB[C];
+    uint16_t* sK = reinterpret_cast<uint16_t*>(sRaw);
+    uint16_t* sQ = sK + C * LDK;
+    float* sA = reinterpret_cast<float*>(sRaw);
+    float* sT = sA + C * LDF;
+    static_assert(2 * C * LDF * sizeof(float) <= sizeof(sRaw), "A and T must fit where K and Q were");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, n = lane & 15;
-    const int x = blockIdx.x, vh = blockIdx.y;
-    const int kh = vh / (Hv / Hk);
+    const int x = blockIdx.x, kh = blockIdx.y;
+    const int G = Hv / Hk;
 
-    // which sequence and chunk this workgroup serves
     int b, c;
     if (!cu) {
         b = x / nc_dense;
         c = x % nc_dense;
     } else {
         if (x >= chunk_base[B]) return;   // beyond the last chunk
-        int lo = 0, hi = B - 1;  // last b with chunk_base[b] <= x
+        int lo = 0, hi = B - 1;           // last b with chunk_base[b] <= x
         while (lo < hi) {
             int mid = (lo + hi + 1) >> 1;
             if (chunk_base[mid] <= x) lo = mid; else hi = mid - 1;
@@ -191,107 +197,408 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     row0 += (long)c * C;
     const int L = (int)min((long)C, len - (long)c * C);
 
-    load_rows_128<256>(sK, k, row0, L, Hk, kh, tid);
-    load_rows_128<256>(sQ, q, row0, L, Hk, kh, tid);
-    for (int e = tid; e < C * LDF; e += 256) sT[e] = 0.f;
-    if (w == 0) {
-        float gv = 0.f, bv = 0.f;
-        if (lane < L) {
-            gv = log_g[(size_t)(row0 + lane) * Hv + vh];
-            bv = beta[(size_t)(row0 + lane) * Hv + vh];
+    {   // K and Q rows, all loads in flight before any store
+        uint4 kr[4], qr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
+            kr[i] = qr[i] = make_uint4(0, 0, 0, 0);
+            if (r < L) {
+                const size_t off = ((size_t)(row0 + r) * Hk + kh) * D + c8;
+                kr[i] = *reinterpret_cast<const uint4*>(k + off);
+                qr[i] = *reinterpret_cast<const uint4*>(q + off);
+            }
         }
-        sG[lane] = wave_inclusive_sum(gv, lane);
-        sB[lane] = bv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
+            *reinterpret_cast<uint4*>(sK + r * LDK + c8) = kr[i];
+            *reinterpret_cast<uint4*>(sQ + r * LDK + c8) = qr[i];
+        }
     }
     __syncthreads();
 
-    // K K^T -> A (fp32, strictly lower, beta_r Gamma_rs folded in) and
-    // Q K^T -> P (bf16, lower incl. diagonal); 16x16 tiles, 20 lower ones.
-    for (int t = w; t < 32; t += 4) {
-        const bool is_kk = t < 16;
-        const int tt = t & 15;
-        const int rb = tt >> 2, cb = tt & 3;
-        if (cb > rb) {
-            if (!is_kk)  // upper P tiles are zero
-                for (int r = 0; r < 4; ++r) sP[(16 * rb + 4 * g + r) * LDC + 16 * cb + n] = 0;
-            continue;
-        }
+    // raw Grams, lower 16x16 tiles (diagonal tiles whole)
+    for (int t = w; t < 20; t += 4) {
+        const bool is_kk = t < 10;
+        int tt = is_kk ? t : t - 10, rb = 0;
+        while (tt > rb) { tt -= rb + 1; ++rb; }
+        const int cb = tt;
         const uint16_t* a_src = is_kk ? sK : sQ;
         f32x4 acc = zero4();
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
             acc = mfma_bf16(frag_a(a_src, LDK, 16 * rb + n, 32 * kk, g),
                             frag_a(sK, LDK, 16 * cb + n, 32 * kk, g), acc);
+        float* dst = is_kk ? sKK : sQK;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * rb + 4 * g + r, col = 16 * cb + n;
-            if (is_kk) {
-                sA[row * LDF + col] = col < row ? sB[row] * __expf(sG[row] - sG[col]) * acc[r] : 0.f;
-            } else {
-                const float p = col <= row ? __expf(sG[row] - sG[col]) * acc[r] : 0.f;
-                sP[row * LDC + col] = __builtin_bit_cast(uint16_t, (__bf16)p);
+        for (int r = 0; r < 4; ++r) dst[(16 * rb + 4 * g + r) * LDF + 16 * cb + n] = acc[r];
+    }
+    __syncthreads();
+
+    for (int gi = 0; gi < G; ++gi) {
+        const int vh = kh * G + gi;
+        if (w == 0) {
+            float gv = 0.f, bv = 0.f;
+            if (lane < L) {
+                gv = log_g[(size_t)(row0 + lane) * Hv + vh];
+                bv = beta[(size_t)(row0 + lane) * Hv + vh];
             }
-        }
-    }
-    __syncthreads();
-
-    // T_ii = (I + A_ii)^-1 for the four 16x16 diagonal blocks: wave w, lane j
-    // walks column j of block w by forward substitution.
-    if (lane < 16) {
-        const int j = lane, o = 16 * w;
-        float xcol[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) xcol[r] = r == j ? 1.f : 0.f;
-#pragma unroll
-        for (int r = 1; r < 16; ++r) {
-            float s = 0.f;
-#pragma unroll
-            for (int m = 0; m < r; ++m) s += sA[(o + r) * LDF + o + m] * xcol[m];
-            if (r > j) xcol[r] = -s;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sT[(o + r) * LDF + o + j] = xcol[r];
-    }
-    __syncthreads();
-
-    // Blocks below the diagonal, by distance d:  T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj.
-    for (int d = 1; d < 4; ++d) {
-        if (w < 4 - d) {
-            const int i = w + d, j = w;
-            f32x4 acc = zero4();
-            for (int m = j; m < i; ++m)
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    acc = mfma_f32(sA[(16 * i + n) * LDF + 16 * m + 4 * s + g],
-                                   sT[(16 * m + 4 * s + g) * LDF + 16 * j + n], acc);
-            // acc (lane 16g+n, reg r) holds M[4g + r][n]; use it as the B operand
-            // with k = 4g + s at step s.
-            f32x4 t = zero4();
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                t = mfma_f32(sT[(16 * i + n) * LDF + 16 * i + 4 * g + s], acc[s], t);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sT[(16 * i + 4 * g + r) * LDF + 16 * j + n] = -t[r];
+            sG[lane] = wave_inclusive_sum(gv, lane);
+            sB[lane] = bv;
+        } else {
+            for (int e = tid - 64; e < C * LDF; e += 192) sT[e] = 0.f;
         }
         __syncthreads();
-    }
 
-    // Store T then P as bf16 rows of 64.
-    uint16_t* dstT = slots + ((size_t)x * Hv + vh) * SLOT_ELEMS;
-    uint16_t* dstP = dstT + C * C;
-    for (int idx = tid; idx < C * C / 8; idx += 256) {
-        const int r = idx >> 3, c8 = (idx & 7) * 8;
-        s16x8 v;
+        uint16_t* dstT = slots + ((size_t)x * Hv + vh) * SLOT_ELEMS;
+        uint16_t* dstP = dstT + C * C;
+        // A (fp32, LDS) and P (bf16, straight to the workspace), 8 entries per step
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = bf16_bits(sT[r * LDF + c8 + e]);
-        *reinterpret_cast<s16x8*>(dstT + r * C + c8) = v;
-        *reinterpret_cast<uint4*>(dstP + r * C + c8) = *reinterpret_cast<const uint4*>(sP + r * LDC + c8);
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + 256 * i, r = idx >> 3, s0 = (idx & 7) * 8;
+            const float gr = sG[r], br = sB[r];
+            s16x8 pv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int s = s0 + e;
+                // upper-triangle Gram entries were never written: select, never multiply
+                const float gam = s <= r ? __expf(gr - sG[s]) : 0.f;
+                sA[r * LDF + s] = s < r ? br * gam * sKK[r * LDF + s] : 0.f;
+                pv[e] = s <= r ? bf16_bits(gam * sQK[r * LDF + s]) : (short)0;
+            }
+            *reinterpret_cast<s16x8*>(dstP + r * C + s0) = pv;
+        }
+        __syncthreads();
+
+        // T_ii = (I + A_ii)^-1: wave w, lane j walks column j of block w.
+        if (lane < 16) {
+            const int j = lane, o = 16 * w;
+            float xc[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xc[r] = r == j ? 1.f : 0.f;
+#pragma unroll
+            for (int r = 1; r < 16; ++r) {
+                const float4* arow = reinterpret_cast<const float4*>(sA + (o + r) * LDF + o);
+                float a[16];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 t4 = arow[q4];
+                    a[4 * q4] = t4.x; a[4 * q4 + 1] = t4.y; a[4 * q4 + 2] = t4.z; a[4 * q4 + 3] = t4.w;
+                }
+                float s = 0.f;
+#pragma unroll
+                for (int m = 0; m < r; ++m) s += a[m] * xc[m];
+                if (r > j) xc[r] = -s;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sT[(o + r) * LDF + o + j] = xc[r];
+        }
+        __syncthreads();
+
+        // blocks below the diagonal, by distance d: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
+        for (int d = 1; d < 4; ++d) {
+            if (w < 4 - d) {
+                const int i = w + d, j = w;
+                f32x4 acc = zero4();
+                for (int m = j; m < i; ++m)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        acc = mfma_f32(sA[(16 * i + n) * LDF + 16 * m + 4 * s + g],
+                                       sT[(16 * m + 4 * s + g) * LDF + 16 * j + n], acc);
+                // acc (lane 16g+n, reg r) = M[4g + r][n]: the B operand with k = 4g + s at step s
+                f32x4 t = zero4();
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    t = mfma_f32(sT[(16 * i + n) * LDF + 16 * i + 4 * g + s], acc[s], t);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sT[(16 * i + 4 * g + r) * LDF + 16 * j + n] = -t[r];
+            }
+            __syncthreads();
+        }
+
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + 256 * i, r = idx >> 3, c8 = (idx & 7) * 8;
+            s16x8 tv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tv[e] = bf16_bits(sT[r * LDF + c8 + e]);
+            *reinterpret_cast<s16x8*>(dstT + r * C + c8) = tv;
+        }
+        __syncthreads();   // sG, sA and sT are rewritten by the next v-head
     }
 }
 
 // ---------------------------------------------------------------------------
+// Operands of one chunk for the spine, as the compute waves read them.
+struct alignas(16) SpineBuf {
+    uint16_t K[C * LDK];        // K, row-major (A operand of K h)
+    uint16_t Q[C * LDK];        // Q, row-major (A operand of Q h)
+    uint16_t Kt[D * LDC];       // K^T (A operand of K^T Delta)
+    uint16_t T[C * LDC];        // (I + A)^-1
+    uint16_t P[C * LDC];        // lower_incl(Gamma o Q K^T)
+    uint16_t Vt[TILE_COLS * LDC];  // this workgroup's 32 columns of V, transposed
+    float gam[C];               // exp(G_r)
+    float el[C];                // exp(G_L - G_r)
+    float beta[C];
+    float gamL;                 // exp(G_L)
+};
+
+// One chunk's worth of global data in a loader thread's registers.
+struct SpineRegs {
+    uint4 k[8], q[8], t[4], p[4], v[2];
+    float g, b;
+};
+
+// Two loader waves (128 threads, lt = 0..127) fetch chunk rows [r0, r0 + L)
+// into registers; every load is issued before any is used.
+__device__ __forceinline__ void spine_fetch(SpineRegs& R, const uint16_t* __restrict__ q,
+                                            const uint16_t* __restrict__ k,
+                                            const uint16_t* __restrict__ v,
+                                            const float* __restrict__ log_g,
+                                            const float* __restrict__ beta,
+                                            const uint16_t* __restrict__ slot, long r0, int L,
+                                            int Hk, int Hv, int kh, int vh, int tile, int lt)
+{
+    const int rb = lt >> 4, cb = lt & 15;   // 8x8 block of K and Q
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 8 * rb + i;
+        R.k[i] = R.q[i] = make_uint4(0, 0, 0, 0);
+        if (row < L) {
+            const size_t off = ((size_t)(r0 + row) * Hk + kh) * D + 8 * cb;
+            R.k[i] = *reinterpret_cast<const uint4*>(k + off);
+            R.q[i] = *reinterpret_cast<const uint4*>(q + off);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = lt + 128 * i, r = idx >> 3, c8 = (idx & 7) * 8;
+        R.t[i] = *reinterpret_cast<const uint4*>(slot + r * C + c8);
+        R.p[i] = *reinterpret_cast<const uint4*>(slot + C * C + r * C + c8);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int idx = lt + 128 * i, r = idx >> 2, c8 = (idx & 3) * 8;
+        R.v[i] = make_uint4(0, 0, 0, 0);
+        if (r < L) R.v[i] = *reinterpret_cast<const uint4*>(v + ((size_t)(r0 + r) * Hv + vh) * D + tile * TILE_COLS + c8);
+    }
+    R.g = R.b = 0.f;
+    if (lt < 64 && lt < L) {
+        R.g = log_g[(size_t)(r0 + lt) * Hv + vh];
+        R.b = beta[(size_t)(r0 + lt) * Hv + vh];
+    }
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& u, int i) {
+    return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+// Halves e of two packed bf16 words: (lo's, hi's) as one word.
+__device__ __forceinline__ uint32_t pair_half(uint32_t lo, uint32_t hi, int e) {
+    return (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+}
+
+// Stores a fetched chunk into `sb`: K, Q and T, P rows as they are; K^T by
+// transposing each thread's 8x8 block in registers; V transposed element-wise.
+__device__ __forceinline__ void spine_store(SpineBuf& sb, const SpineRegs& R, int lt)
+{
+    const int rb = lt >> 4, cb = lt & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        *reinterpret_cast<uint4*>(sb.K + (8 * rb + i) * LDK + 8 * cb) = R.k[i];
+        *reinterpret_cast<uint4*>(sb.Q + (8 * rb + i) * LDK + 8 * cb) = R.q[i];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {   // column e of the block = row 8 cb + e of K^T
+        uint4 o;
+        o.x = pair_half(word_of(R.k[0], e >> 1), word_of(R.k[1], e >> 1), e);
+        o.y = pair_half(word_of(R.k[2], e >> 1), word_of(R.k[3], e >> 1), e);
+        o.z = pair_half(word_of(R.k[4], e >> 1), word_of(R.k[5], e >> 1), e);
+        o.w = pair_half(word_of(R.k[6], e >> 1), word_of(R.k[7], e >> 1), e);
+        *reinterpret_cast<uint4*>(sb.Kt + (8 * cb + e) * LDC + 8 * rb) = o;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = lt + 128 * i, r = idx >> 3, c8 = (idx & 7) * 8;
+        *reinterpret_cast<uint4*>(sb.T + r * LDC + c8) = R.t[i];
+        *reinterpret_cast<uint4*>(sb.P + r * LDC + c8) = R.p[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int idx = lt + 128 * i, r = idx >> 2, c8 = (idx & 3) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t wv = word_of(R.v[i], e >> 1);
+            sb.Vt[(c8 + e) * LDC + r] = (uint16_t)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
+        }
+    }
+    if (lt < 64) {   // wave-uniform: the first loader wave
+        const float Gr = wave_inclusive_sum(R.g, lt);
+        const float GL = __shfl(Gr, 63, 64);
+        sb.gam[lt] = __expf(Gr);
+        sb.el[lt] = __expf(GL - Gr);
+        sb.beta[lt] = R.b;
+        if (lt == 0) sb.gamL = __expf(GL);
+    }
+}
+
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// One compute wave, one chunk, 16 columns (wave w of the workgroup).  LDS
+// fragment reads are issued one group ahead of the MFMAs that consume them,
+// so that a single wave per SIMD does not wait out each read's latency.
 template <bool kOutF32>
-__global__ void __launch_bounds__(128)
+__device__ __forceinline__ void spine_step(const SpineBuf& sb, f32x4 (&h)[8], void* __restrict__ out,
+                                           long r0, int L, int Hv, int vh, int col, int w, int g, int n)
+{
+    s16x8 hb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) hb[kk] = frag_b(h[2 * kk], h[2 * kk + 1]);
+
+    // X = K h, Y = Q h: 4 k-steps x 8 independent accumulators
+    f32x4 X[4], Y[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) X[cb] = Y[cb] = zero4();
+    s16x8 fa[8], fb[8];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        fa[cb] = frag_a(sb.K, LDK, 16 * cb + n, 0, g);
+        fa[4 + cb] = frag_a(sb.Q, LDK, 16 * cb + n, 0, g);
+    }
+    float4 gm4[4], bt4[4], el4[4];
+    uint2 vv[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        s16x8 (&cur)[8] = (kk & 1) ? fb : fa;
+        s16x8 (&nxt)[8] = (kk & 1) ? fa : fb;
+        if (kk < 3) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                nxt[cb] = frag_a(sb.K, LDK, 16 * cb + n, 32 * (kk + 1), g);
+                nxt[4 + cb] = frag_a(sb.Q, LDK, 16 * cb + n, 32 * (kk + 1), g);
+            }
+        } else {
+            // per-row scalars of the next phases, and the first T fragments
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const int row = 16 * cb + 4 * g;
+                gm4[cb] = *reinterpret_cast<const float4*>(sb.gam + row);
+                bt4[cb] = *reinterpret_cast<const float4*>(sb.beta + row);
+                el4[cb] = *reinterpret_cast<const float4*>(sb.el + row);
+                vv[cb] = *reinterpret_cast<const uint2*>(sb.Vt + (16 * w + n) * LDC + row);
+            }
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) nxt[cb] = frag_a(sb.T, LDC, 16 * cb + n, 0, g);
+            nxt[4] = frag_a(sb.T, LDC, 32 + n, 32, g);
+            nxt[5] = frag_a(sb.T, LDC, 48 + n, 32, g);
+        }
+        sched_fence();
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            X[cb] = mfma_bf16(cur[cb], hb[kk], X[cb]);
+            Y[cb] = mfma_bf16(cur[4 + cb], hb[kk], Y[cb]);
+        }
+        sched_fence();
+    }
+    s16x8 (&ft)[8] = fa;   // T fragments (the last k-step's "next" buffer)
+
+    // R = beta (V - gamma X) in place of X; gamma Y in place of Y
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const float gmr[4] = {gm4[cb].x, gm4[cb].y, gm4[cb].z, gm4[cb].w};
+        const float btr[4] = {bt4[cb].x, bt4[cb].y, bt4[cb].z, bt4[cb].w};
+        const float vr[4] = {bf16_bits_to_f32((uint16_t)(vv[cb].x & 0xffffu)), bf16_bits_to_f32((uint16_t)(vv[cb].x >> 16)),
+                             bf16_bits_to_f32((uint16_t)(vv[cb].y & 0xffffu)), bf16_bits_to_f32((uint16_t)(vv[cb].y >> 16))};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            X[cb][r] = btr[r] * (vr[r] - gmr[r] * X[cb][r]);
+            Y[cb][r] *= gmr[r];
+        }
+    }
+    const s16x8 rb0 = frag_b(X[0], X[1]), rb1 = frag_b(X[2], X[3]);
+
+    // Delta = T R (T lower triangular: rows < 32 need only k < 32); meanwhile
+    // fetch the first half of the K^T fragments
+    s16x8 fk[8];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        fk[2 * db] = frag_a(sb.Kt, LDC, 16 * db + n, 0, g);
+        fk[2 * db + 1] = frag_a(sb.Kt, LDC, 16 * db + n, 32, g);
+    }
+    sched_fence();
+    f32x4 Dl[4];
+    Dl[0] = mfma_bf16(ft[0], rb0, zero4());
+    Dl[1] = mfma_bf16(ft[1], rb0, zero4());
+    Dl[2] = mfma_bf16(ft[2], rb0, zero4());
+    Dl[3] = mfma_bf16(ft[3], rb0, zero4());
+    Dl[2] = mfma_bf16(ft[4], rb1, Dl[2]);
+    Dl[3] = mfma_bf16(ft[5], rb1, Dl[3]);
+    sched_fence();
+    const s16x8 db0 = frag_b(Dl[0], Dl[1]), db1 = frag_b(Dl[2], Dl[3]);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        Dl[cb][0] *= el4[cb].x; Dl[cb][1] *= el4[cb].y;
+        Dl[cb][2] *= el4[cb].z; Dl[cb][3] *= el4[cb].w;
+    }
+    const s16x8 ds0 = frag_b(Dl[0], Dl[1]), ds1 = frag_b(Dl[2], Dl[3]);
+
+    // h <- gamma_L h + K^T (exp(G_L - G) Delta): two groups of 4 row blocks
+    const float gl = sb.gamL;
+    s16x8 fk2[8];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        fk2[2 * db] = frag_a(sb.Kt, LDC, 16 * (db + 4) + n, 0, g);
+        fk2[2 * db + 1] = frag_a(sb.Kt, LDC, 16 * (db + 4) + n, 32, g);
+    }
+    sched_fence();
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        f32x4 acc = h[db] * gl;
+        acc = mfma_bf16(fk[2 * db], ds0, acc);
+        h[db] = mfma_bf16(fk[2 * db + 1], ds1, acc);
+    }
+    sched_fence();
+    s16x8 fp[6];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) fp[cb] = frag_a(sb.P, LDC, 16 * cb + n, 0, g);
+    fp[4] = frag_a(sb.P, LDC, 32 + n, 32, g);
+    fp[5] = frag_a(sb.P, LDC, 48 + n, 32, g);
+    sched_fence();
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        f32x4 acc = h[db + 4] * gl;
+        acc = mfma_bf16(fk2[2 * db], ds0, acc);
+        h[db + 4] = mfma_bf16(fk2[2 * db + 1], ds1, acc);
+    }
+    sched_fence();
+
+    // O = gamma Y + P Delta, for the rows of the chunk
+    f32x4 O[4];
+    O[0] = mfma_bf16(fp[0], db0, Y[0]);
+    O[1] = mfma_bf16(fp[1], db0, Y[1]);
+    O[2] = mfma_bf16(fp[2], db0, Y[2]);
+    O[3] = mfma_bf16(fp[3], db0, Y[3]);
+    O[2] = mfma_bf16(fp[4], db1, O[2]);
+    O[3] = mfma_bf16(fp[5], db1, O[3]);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * cb + 4 * g + r;
+            if (row < L) {
+                const size_t off = ((size_t)(r0 + row) * Hv + vh) * D + col;
+                if (kOutF32) reinterpret_cast<float*>(out)[off] = O[cb][r];
+                else reinterpret_cast<uint16_t*>(out)[off] = f32_to_bf16_bits(O[cb][r]);
+            }
+        }
+}
+
+// One workgroup per (sequence, v-head, 32 dv columns): waves 0-1 compute
+// (16 columns each, state in registers), waves 2-3 keep the next chunk in
+// LDS and the one after it in registers.
+template <bool kOutF32>
+__global__ void __launch_bounds__(256)
 gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const float* __restrict__ log_g,
                  const float* __restrict__ beta, const float* h0, void* __restrict__ out,
@@ -299,154 +606,65 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_base,
                  int nc_dense, long n_slots)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t sK[C * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[C * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t sKt[D * LDC];
-    __shared__ __attribute__((aligned(16))) uint16_t sT[C * LDC];
-    __shared__ __attribute__((aligned(16))) uint16_t sP[C * LDC];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[C * (TILE_COLS + 8)];
-    __shared__ float sGam[C], sEL[C], sB[C];
-    __shared__ float sGamL;
+    __shared__ SpineBuf buf[2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, n = lane & 15;
-    const int vh = blockIdx.x / N_TILES;
-    const int tile = blockIdx.x % N_TILES;
+    // Workgroup i runs on XCD i % 8.  Map the grid so that the workgroups of
+    // one k-head (its v-heads and column tiles) share an XCD and its L2.
+    const int W = gridDim.x;
+    const int lin = (W % 8 == 0) ? (blockIdx.x % 8) * (W / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int vh = lin / N_TILES;
+    const int tile = lin % N_TILES;
     const int b = blockIdx.y;
     const int kh = vh / (Hv / Hk);
-    const int col = tile * TILE_COLS + 16 * w + n;   // this lane's dv column
+    const int col = tile * TILE_COLS + 16 * (w & 1) + n;   // compute lane's dv column
 
     long row0, len;
     seq_rows(cu, b, T, &row0, &len);
     const long slot0 = cu ? (long)chunk_base[b] : (long)b * nc_dense;
-    const int nc = (int)((len + C - 1) / C);
+    int nc = (int)((len + C - 1) / C);
+    // Only a decreasing cu_seqlens (a broken precondition) can make this
+    // bind; it keeps every read inside the workspace.
+    if (slot0 + nc > n_slots) nc = (int)max(0L, n_slots - slot0);
+    auto rows_of = [&](int c) { return (int)min((long)C, len - (long)c * C); };
 
-    // the state: h[16 db + 4 g + r][col] in acc tile db, register r
     f32x4 h[8];
     const size_t hoff = ((size_t)b * Hv + vh) * D * D;
+    const uint16_t* slot_base = slots + ((size_t)slot0 * Hv + vh) * SLOT_ELEMS;
+    const size_t slot_stride = (size_t)Hv * SLOT_ELEMS;
+    const int lt = tid - 128;
+    SpineRegs R;
+    if (w < 2) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+        for (int db = 0; db < 8; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            h[db][r] = h0 ? h0[hoff + (size_t)(16 * db + 4 * g + r) * D + col] : 0.f;
+            for (int r = 0; r < 4; ++r)
+                h[db][r] = h0 ? h0[hoff + (size_t)(16 * db + 4 * g + r) * D + col] : 0.f;
+    } else if (nc > 0) {
+        spine_fetch(R, q, k, v, log_g, beta, slot_base, row0, rows_of(0), Hk, Hv, kh, vh, tile, lt);
+        spine_store(buf[0], R, lt);
+        if (nc > 1)
+            spine_fetch(R, q, k, v, log_g, beta, slot_base + slot_stride, row0 + C, rows_of(1), Hk, Hv,
+                        kh, vh, tile, lt);
+    }
+    __syncthreads();
 
     for (int c = 0; c < nc; ++c) {
-        // Only reachable when cu_seqlens decreases somewhere (a broken
-        // precondition): never read past the workspace.  Uniform per workgroup.
-        if (slot0 + c >= n_slots) break;
         const long r0 = row0 + (long)c * C;
-        const int L = (int)min((long)C, len - (long)c * C);
-        __syncthreads();  // the previous chunk is done with the LDS tiles
-
-        // K (both layouts), Q, V columns of this workgroup, T, P
-        for (int idx = tid; idx < C * (D / 8); idx += 128) {
-            const int r = idx >> 4, c8 = (idx & 15) * 8;
-            uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-            if (r < L) {
-                const size_t off = ((size_t)(r0 + r) * Hk + kh) * D + c8;
-                kv = *reinterpret_cast<const uint4*>(k + off);
-                qv = *reinterpret_cast<const uint4*>(q + off);
-            }
-            *reinterpret_cast<uint4*>(sK + r * LDK + c8) = kv;
-            *reinterpret_cast<uint4*>(sQ + r * LDK + c8) = qv;
-            const uint16_t* ke = reinterpret_cast<const uint16_t*>(&kv);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sKt[(c8 + e) * LDC + r] = ke[e];
-        }
-        const uint16_t* slot = slots + ((size_t)(slot0 + c) * Hv + vh) * SLOT_ELEMS;
-        for (int idx = tid; idx < C * C / 8; idx += 128) {
-            const int r = idx >> 3, c8 = (idx & 7) * 8;
-            *reinterpret_cast<uint4*>(sT + r * LDC + c8) = *reinterpret_cast<const uint4*>(slot + r * C + c8);
-            *reinterpret_cast<uint4*>(sP + r * LDC + c8) = *reinterpret_cast<const uint4*>(slot + C * C + r * C + c8);
-        }
-        for (int idx = tid; idx < C * (TILE_COLS / 8); idx += 128) {
-            const int r = idx >> 2, c8 = (idx & 3) * 8;
-            uint4 vv = make_uint4(0, 0, 0, 0);
-            if (r < L) vv = *reinterpret_cast<const uint4*>(v + ((size_t)(r0 + r) * Hv + vh) * D + tile * TILE_COLS + c8);
-            *reinterpret_cast<uint4*>(sV + r * (TILE_COLS + 8) + c8) = vv;
-        }
-        if (w == 0) {
-            float gv = 0.f, bv = 0.f;
-            if (lane < L) {
-                gv = log_g[(size_t)(r0 + lane) * Hv + vh];
-                bv = beta[(size_t)(r0 + lane) * Hv + vh];
-            }
-            const float G = wave_inclusive_sum(gv, lane);
-            const float GL = __shfl(G, 63, 64);
-            sGam[lane] = __expf(G);
-            sEL[lane] = __expf(GL - G);
-            sB[lane] = bv;
-            if (lane == 0) sGamL = __expf(GL);
+        if (w < 2) {
+            spine_step<kOutF32>(buf[c & 1], h, out, r0, rows_of(c), Hv, vh, col, w, g, n);
+        } else if (c + 1 < nc) {
+            spine_store(buf[(c + 1) & 1], R, lt);       // chunk c + 1, fetched last iteration
+            if (c + 2 < nc)
+                spine_fetch(R, q, k, v, log_g, beta, slot_base + (size_t)(c + 2) * slot_stride,
+                            r0 + 2 * C, rows_of(c + 2), Hk, Hv, kh, vh, tile, lt);
         }
         __syncthreads();
-
-        // X = K h and Y = Q h for this wave's 16 columns
-        s16x8 hb[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) hb[kk] = frag_b(h[2 * kk], h[2 * kk + 1]);
-        f32x4 X[4], Y[4];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            X[cb] = zero4();
-            Y[cb] = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                X[cb] = mfma_bf16(frag_a(sK, LDK, 16 * cb + n, 32 * kk, g), hb[kk], X[cb]);
-                Y[cb] = mfma_bf16(frag_a(sQ, LDK, 16 * cb + n, 32 * kk, g), hb[kk], Y[cb]);
-            }
-        }
-        // R = beta (V - gamma X), in place
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * cb + 4 * g + r;
-                const float vv = bf16_bits_to_f32(sV[row * (TILE_COLS + 8) + 16 * w + n]);
-                X[cb][r] = sB[row] * (vv - sGam[row] * X[cb][r]);
-                Y[cb][r] *= sGam[row];
-            }
-        const s16x8 rb0 = frag_b(X[0], X[1]), rb1 = frag_b(X[2], X[3]);
-        // Delta = T R (T is lower triangular: rows < 32 need only k < 32)
-        f32x4 Dl[4];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            Dl[cb] = mfma_bf16(frag_a(sT, LDC, 16 * cb + n, 0, g), rb0, zero4());
-            if (cb >= 2) Dl[cb] = mfma_bf16(frag_a(sT, LDC, 16 * cb + n, 32, g), rb1, Dl[cb]);
-        }
-        const s16x8 db0 = frag_b(Dl[0], Dl[1]), db1 = frag_b(Dl[2], Dl[3]);
-        // O = gamma Y + P Delta, written for the rows of the chunk
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            f32x4 o = mfma_bf16(frag_a(sP, LDC, 16 * cb + n, 0, g), db0, Y[cb]);
-            if (cb >= 2) o = mfma_bf16(frag_a(sP, LDC, 16 * cb + n, 32, g), db1, o);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * cb + 4 * g + r;
-                if (row < L) {
-                    const size_t off = ((size_t)(r0 + row) * Hv + vh) * D + col;
-                    if (kOutF32) reinterpret_cast<float*>(out)[off] = o[r];
-                    else reinterpret_cast<uint16_t*>(out)[off] = f32_to_bf16_bits(o[r]);
-                }
-            }
-        }
-        // h <- gamma_L h + K^T (exp(G_L - G) Delta)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Dl[cb][r] *= sEL[16 * cb + 4 * g + r];
-        const s16x8 ds0 = frag_b(Dl[0], Dl[1]), ds1 = frag_b(Dl[2], Dl[3]);
-        const float gl = sGamL;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-            f32x4 acc = h[db] * gl;
-            acc = mfma_bf16(frag_a(sKt, LDC, 16 * db + n, 0, g), ds0, acc);
-            acc = mfma_bf16(frag_a(sKt, LDC, 16 * db + n, 32, g), ds1, acc);
-            h[db] = acc;
-        }
     }
 
-    if (h_final) {
+    if (w < 2 && h_final) {
 #pragma unroll
         for (int db = 0; db < 8; ++db)
 #pragma unroll
@@ -475,9 +693,8 @@ bool prefill_mfma_accepts(const PrefillArgs& a)
 
 Geometry prefill_mfma_geometry(const PrefillArgs& a)
 {
-    Geometry g{"gdn_wy_prep_kernel+gdn_spine_kernel", {(unsigned)(a.Hv * N_TILES), (unsigned)a.B, 1u}, 128u,
-               (unsigned)(sizeof(uint16_t) * (2 * C * LDK + D * LDC + 2 * C * LDC + C * (TILE_COLS + 8)) +
-                          sizeof(float) * (3 * C + 1))};
+    Geometry g{"gdn_wy_prep_kernel+gdn_spine_kernel", {(unsigned)(a.Hv * N_TILES), (unsigned)a.B, 1u}, 256u,
+               (unsigned)(2 * sizeof(SpineBuf))};
     return g;
 }
 
@@ -492,17 +709,17 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
         hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.B, a.T, base);
     }
     if (n_slots > 0) {
-        hipLaunchKernelGGL(gdn_wy_prep_kernel, dim3((unsigned)n_slots, a.Hv), dim3(256), 0, s,
+        hipLaunchKernelGGL(gdn_wy_prep_kernel, dim3((unsigned)n_slots, a.Hk), dim3(256), 0, s,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, a.log_g, a.beta, slots, a.B,
                            a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense);
     }
     dim3 grid(a.Hv * N_TILES, a.B);
     if (a.out_dtype == 0)
-        hipLaunchKernelGGL((gdn_spine_kernel<true>), grid, dim3(128), 0, s, (const uint16_t*)a.q,
+        hipLaunchKernelGGL((gdn_spine_kernel<true>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, a.log_g, a.beta, a.h0, a.out,
                            a.h_final, slots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense, n_slots);
     else
-        hipLaunchKernelGGL((gdn_spine_kernel<false>), grid, dim3(128), 0, s, (const uint16_t*)a.q,
+        hipLaunchKernelGGL((gdn_spine_kernel<false>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, a.log_g, a.beta, a.h0, a.out,
                            a.h_final, slots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense, n_slots);
     return hipGetLastError();
