@@ -39,8 +39,11 @@ namespace {
 
 constexpr int C = 64;        // chunk rows
 constexpr int D = 128;       // dk = dv
-constexpr int LDK = D + 8;   // LDS row stride (bf16) of K and Q
-constexpr int LDC = C + 8;   // LDS row stride (bf16) of T, P and K^T
+// LDS row strides.  A fragment read is 16 lanes x 8 bytes from 16 consecutive
+// rows; rows that start 8 bytes apart modulo 128 put those 16 reads on
+// distinct banks, so bf16 rows are padded by 4 elements (8 bytes).
+constexpr int LDK = D + 4;   // LDS row stride (bf16) of K and Q: 264 bytes
+constexpr int LDC = C + 4;   // LDS row stride (bf16) of T, P, K^T and V^T: 136 bytes
 constexpr int LDF = C + 4;   // LDS row stride (fp32) of A and the fp32 T
 constexpr int TILE_COLS = 32;            // dv columns per spine workgroup
 constexpr int N_TILES = D / TILE_COLS;   // 4
@@ -79,6 +82,12 @@ __device__ __forceinline__ short bf16_bits(float x) {
 __device__ __forceinline__ s16x8 frag_b(f32x4 lo, f32x4 hi) {
     return s16x8{bf16_bits(lo[0]), bf16_bits(lo[1]), bf16_bits(lo[2]), bf16_bits(lo[3]),
                  bf16_bits(hi[0]), bf16_bits(hi[1]), bf16_bits(hi[2]), bf16_bits(hi[3])};
+}
+
+// 16 bytes to an LDS row that is only 8-byte aligned.
+__device__ __forceinline__ void store16(uint16_t* dst, const uint4& v) {
+    reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
+    reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -162,7 +171,9 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 {
     // K and Q (bf16) while the Grams are formed; afterwards the same bytes
     // hold A and T (fp32) of the v-head being solved.
-    __shared__ __attribute__((aligned(16))) unsigned char sRaw[2 * C * LDK * sizeof(uint16_t)];
+    constexpr size_t kRaw = 2 * C * LDF * sizeof(float) > 2 * C * LDK * sizeof(uint16_t)
+                                ? 2 * C * LDF * sizeof(float) : 2 * C * LDK * sizeof(uint16_t);
+    __shared__ __attribute__((aligned(16))) unsigned char sRaw[kRaw];
     __shared__ __attribute__((aligned(16))) float sKK[C * LDF];
     __shared__ __attribute__((aligned(16))) float sQK[C * LDF];
     __shared__ float sG[C], sB[C];
@@ -212,8 +223,8 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
-            *reinterpret_cast<uint4*>(sK + r * LDK + c8) = kr[i];
-            *reinterpret_cast<uint4*>(sQ + r * LDK + c8) = qr[i];
+            store16(sK + r * LDK + c8, kr[i]);
+            store16(sQ + r * LDK + c8, qr[i]);
         }
     }
     __syncthreads();
@@ -347,46 +358,72 @@ struct alignas(16) SpineBuf {
 // One chunk's worth of global data in a loader thread's registers.
 struct SpineRegs {
     uint4 k[8], q[8], t[4], p[4], v[2];
-    float g, b;
+    float g = 0.f, b = 0.f;
 };
 
-// Two loader waves (128 threads, lt = 0..127) fetch chunk rows [r0, r0 + L)
-// into registers; every load is issued before any is used.
-__device__ __forceinline__ void spine_fetch(SpineRegs& R, const uint16_t* __restrict__ q,
-                                            const uint16_t* __restrict__ k,
-                                            const uint16_t* __restrict__ v,
-                                            const float* __restrict__ log_g,
-                                            const float* __restrict__ beta,
-                                            const uint16_t* __restrict__ slot, long r0, int L,
-                                            int Hk, int Hv, int kh, int vh, int tile, int lt)
+// Buffer resources (gfx9 family): a wave-uniform base in SGPRs, 32-bit lane
+// byte offsets, and a byte range; reads beyond the range return 0 and writes
+// beyond it are dropped, which is how partial chunks are masked.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load4f(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Per-thread byte offsets of the loader's fetches within one chunk.
+struct LoaderOffsets {
+    uint32_t kq, kq_row;   // row 8 rb + i of K and Q at kq + i * kq_row
+    uint32_t tp[4];        // T pieces (P at + C*C*2)
+    uint32_t v[2];
+    uint32_t gb;           // log_g / beta of row lt (first loader wave)
+};
+
+__device__ __forceinline__ LoaderOffsets loader_offsets(int lt, int Hk, int Hv)
 {
-    const int rb = lt >> 4, cb = lt & 15;   // 8x8 block of K and Q
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 8 * rb + i;
-        R.k[i] = R.q[i] = make_uint4(0, 0, 0, 0);
-        if (row < L) {
-            const size_t off = ((size_t)(r0 + row) * Hk + kh) * D + 8 * cb;
-            R.k[i] = *reinterpret_cast<const uint4*>(k + off);
-            R.q[i] = *reinterpret_cast<const uint4*>(q + off);
-        }
-    }
+    LoaderOffsets o;
+    const int rb = lt >> 4, cb = lt & 15;
+    o.kq_row = (uint32_t)Hk * D * 2u;
+    o.kq = (uint32_t)(8 * rb) * o.kq_row + (uint32_t)(8 * cb) * 2u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int idx = lt + 128 * i, r = idx >> 3, c8 = (idx & 7) * 8;
-        R.t[i] = *reinterpret_cast<const uint4*>(slot + r * C + c8);
-        R.p[i] = *reinterpret_cast<const uint4*>(slot + C * C + r * C + c8);
+        const int idx = lt + 128 * i;
+        o.tp[i] = (uint32_t)((idx >> 3) * C + (idx & 7) * 8) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int idx = lt + 128 * i, r = idx >> 2, c8 = (idx & 3) * 8;
-        R.v[i] = make_uint4(0, 0, 0, 0);
-        if (r < L) R.v[i] = *reinterpret_cast<const uint4*>(v + ((size_t)(r0 + r) * Hv + vh) * D + tile * TILE_COLS + c8);
+        const int idx = lt + 128 * i;
+        o.v[i] = (uint32_t)(idx >> 2) * Hv * D * 2u + (uint32_t)((idx & 3) * 8) * 2u;
     }
-    R.g = R.b = 0.f;
-    if (lt < 64 && lt < L) {
-        R.g = log_g[(size_t)(r0 + lt) * Hv + vh];
-        R.b = beta[(size_t)(r0 + lt) * Hv + vh];
+    o.gb = (uint32_t)(lt & 63) * Hv * 4u;
+    return o;
+}
+
+// Two loader waves (128 threads, lt = 0..127) fetch one chunk into registers;
+// every load is issued before any is used.  Rows >= L read as zero.
+__device__ __forceinline__ void spine_fetch(SpineRegs& R, const LoaderOffsets& o, rsrc_t rk,
+                                            rsrc_t rq, rsrc_t rv, rsrc_t rg, rsrc_t rb_,
+                                            rsrc_t rs, int lt)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        R.k[i] = buf_load16(rk, o.kq + i * o.kq_row);
+        R.q[i] = buf_load16(rq, o.kq + i * o.kq_row);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        R.t[i] = buf_load16(rs, o.tp[i]);
+        R.p[i] = buf_load16(rs, o.tp[i] + C * C * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) R.v[i] = buf_load16(rv, o.v[i]);
+    if (lt < 64) {   // wave-uniform
+        R.g = buf_load4f(rg, o.gb);
+        R.b = buf_load4f(rb_, o.gb);
     }
 }
 
@@ -406,8 +443,8 @@ __device__ __forceinline__ void spine_store(SpineBuf& sb, const SpineRegs& R, in
     const int rb = lt >> 4, cb = lt & 15;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        *reinterpret_cast<uint4*>(sb.K + (8 * rb + i) * LDK + 8 * cb) = R.k[i];
-        *reinterpret_cast<uint4*>(sb.Q + (8 * rb + i) * LDK + 8 * cb) = R.q[i];
+        store16(sb.K + (8 * rb + i) * LDK + 8 * cb, R.k[i]);
+        store16(sb.Q + (8 * rb + i) * LDK + 8 * cb, R.q[i]);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {   // column e of the block = row 8 cb + e of K^T
@@ -416,13 +453,13 @@ __device__ __forceinline__ void spine_store(SpineBuf& sb, const SpineRegs& R, in
         o.y = pair_half(word_of(R.k[2], e >> 1), word_of(R.k[3], e >> 1), e);
         o.z = pair_half(word_of(R.k[4], e >> 1), word_of(R.k[5], e >> 1), e);
         o.w = pair_half(word_of(R.k[6], e >> 1), word_of(R.k[7], e >> 1), e);
-        *reinterpret_cast<uint4*>(sb.Kt + (8 * cb + e) * LDC + 8 * rb) = o;
+        store16(sb.Kt + (8 * cb + e) * LDC + 8 * rb, o);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int idx = lt + 128 * i, r = idx >> 3, c8 = (idx & 7) * 8;
-        *reinterpret_cast<uint4*>(sb.T + r * LDC + c8) = R.t[i];
-        *reinterpret_cast<uint4*>(sb.P + r * LDC + c8) = R.p[i];
+        store16(sb.T + r * LDC + c8, R.t[i]);
+        store16(sb.P + r * LDC + c8, R.p[i]);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -581,17 +618,47 @@ __device__ __forceinline__ void spine_step(const SpineBuf& sb, f32x4 (&h)[8], vo
     O[3] = mfma_bf16(fp[3], db0, Y[3]);
     O[2] = mfma_bf16(fp[4], db1, O[2]);
     O[3] = mfma_bf16(fp[5], db1, O[3]);
+    // hardware RNE conversion; stores through a buffer resource covering the
+    // chunk's L rows, so rows beyond a partial chunk are dropped
+    constexpr uint32_t es = kOutF32 ? 4u : 2u;
+    const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)r0);
+    const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)r0 >> 32));
+    const size_t ru = ((size_t)rhi << 32) | rlo;
+    const rsrc_t ro = make_rsrc(reinterpret_cast<char*>(out) + (ru * Hv + vh) * D * es,
+                                __builtin_amdgcn_readfirstlane((uint32_t)L * Hv * D * es));
+    const uint32_t rs = (uint32_t)Hv * D * es;
+    const uint32_t lane_off = (uint32_t)(4 * g) * rs + (uint32_t)col * es;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = 16 * cb + 4 * g + r;
-            if (row < L) {
-                const size_t off = ((size_t)(r0 + row) * Hv + vh) * D + col;
-                if (kOutF32) reinterpret_cast<float*>(out)[off] = O[cb][r];
-                else reinterpret_cast<uint16_t*>(out)[off] = f32_to_bf16_bits(O[cb][r]);
-            }
+            const uint32_t off = lane_off + (uint32_t)(16 * cb + r) * rs;
+            const float val = O[cb][r];   // by value: never bit-cast a vector element in place
+            if (kOutF32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
+            else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_bits(val), ro, off, 0, 0);
         }
+}
+
+// Chunk c of the sequence at rows [row0, row0 + len): its buffer resources
+// (rows beyond the chunk read as 0), fetched into the loader's registers.
+__device__ __forceinline__ void spine_fetch_chunk(SpineRegs& R, const LoaderOffsets& lo,
+                                                  const uint16_t* q, const uint16_t* k,
+                                                  const uint16_t* v, const float* log_g,
+                                                  const float* beta, const uint16_t* slot_base,
+                                                  size_t slot_stride, long row0, long len, int c,
+                                                  int Hk, int Hv, int kh, int vh, int tile, int lt)
+{
+    // all of these are wave-uniform; say so, so the resources live in SGPRs
+    const long r = row0 + (long)c * C;
+    const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)r);
+    const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)r >> 32));
+    const size_t ru = ((size_t)rhi << 32) | rlo;
+    const uint32_t L = __builtin_amdgcn_readfirstlane((uint32_t)min((long)C, len - (long)c * C));
+    spine_fetch(R, lo, make_rsrc(k + (ru * Hk + kh) * D, L * Hk * D * 2u),
+                make_rsrc(q + (ru * Hk + kh) * D, L * Hk * D * 2u),
+                make_rsrc(v + (ru * Hv + vh) * D + tile * TILE_COLS, L * Hv * D * 2u),
+                make_rsrc(log_g + ru * Hv + vh, L * Hv * 4u), make_rsrc(beta + ru * Hv + vh, L * Hv * 4u),
+                make_rsrc(slot_base + (size_t)c * slot_stride, SLOT_ELEMS * 2u), lt);
 }
 
 // One workgroup per (sequence, v-head, 32 dv columns): waves 0-1 compute
@@ -636,6 +703,7 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const size_t slot_stride = (size_t)Hv * SLOT_ELEMS;
     const int lt = tid - 128;
     SpineRegs R;
+    LoaderOffsets lo;
     if (w < 2) {
 #pragma unroll
         for (int db = 0; db < 8; ++db)
@@ -643,23 +711,24 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             for (int r = 0; r < 4; ++r)
                 h[db][r] = h0 ? h0[hoff + (size_t)(16 * db + 4 * g + r) * D + col] : 0.f;
     } else if (nc > 0) {
-        spine_fetch(R, q, k, v, log_g, beta, slot_base, row0, rows_of(0), Hk, Hv, kh, vh, tile, lt);
+        lo = loader_offsets(lt, Hk, Hv);
+        spine_fetch_chunk(R, lo, q, k, v, log_g, beta, slot_base, slot_stride, row0, len, 0, Hk, Hv,
+                          kh, vh, tile, lt);
         spine_store(buf[0], R, lt);
         if (nc > 1)
-            spine_fetch(R, q, k, v, log_g, beta, slot_base + slot_stride, row0 + C, rows_of(1), Hk, Hv,
-                        kh, vh, tile, lt);
+            spine_fetch_chunk(R, lo, q, k, v, log_g, beta, slot_base, slot_stride, row0, len, 1, Hk,
+                              Hv, kh, vh, tile, lt);
     }
     __syncthreads();
 
     for (int c = 0; c < nc; ++c) {
-        const long r0 = row0 + (long)c * C;
         if (w < 2) {
-            spine_step<kOutF32>(buf[c & 1], h, out, r0, rows_of(c), Hv, vh, col, w, g, n);
+            spine_step<kOutF32>(buf[c & 1], h, out, row0 + (long)c * C, rows_of(c), Hv, vh, col, w, g, n);
         } else if (c + 1 < nc) {
             spine_store(buf[(c + 1) & 1], R, lt);       // chunk c + 1, fetched last iteration
             if (c + 2 < nc)
-                spine_fetch(R, q, k, v, log_g, beta, slot_base + (size_t)(c + 2) * slot_stride,
-                            r0 + 2 * C, rows_of(c + 2), Hk, Hv, kh, vh, tile, lt);
+                spine_fetch_chunk(R, lo, q, k, v, log_g, beta, slot_base, slot_stride, row0, len, c + 2,
+                                  Hk, Hv, kh, vh, tile, lt);
         }
         __syncthreads();
     }
