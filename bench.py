@@ -250,6 +250,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill_t4576_h0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="only run plain device-to-device copies of MIB MiB (the known-size "
+                         "kernel that scales FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -260,6 +263,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     rec = bench_prefill(w, args, torch) if w.kind == "prefill" else bench_verify(w, args, torch)
     print(json.dumps(rec), flush=True)
