@@ -60,6 +60,12 @@ def verify_bytes(B, Hk, Hv, dk, dv, s_io=2, s_out=2, K=4):
             + B * K * Hv * dv * s_out + B * Hv * (K * dv * 4 + K * 4 + K * dk * 2))
 
 
+def fold_bytes(na, Hv, dk, dv, K=4):
+    """Per sequence with na > 0 and v-head: read and write the state once, read
+    the na stashed rows (delta fp32, key bf16) and G."""
+    return sum(Hv * (2 * dk * dv * 4 + n * (dv * 4 + dk * 2) + K * 4) for n in na if n > 0)
+
+
 def kernel_source_sha():
     import glob
     h = hashlib.sha256()
@@ -228,6 +234,19 @@ def bench_verify(w, args, torch):
     ms = total_ms / args.steps
     kern_ms = sum(per) / len(per)
     ach = byt / (kern_ms * 1e-3) / 1e9
+    # the fold that follows a verify (word set by the verify above), on the same sets
+    na_l = inp["na"].tolist()
+    for g in sets:
+        g["na"] = inp["na"].to(d)
+
+    def launch_fold(i):
+        g = sets[i]
+        gdn.gdn_fold(g["table"], g["stash"], g["na"], None, 0, g["flag"], K, w.B, w.Hk, w.Hv, w.dk,
+                     w.dv, ssf, gdn.GDN_BF16, stream=stream)
+
+    _, fper = time_launches(launch_fold, n_sets, args.warmup, args.steps, torch)
+    fold_ms = sum(fper) / len(fper)
+    fbyt = fold_bytes(na_l, w.Hv, w.dk, w.dv, K)
     return {
         "metric": "GDN K=4 write-on-accept verify, achieved HBM GB/s (B=16, Hv=48, d=128)",
         "value": ach, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -238,6 +257,8 @@ def bench_verify(w, args, torch):
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "algorithmic_bytes": byt, "kernel_ms": kern_ms},
         "draft_tokens_per_s": w.B * K / (kern_ms * 1e-3),
+        "fold": {"kernel_ms": fold_ms, "algorithmic_bytes": fbyt, "achieved": fbyt / (fold_ms * 1e-3) / 1e9,
+                 "unit": "GB/s", "frac": fbyt / (fold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "na": na_l},
         "route": route[0] if route else None,
         "input_sets_rotated": n_sets,
     }

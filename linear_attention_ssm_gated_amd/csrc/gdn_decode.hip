@@ -196,6 +196,223 @@ gdn_fold_k4_kernel(float* const* __restrict__ h_table, const float* __restrict__
     }
 }
 
+// dk = dv = 128 verify: one workgroup per (v-head, sequence), every state load
+// issued before any use.  Thread t reads rows 16 (t/32) .. +15 of column group
+// t%32 (4 columns); a wave's load covers two 512-byte row segments.  The 16
+// k.k / q.k dot products are split over all 256 threads and finished with lane
+// shuffles; the 8 slice partials are summed in two LDS passes.  (Splitting a
+// head over several workgroups measured slower: the per-workgroup key loads,
+// dot products and barriers repeat.)
+template <typename TIn, typename TOut>
+__global__ void __launch_bounds__(kThreads)
+gdn_verify_k4_d128_kernel(float* const* __restrict__ h_table, const TIn* __restrict__ q,
+                          const TIn* __restrict__ k, const TIn* __restrict__ v,
+                          const float* __restrict__ gate, const float* __restrict__ beta,
+                          TOut* __restrict__ out, float* __restrict__ stash, int Hk, int Hv,
+                          int qk_stride, int v_stride, int gb_stride, int stash_seq_floats,
+                          uint32_t* __restrict__ engaged_flag)
+{
+    constexpr int D = 128;
+    __shared__ __attribute__((aligned(16))) float sk[kRows][D];
+    __shared__ __attribute__((aligned(16))) float sq[kRows][D];
+    __shared__ __attribute__((aligned(16))) float sv[kRows][D];
+    __shared__ float4 part[kSlices][2 * kRows][kColGroups];
+    __shared__ __attribute__((aligned(16))) float red[2 * kRows][D];
+    __shared__ float sG[kRows], sBeta[kRows], sA[kRows][kRows], sQK[kRows][kRows];
+
+    const int tid = threadIdx.x;
+    const int vh = blockIdx.x, b = blockIdx.y;
+    const int kh = vh / (Hv / Hk);
+    const int sl = tid >> 5, cg = tid & 31;
+
+    const float* h0 = h_table[b] + (size_t)vh * D * D;
+    float4 hv[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+        hv[m] = *reinterpret_cast<const float4*>(h0 + (size_t)(16 * sl + m) * D + 4 * cg);
+
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+        const int idx = tid + 256 * u, which = idx >> 9, r = (idx >> 7) & 3, i = idx & 127;
+        const size_t row = (size_t)b * kRows + r;
+        if (which == 0) sk[r][i] = Elem<TIn>::load(k + row * qk_stride + (size_t)kh * D + i);
+        else if (which == 1) sq[r][i] = Elem<TIn>::load(q + row * qk_stride + (size_t)kh * D + i);
+        else sv[r][i] = Elem<TIn>::load(v + row * v_stride + (size_t)vh * D + i);
+    }
+    if (tid < kRows) {
+        const size_t off = ((size_t)b * kRows + tid) * gb_stride + vh;
+        sG[tid] = gate[off];
+        sBeta[tid] = beta[off];
+    }
+    __syncthreads();
+
+    // partial h0^T k_r and h0^T q_r over this thread's 16 rows
+    float4 acc[2 * kRows];
+#pragma unroll
+    for (int m = 0; m < 2 * kRows; ++m) acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const float4 kk4 = *reinterpret_cast<const float4*>(&sk[r][16 * sl + 4 * m4]);
+            const float4 qq4 = *reinterpret_cast<const float4*>(&sq[r][16 * sl + 4 * m4]);
+            const float kk[4] = {kk4.x, kk4.y, kk4.z, kk4.w};
+            const float qq[4] = {qq4.x, qq4.y, qq4.z, qq4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float4 h = hv[4 * m4 + e];
+                acc[r].x += h.x * kk[e]; acc[r].y += h.y * kk[e]; acc[r].z += h.z * kk[e]; acc[r].w += h.w * kk[e];
+                acc[kRows + r].x += h.x * qq[e]; acc[kRows + r].y += h.y * qq[e];
+                acc[kRows + r].z += h.z * qq[e]; acc[kRows + r].w += h.w * qq[e];
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 2 * kRows; ++m) part[sl][m][cg] = acc[m];
+
+    // k_r . k_s and q_r . k_s: pair tid/16, 8-element segment tid%16
+    {
+        const int pr = tid >> 4, seg = tid & 15, r = pr >> 2, s2 = pr & 3;
+        float kk = 0.f, qk = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ks = sk[s2][8 * seg + e];
+            kk += sk[r][8 * seg + e] * ks;
+            qk += sq[r][8 * seg + e] * ks;
+        }
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+            kk += __shfl_xor(kk, off, 16);
+            qk += __shfl_xor(qk, off, 16);
+        }
+        if (seg == 0) { sA[r][s2] = kk; sQK[r][s2] = qk; }
+    }
+    __syncthreads();
+
+    // sum the 8 slices: thread -> (vector tid/32, column group tid%32)
+    {
+        const int vec = tid >> 5;
+        float4 t = part[0][vec][cg];
+#pragma unroll
+        for (int s2 = 1; s2 < kSlices; ++s2) {
+            const float4 u4 = part[s2][vec][cg];
+            t.x += u4.x; t.y += u4.y; t.z += u4.z; t.w += u4.w;
+        }
+        *reinterpret_cast<float4*>(&red[vec][4 * cg]) = t;
+    }
+    if (tid == 0) {
+        float a = 0.f;
+        for (int r = 0; r < kRows; ++r) { a += sG[r]; sG[r] = a; }
+        for (int r = 0; r < kRows; ++r)
+            for (int s2 = 0; s2 < kRows; ++s2) {
+                const float gam = s2 <= r ? __expf(sG[r] - sG[s2]) : 0.f;
+                sA[r][s2] = s2 < r ? sBeta[r] * gam * sA[r][s2] : 0.f;
+                sQK[r][s2] = s2 <= r ? gam * sQK[r][s2] : 0.f;
+            }
+    }
+    __syncthreads();
+
+    float* st = stash + (size_t)b * stash_seq_floats + (size_t)vh * stash_head_floats(D, D, sizeof(TIn) == 2);
+    if (tid < D) {
+        const int j = tid;
+        float d[kRows];
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            float x = sBeta[r] * (sv[r][j] - __expf(sG[r]) * red[r][j]);
+#pragma unroll
+            for (int m = 0; m < r; ++m) x -= sA[r][m] * d[m];
+            d[r] = x;
+        }
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            float o = __expf(sG[r]) * red[kRows + r][j];
+#pragma unroll
+            for (int s2 = 0; s2 <= r; ++s2) o += sQK[r][s2] * d[s2];
+            Elem<TOut>::store(out + (((size_t)b * kRows + r) * Hv + vh) * D + j, o);
+            st[r * D + j] = d[r];
+        }
+    } else {
+        const int t2 = tid - D;   // 128 threads: G and the keys
+        if (t2 < kRows) st[kRows * D + t2] = sG[t2];
+        float* sk_out = st + kRows * D + kRows;
+        for (int e = t2; e < kRows * D; e += kThreads - D) {
+            const int r = e / D, i = e % D;
+            if (sizeof(TIn) == 2)
+                reinterpret_cast<uint16_t*>(sk_out)[e] =
+                    *reinterpret_cast<const uint16_t*>(k + ((size_t)b * kRows + r) * qk_stride + (size_t)kh * D + i);
+            else
+                sk_out[e] = sk[r][i];
+        }
+    }
+    if (vh == 0 && b == 0 && tid == 0) engaged_flag[0] = 1u;
+}
+
+// The fold splits each state into 32-column quarters (four workgroups per
+// (v-head, sequence)): it has no per-workgroup reduction to repeat, and the
+// extra workgroups overlap one another's loads and stores.
+constexpr int kQuarters = 4;
+constexpr int kQCols = 128 / kQuarters;   // 32 columns
+
+// dk = dv = 128 fold: one workgroup per (v-head, sequence, 32-column quarter);
+// each thread issues its four state loads before anything else.
+template <bool kBf16Keys>
+__global__ void __launch_bounds__(kThreads)
+gdn_fold_k4_d128_kernel(float* const* __restrict__ h_table, const float* __restrict__ stash,
+                        const int32_t* __restrict__ na_tab, const uint32_t* __restrict__ engaged_flag,
+                        int stash_seq_floats)
+{
+    constexpr int D = 128;
+    __shared__ __attribute__((aligned(16))) float sk[kRows][D];
+    __shared__ __attribute__((aligned(16))) float sd[kRows][kQCols];
+    __shared__ float sc[kRows + 1];
+
+    if (engaged_flag[0] == 0u) return;   // the write-on-accept verify did not run
+    const int vh = blockIdx.x / kQuarters, qc = blockIdx.x % kQuarters;
+    const int b = blockIdx.y;
+    const int na = min(max(na_tab[b], 0), kRows);
+    if (na == 0) return;                 // nothing accepted: the state keeps its bytes
+    const int tid = threadIdx.x;
+    const int sl = tid >> 3, cg = tid & 7;
+    const int c0 = qc * kQCols;
+
+    float* h = h_table[b] + (size_t)vh * D * D + c0;
+    float4 hv[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) hv[m] = *reinterpret_cast<const float4*>(h + (size_t)(4 * sl + m) * D + 4 * cg);
+
+    const float* st = stash + (size_t)b * stash_seq_floats + (size_t)vh * stash_head_floats(D, D, kBf16Keys);
+    if (tid < na * kQCols) sd[tid / kQCols][tid % kQCols] = st[(tid / kQCols) * D + c0 + tid % kQCols];
+    const float* sk_in = st + kRows * D + kRows;
+    for (int e = tid; e < na * D; e += kThreads) {
+        float x;
+        if (kBf16Keys) x = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sk_in)[e]);
+        else x = sk_in[e];
+        sk[e / D][e % D] = x;
+    }
+    if (tid <= na) {
+        const float gl = st[kRows * D + na - 1];
+        sc[tid] = tid < na ? __expf(gl - st[kRows * D + tid]) : __expf(gl);
+    }
+    __syncthreads();
+
+    const float gam = sc[na];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int i = 4 * sl + m;
+        float4 x = hv[m];
+        x.x *= gam; x.y *= gam; x.z *= gam; x.w *= gam;
+#pragma unroll
+        for (int s2 = 0; s2 < kRows; ++s2) {
+            if (s2 < na) {
+                const float ks = sc[s2] * sk[s2][i];
+                const float4 dv4 = *reinterpret_cast<const float4*>(&sd[s2][4 * cg]);
+                x.x += ks * dv4.x; x.y += ks * dv4.y; x.z += ks * dv4.z; x.w += ks * dv4.w;
+            }
+        }
+        *reinterpret_cast<float4*>(h + (size_t)i * D + 4 * cg) = x;
+    }
+}
+
 __global__ void __launch_bounds__(64) gdn_flag_clear_kernel(uint32_t* flag)
 {
     if (threadIdx.x == 0) flag[0] = 0u;
@@ -204,6 +421,13 @@ __global__ void __launch_bounds__(64) gdn_flag_clear_kernel(uint32_t* flag)
 template <typename TIn, typename TOut>
 hipError_t launch_verify_typed(const VerifyArgs& a, hipStream_t s)
 {
+    if (a.dk == 128 && a.dv == 128) {
+        hipLaunchKernelGGL((gdn_verify_k4_d128_kernel<TIn, TOut>), dim3(a.Hv, a.B), dim3(kThreads), 0, s,
+                           a.h_table, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.gate, a.beta,
+                           (TOut*)a.out, a.stash, a.Hk, a.Hv, a.qk_stride, a.v_stride, a.gb_stride,
+                           a.stash_seq_floats, a.engaged_flag);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((gdn_verify_k4_kernel<TIn, TOut>), dim3(a.Hv, a.B), dim3(kThreads), 0, s,
                        a.h_table, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.gate, a.beta,
                        (TOut*)a.out, a.stash, a.Hk, a.Hv, a.dk, a.dv, a.qk_stride, a.v_stride,
@@ -215,6 +439,12 @@ hipError_t launch_verify_typed(const VerifyArgs& a, hipStream_t s)
 
 Geometry verify_geometry(const VerifyArgs& a)
 {
+    if (a.dk == 128 && a.dv == 128) {
+        Geometry g{"gdn_verify_k4_d128_kernel", {(unsigned)a.Hv, (unsigned)a.B, 1u}, kThreads,
+                   (unsigned)(sizeof(float) * (3 * kRows * 128 + 2 * kRows * 128 + 2 * kRows + 2 * kRows * kRows) +
+                              sizeof(float4) * kSlices * 2 * kRows * kColGroups)};
+        return g;
+    }
     Geometry g{"gdn_verify_k4_kernel", {(unsigned)a.Hv, (unsigned)a.B, 1u}, kThreads,
                (unsigned)(sizeof(float) * 3 * kRows * kMaxD + sizeof(float4) * kSlices * 2 * kRows * kColGroups +
                           sizeof(float) * (2 * kRows + 2 * kRows * kRows))};
@@ -223,6 +453,11 @@ Geometry verify_geometry(const VerifyArgs& a)
 
 Geometry fold_geometry(const FoldArgs& a)
 {
+    if (a.dk == 128 && a.dv == 128) {
+        Geometry g{"gdn_fold_k4_d128_kernel", {(unsigned)(a.Hv * kQuarters), (unsigned)a.B, 1u}, kThreads,
+                   (unsigned)(sizeof(float) * (kRows * 128 + kRows * kQCols + kRows + 1))};
+        return g;
+    }
     Geometry g{"gdn_fold_k4_kernel", {(unsigned)a.Hv, (unsigned)a.B, 1u}, kThreads,
                (unsigned)(sizeof(float) * (2 * kRows * kMaxD + kRows + 1))};
     return g;
@@ -244,6 +479,15 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t s)
 
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s)
 {
+    if (a.dk == 128 && a.dv == 128) {
+        if (a.io_dtype == 1)
+            hipLaunchKernelGGL((gdn_fold_k4_d128_kernel<true>), dim3(a.Hv * kQuarters, a.B), dim3(kThreads), 0, s,
+                               a.h_table, a.stash, a.na_tab, a.engaged_flag, a.stash_seq_floats);
+        else
+            hipLaunchKernelGGL((gdn_fold_k4_d128_kernel<false>), dim3(a.Hv * kQuarters, a.B), dim3(kThreads), 0, s,
+                               a.h_table, a.stash, a.na_tab, a.engaged_flag, a.stash_seq_floats);
+        return hipGetLastError();
+    }
     if (a.io_dtype == 1)
         hipLaunchKernelGGL((gdn_fold_k4_kernel<true>), dim3(a.Hv, a.B), dim3(kThreads), 0, s,
                            a.h_table, a.stash, a.na_tab, a.engaged_flag, a.dk, a.dv, a.stash_seq_floats);

@@ -26,3 +26,8 @@ def test_verify_bytes():
     assert b == 16 * 48 * 65536 + 16 * 4 * (2 * 16 * 128 + 48 * 128) * 2 + 16 * 4 * 48 * 8 \
         + 16 * 4 * 48 * 128 * 2 + 16 * 48 * (4 * 128 * 4 + 16 + 4 * 128 * 2)
     assert 54e6 < b < 55e6
+
+
+def test_fold_bytes():
+    # two sequences folded (na = 1 and 4), one not (na = 0)
+    assert bench.fold_bytes([0, 1, 4], 48, 128, 128) == 48 * (131072 + 1 * 768 + 16) + 48 * (131072 + 4 * 768 + 16)  # state 64 KiB read + write

@@ -102,7 +102,7 @@ def test_verify_fold_workload(io, out_dtype, tol, pad):
     assert int(s.flag.item()) == 0
     route = s.verify()
     torch.cuda.synchronize()
-    assert route.startswith("gdn_verify_k4_kernel grid=[48,16,1]"), route
+    assert route.startswith("gdn_verify_k4_d128_kernel grid=[48,16,1]"), route
     assert int(s.flag.item()) == 1, "verify marks the engaged word"
     assert torch.equal(s.states(), before), "verify writes no state"
     ro, after = oracle_decode(inp)
@@ -118,6 +118,29 @@ def test_verify_fold_workload(io, out_dtype, tol, pad):
             assert rel_err(got[b], after[b, na[b]]) <= 1e-4, f"sequence {b} na={na[b]}"
     for x, y in zip(s.spares, spares_before):
         assert torch.equal(x.cpu(), y), "a slot outside the table changed"
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 96), (128, 64), (32, 128)])
+def test_generic_shapes(dk, dv):
+    """Head sizes other than 128 take the generic verify/fold kernels."""
+    inp = synth.decode_inputs(6, K, 2, 4, dk, dv, io=torch.bfloat16, seed=40 + dk + dv)
+    say("decode generic", dk, dv)
+    s = Setup(inp, torch.bfloat16, torch.float32, qk_pad=8)
+    before = s.states()
+    s.clear()
+    route = s.verify()
+    assert route.startswith("gdn_verify_k4_kernel "), route
+    s.fold()
+    torch.cuda.synchronize()
+    ro, after = oracle_decode(inp)
+    assert rel_err(s.out, ro) <= 1e-4
+    got = s.states()
+    for b in range(s.B):
+        na = int(inp["na"][b])
+        if na == 0:
+            assert torch.equal(got[b], before[b])
+        else:
+            assert rel_err(got[b], after[b, na]) <= 1e-4
 
 
 def test_fold_without_verify_is_a_no_op():

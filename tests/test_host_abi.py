@@ -124,7 +124,9 @@ def verify_plan(lib, **kw):
 def test_verify_plan(lib):
     assert verify_plan(lib) == 0
     r = gdn.last_route()
-    assert r.startswith("gdn_verify_k4_kernel grid=[48,16,1] block=256"), r
+    assert r.startswith("gdn_verify_k4_d128_kernel grid=[48,16,1] block=256"), r
+    assert verify_plan(lib, dk=64, dv=64, qks=16 * 64, vs=48 * 64, ssf=48 * (256 + 4 + 128)) == 0
+    assert gdn.last_route().startswith("gdn_verify_k4_kernel grid=[48,16,1]")
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -148,7 +150,7 @@ def fold_plan(lib, **kw):
 
 def test_fold_plan(lib):
     assert fold_plan(lib) == 0
-    assert gdn.last_route().startswith("gdn_fold_k4_kernel grid=[48,16,1] block=256")
+    assert gdn.last_route().startswith("gdn_fold_k4_d128_kernel grid=[192,16,1] block=256")
 
 
 @pytest.mark.parametrize("kw,status", [
