@@ -341,26 +341,6 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Operands of one chunk for the spine, as the compute waves read them.
-struct alignas(16) SpineBuf {
-    uint16_t K[C * LDK];        // K, row-major (A operand of K h)
-    uint16_t Q[C * LDK];        // Q, row-major (A operand of Q h)
-    uint16_t Kt[D * LDC];       // K^T (A operand of K^T Delta)
-    uint16_t T[C * LDC];        // (I + A)^-1
-    uint16_t P[C * LDC];        // lower_incl(Gamma o Q K^T)
-    uint16_t Vt[TILE_COLS * LDC];  // this workgroup's 32 columns of V, transposed
-    float gam[C];               // exp(G_r)
-    float el[C];                // exp(G_L - G_r)
-    float beta[C];
-    float gamL;                 // exp(G_L)
-};
-
-// One chunk's worth of global data in a loader thread's registers.
-struct SpineRegs {
-    uint4 k[8], q[8], t[4], p[4], v[2];
-    float g = 0.f, b = 0.f;
-};
-
 // Buffer resources (gfx9 family): a wave-uniform base in SGPRs, 32-bit lane
 // byte offsets, and a byte range; reads beyond the range return 0 and writes
 // beyond it are dropped, which is how partial chunks are masked.
@@ -368,201 +348,274 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ float buf_load4f(rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
 
-// Per-thread byte offsets of the loader's fetches within one chunk.
-struct LoaderOffsets {
-    uint32_t kq, kq_row;   // row 8 rb + i of K and Q at kq + i * kq_row
-    uint32_t tp[4];        // T pieces (P at + C*C*2)
-    uint32_t v[2];
-    uint32_t gb;           // log_g / beta of row lt (first loader wave)
+// ---------------------------------------------------------------------------
+// The spine's LDS ring: three stages, each holding one chunk's operands.  Two
+// loader waves fill stage c+2 by buffer->LDS DMA (a 64-lane DMA writes lane
+// l's 16 bytes at base + 16 l, and lanes beyond the buffer's range write
+// zeros, which pads a partial chunk) and prepare the chunk's decay factors,
+// while two compute waves walk chunk c.
+//
+// MFMA k-slots.  Lane group g (lanes 16g .. 16g+15) supplies k-values
+// 8g .. 8g+7 of each 32-wide k-step, so every A fragment is one 16-byte read.
+// An accumulator tile holds rows 4g .. 4g+3 in lane group g; tiles 2j and
+// 2j+1 form the B operand of k-step j without any exchange when row m of
+// tile t stands for index
+//     sig(t, m) = 32 (t/2) + 8 (m/4) + 4 (t%2) + m%4.
+// The state tiles h[db] (state rows) and the chunk-row tiles X, Y, Delta and
+// O all use this map.
+//
+// Stage layout.  Rows are dense; the 16-byte granules of a row are permuted
+// so that every fragment read is free of bank conflicts (64 banks of 4
+// bytes; a 16-byte read serves 8 lanes per pass, an 8-byte read 16):
+//   K, Q (64 rows x 256 B): granule q of row r at q ^ fK(r), fK(r) = 4 (r%4) + (r/8)%2
+//   T, P (64 rows x 128 B): granule q of row r at q ^ fT(r), fT(r) = (r/2)%2 + 2 ((r/8)%2)
+//   V    (64 rows x  64 B: the workgroup's 32 columns)
+//   log_g, beta as loaded (64 fp32 each), then the prepared decay factors
+//   gm_r = exp(G_r) and el_r = exp(G_L - G_r), and gamma_L = exp(G_L).
+constexpr int ST_K = 0;
+constexpr int ST_Q = 16384;
+constexpr int ST_T = 32768;
+constexpr int ST_P = 40960;
+constexpr int ST_V = 49152;
+constexpr int ST_G = 53248;
+constexpr int ST_B = 53504;
+constexpr int ST_GM = 53760;
+constexpr int ST_EL = 54016;
+constexpr int ST_SO = 54272;
+constexpr int ST_BYTES = 54288;
+constexpr int N_STAGES = 3;
+constexpr int DMA_PER_WAVE = 27;   // 16 K or Q + 8 T or P + 2 V + 1 log_g or beta
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Buffer->LDS DMA, written as inline assembly: the compiler would otherwise
+// make later LDS reads wait for every DMA in flight.  Completion is tracked
+// by hand (wait_vmcnt).  The range check that zero-fills rows beyond a chunk
+// covers the lane offset and the SGPR offset alike.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+struct Rsrc { u32x4 d; };
+__device__ __forceinline__ Rsrc make_dma_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    Rsrc r;
+    r.d = u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu),
+                (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+    return r;
+}
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)p;
+}
+__device__ __forceinline__ void dma16(const Rsrc& r, unsigned char* lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"((uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(lds))), "v"(voff), "s"(r.d),
+                    "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const Rsrc& r, unsigned char* lds, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"((uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(lds))), "v"(voff), "s"(r.d) : "memory", "m0");
+}
+// A workgroup barrier without the fences of __syncthreads, whose vmcnt(0)
+// would wait for the DMA of later chunks too.  Producers wait for their own
+// writes (wait_vmcnt, wait_lgkm0) before they arrive.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// s_waitcnt with one counter constrained (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt 6:4, lgkmcnt 11:8).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    if (n == 0) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt((DMA_PER_WAVE & 15) | ((DMA_PER_WAVE >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+__device__ __forceinline__ s16x8 lds_read16(const unsigned char* p) {
+    return *reinterpret_cast<const s16x8*>(p);
+}
+__device__ __forceinline__ s16x4 lds_read_tr(const unsigned char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
+__device__ __forceinline__ s16x8 join(s16x4 a, s16x4 b) {
+    return s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+// first index of tile t under sig(t, .), and of lane group g within it
+__device__ __forceinline__ constexpr int sig_tile(int t) { return 32 * (t >> 1) + 4 * (t & 1); }
+
+// Per-lane DMA byte offsets of a loader wave (chunk-independent).
+struct LoadOffsets {
+    uint32_t kq[2];   // K / Q rows, by (j/2)%2 of the 4-row block j
+    uint32_t tp[2];   // T / P rows, by j%2 of the 8-row block j
+    uint32_t v;       // V
+    uint32_t gb;      // log_g / beta
 };
 
-__device__ __forceinline__ LoaderOffsets loader_offsets(int lt, int Hk, int Hv)
-{
-    LoaderOffsets o;
-    const int rb = lt >> 4, cb = lt & 15;
-    o.kq_row = (uint32_t)Hk * D * 2u;
-    o.kq = (uint32_t)(8 * rb) * o.kq_row + (uint32_t)(8 * cb) * 2u;
+__device__ __forceinline__ LoadOffsets load_offsets(int lane, int Hk, int Hv) {
+    LoadOffsets o;
+    const uint32_t kq_row = (uint32_t)Hk * D * 2u, v_row = (uint32_t)Hv * D * 2u;
+    const int rr = lane >> 4, p = lane & 15, p8 = lane & 7, hb = (lane >> 4) & 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = lt + 128 * i;
-        o.tp[i] = (uint32_t)((idx >> 3) * C + (idx & 7) * 8) * 2u;
+    for (int s = 0; s < 2; ++s) {
+        o.kq[s] = rr * kq_row + (uint32_t)((p ^ (4 * rr + s)) * 16);
+        o.tp[s] = (uint32_t)((lane >> 3) * 128 + ((p8 ^ (hb | (s << 1))) * 16));
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int idx = lt + 128 * i;
-        o.v[i] = (uint32_t)(idx >> 2) * Hv * D * 2u + (uint32_t)((idx & 3) * 8) * 2u;
-    }
-    o.gb = (uint32_t)(lt & 63) * Hv * 4u;
+    o.v = (uint32_t)(lane >> 2) * v_row + (uint32_t)((lane & 3) * 16);
+    o.gb = (uint32_t)lane * Hv * 4u;
     return o;
 }
 
-// Two loader waves (128 threads, lt = 0..127) fetch one chunk into registers;
-// every load is issued before any is used.  Rows >= L read as zero.
-__device__ __forceinline__ void spine_fetch(SpineRegs& R, const LoaderOffsets& o, rsrc_t rk,
-                                            rsrc_t rq, rsrc_t rv, rsrc_t rg, rsrc_t rb_,
-                                            rsrc_t rs, int lt)
+// Loader wave wl's share of chunk c's DMA into `stage`: K (wl = 0) or Q
+// (wl = 1), T or P, half of V, log_g or beta.  Rows beyond the chunk read as
+// zero.  Exactly DMA_PER_WAVE operations.
+__device__ __forceinline__ void spine_load(unsigned char* stage, const LoadOffsets& o,
+                                           const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                           const float* log_g, const float* beta,
+                                           const uint16_t* slot, long row0, long len, int c, int Hk,
+                                           int Hv, int kh, int vh, int tile, int wl)
 {
+    const long r = row0 + (long)c * C;
+    const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)r);
+    const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)r >> 32));
+    const size_t ru = ((size_t)rhi << 32) | rlo;
+    const uint32_t L = __builtin_amdgcn_readfirstlane((uint32_t)min((long)C, len - (long)c * C));
+    const uint32_t kq_row = (uint32_t)Hk * D * 2u, v_row = (uint32_t)Hv * D * 2u;
+
+    const Rsrc rkq = make_dma_rsrc((wl == 0 ? k : q) + (ru * Hk + kh) * D, L * kq_row);
+    unsigned char* dkq = stage + (wl == 0 ? ST_K : ST_Q);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        R.k[i] = buf_load16(rk, o.kq + i * o.kq_row);
-        R.q[i] = buf_load16(rq, o.kq + i * o.kq_row);
-    }
+    for (int j = 0; j < 16; ++j)
+        dma16(rkq, dkq + 1024 * j, o.kq[(j >> 1) & 1], (uint32_t)(4 * j) * kq_row);
+    const Rsrc rtp = make_dma_rsrc(slot + (wl == 0 ? 0 : C * C), C * C * 2u);
+    unsigned char* dtp = stage + (wl == 0 ? ST_T : ST_P);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        R.t[i] = buf_load16(rs, o.tp[i]);
-        R.p[i] = buf_load16(rs, o.tp[i] + C * C * 2);
-    }
+    for (int j = 0; j < 8; ++j) dma16(rtp, dtp + 1024 * j, o.tp[j & 1], (uint32_t)(1024 * j));
+    const Rsrc rv = make_dma_rsrc(v + (ru * Hv + vh) * D + tile * TILE_COLS, L * v_row);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) R.v[i] = buf_load16(rv, o.v[i]);
-    if (lt < 64) {   // wave-uniform
-        R.g = buf_load4f(rg, o.gb);
-        R.b = buf_load4f(rb_, o.gb);
+    for (int j = 0; j < 2; ++j) {
+        const int jj = 2 * wl + j;
+        dma16(rv, stage + ST_V + 1024 * jj, o.v, (uint32_t)(16 * jj) * v_row);
     }
+    const Rsrc rg = make_dma_rsrc((wl == 0 ? log_g : beta) + ru * Hv + vh, L * Hv * 4u);
+    dma4(rg, stage + (wl == 0 ? ST_G : ST_B), o.gb);
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& u, int i) {
-    return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+// Decay factors of the chunk in `stage` (its log_g has landed): G = cumsum
+// of log_g within the chunk.  One wave, lane = row.
+__device__ __forceinline__ void spine_scan(unsigned char* stage, int lane) {
+    const float gv = reinterpret_cast<const float*>(stage + ST_G)[lane];
+    const float G = wave_inclusive_sum(gv, lane);
+    const float GL = __shfl(G, 63, 64);
+    reinterpret_cast<float*>(stage + ST_GM)[lane] = __expf(G);
+    reinterpret_cast<float*>(stage + ST_EL)[lane] = __expf(GL - G);
+    if (lane == 0) *reinterpret_cast<float*>(stage + ST_SO) = __expf(GL);
 }
 
-// Halves e of two packed bf16 words: (lo's, hi's) as one word.
-__device__ __forceinline__ uint32_t pair_half(uint32_t lo, uint32_t hi, int e) {
-    return (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+// Per-lane byte offsets of the compute waves' operand reads inside a stage
+// (chunk- and stage-independent).  Each chunk then needs 10 base additions;
+// the tile and k-step parts of every address are immediates.
+struct FragOffsets {
+    uint32_t kq[4];   // K / Q fragments, by k-step
+    uint32_t tp;      // T / P fragments
+    uint32_t kt[4];   // K^T (transposing) fragments, by db / 2
+    uint32_t v;       // V (transposing)
+};
+
+__device__ __forceinline__ FragOffsets frag_offsets(int g, int n, int w) {
+    FragOffsets o;
+    const int sig0 = 8 * (n >> 2) + (n & 3);                 // sig(0, n)
+    const int fKn = 4 * (n & 3) + ((n >> 2) & 1);            // fK(sig(t, n)), any t
+    const int fTn = ((n >> 1) & 1) | (((n >> 2) & 1) << 1);  // fT(sig(t, n)), any t
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) o.kq[kk] = (uint32_t)(sig0 * 256 + 16 * ((4 * kk + g) ^ fKn));
+    o.tp = (uint32_t)(sig0 * 128 + 16 * (g ^ fTn));
+    // transposing reads: this lane sources row 8g + kr (+ 32 kk + 4 half) and
+    // the 4 columns of quarter qq of the 8-column group
+    const int kr = n >> 2, qq = n & 3;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        o.kt[d] = (uint32_t)((8 * g + kr) * 256 + 16 * (4 * (d ^ kr) + (qq ^ (g & 1))));
+    o.v = (uint32_t)((8 * g + kr) * 64 + 32 * w + 8 * qq);
+    return o;
 }
 
-// Stores a fetched chunk into `sb`: K, Q and T, P rows as they are; K^T by
-// transposing each thread's 8x8 block in registers; V transposed element-wise.
-__device__ __forceinline__ void spine_store(SpineBuf& sb, const SpineRegs& R, int lt)
-{
-    const int rb = lt >> 4, cb = lt & 15;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        store16(sb.K + (8 * rb + i) * LDK + 8 * cb, R.k[i]);
-        store16(sb.Q + (8 * rb + i) * LDK + 8 * cb, R.q[i]);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {   // column e of the block = row 8 cb + e of K^T
-        uint4 o;
-        o.x = pair_half(word_of(R.k[0], e >> 1), word_of(R.k[1], e >> 1), e);
-        o.y = pair_half(word_of(R.k[2], e >> 1), word_of(R.k[3], e >> 1), e);
-        o.z = pair_half(word_of(R.k[4], e >> 1), word_of(R.k[5], e >> 1), e);
-        o.w = pair_half(word_of(R.k[6], e >> 1), word_of(R.k[7], e >> 1), e);
-        store16(sb.Kt + (8 * cb + e) * LDC + 8 * rb, o);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = lt + 128 * i, r = idx >> 3, c8 = (idx & 7) * 8;
-        store16(sb.T + r * LDC + c8, R.t[i]);
-        store16(sb.P + r * LDC + c8, R.p[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int idx = lt + 128 * i, r = idx >> 2, c8 = (idx & 3) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t wv = word_of(R.v[i], e >> 1);
-            sb.Vt[(c8 + e) * LDC + r] = (uint16_t)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
-        }
-    }
-    if (lt < 64) {   // wave-uniform: the first loader wave
-        const float Gr = wave_inclusive_sum(R.g, lt);
-        const float GL = __shfl(Gr, 63, 64);
-        sb.gam[lt] = __expf(Gr);
-        sb.el[lt] = __expf(GL - Gr);
-        sb.beta[lt] = R.b;
-        if (lt == 0) sb.gamL = __expf(GL);
-    }
-}
-
-__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
-
-// One compute wave, one chunk, 16 columns (wave w of the workgroup).  LDS
-// fragment reads are issued one group ahead of the MFMAs that consume them,
-// so that a single wave per SIMD does not wait out each read's latency.
+// One compute wave, one chunk, 16 columns (wave w of the workgroup) from
+// stage S.  The chunk's outputs go through `ro`, a buffer resource that
+// covers exactly its rows: `lane_off` is the lane's byte offset (row 8g,
+// column col) and soff[4 cb + r] the uniform offset of row sig_tile(cb) + r.
 template <bool kOutF32>
-__device__ __forceinline__ void spine_step(const SpineBuf& sb, f32x4 (&h)[8], void* __restrict__ out,
-                                           long r0, int L, int Hv, int vh, int col, int w, int g, int n)
+__device__ __forceinline__ void spine_step(const unsigned char* S, f32x4 (&h)[8], rsrc_t ro,
+                                           uint32_t lane_off, const uint32_t (&soff)[16], int g,
+                                           const FragOffsets& fo)
 {
+    const float* gmv = reinterpret_cast<const float*>(S + ST_GM);
+    const float* elv = reinterpret_cast<const float*>(S + ST_EL);
+    const float* btv = reinterpret_cast<const float*>(S + ST_B);
+    const unsigned char* pk[4];
+    const unsigned char* pz[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { pk[i] = S + fo.kq[i]; pz[i] = S + fo.kt[i]; }
+    const unsigned char* pt = S + fo.tp;
+    const unsigned char* pv = S + fo.v;
+#define KQF(sec, cb, kk) lds_read16(pk[kk] + (sec) + 256 * sig_tile(cb))
+#define TPF(sec, cb, kk) lds_read16(pt + (sec) + 128 * sig_tile(cb) + 64 * (kk))
+#define KTF(db, kk) join(lds_read_tr(pz[(db) >> 1] + ST_K + 8192 * (kk) + 8 * ((db) & 1)), \
+                         lds_read_tr(pz[(db) >> 1] + ST_K + 8192 * (kk) + 1024 + 8 * ((db) & 1)))
+
     s16x8 hb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) hb[kk] = frag_b(h[2 * kk], h[2 * kk + 1]);
 
-    // X = K h, Y = Q h: 4 k-steps x 8 independent accumulators
+    // X = K h, Y = Q h: per k-step, 4 K fragments then 4 Q fragments, each
+    // group loaded one group ahead
     f32x4 X[4], Y[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) X[cb] = Y[cb] = zero4();
-    s16x8 fa[8], fb[8];
+    s16x8 fcur[4], fnext[4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        fa[cb] = frag_a(sb.K, LDK, 16 * cb + n, 0, g);
-        fa[4 + cb] = frag_a(sb.Q, LDK, 16 * cb + n, 0, g);
-    }
-    float4 gm4[4], bt4[4], el4[4];
-    uint2 vv[4];
+    for (int cb = 0; cb < 4; ++cb) fcur[cb] = KQF(ST_K, cb, 0);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        s16x8 (&cur)[8] = (kk & 1) ? fb : fa;
-        s16x8 (&nxt)[8] = (kk & 1) ? fa : fb;
-        if (kk < 3) {
+    for (int gi = 0; gi < 8; ++gi) {   // group gi: k-step gi/2, K (even) or Q (odd)
+        const int kk = gi >> 1;
+        if (gi + 1 < 8) {
+            const int kn = (gi + 1) >> 1;
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                nxt[cb] = frag_a(sb.K, LDK, 16 * cb + n, 32 * (kk + 1), g);
-                nxt[4 + cb] = frag_a(sb.Q, LDK, 16 * cb + n, 32 * (kk + 1), g);
-            }
-        } else {
-            // per-row scalars of the next phases, and the first T fragments
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const int row = 16 * cb + 4 * g;
-                gm4[cb] = *reinterpret_cast<const float4*>(sb.gam + row);
-                bt4[cb] = *reinterpret_cast<const float4*>(sb.beta + row);
-                el4[cb] = *reinterpret_cast<const float4*>(sb.el + row);
-                vv[cb] = *reinterpret_cast<const uint2*>(sb.Vt + (16 * w + n) * LDC + row);
-            }
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) nxt[cb] = frag_a(sb.T, LDC, 16 * cb + n, 0, g);
-            nxt[4] = frag_a(sb.T, LDC, 32 + n, 32, g);
-            nxt[5] = frag_a(sb.T, LDC, 48 + n, 32, g);
+            for (int cb = 0; cb < 4; ++cb) fnext[cb] = ((gi + 1) & 1) ? KQF(ST_Q, cb, kn) : KQF(ST_K, cb, kn);
         }
         sched_fence();
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            X[cb] = mfma_bf16(cur[cb], hb[kk], X[cb]);
-            Y[cb] = mfma_bf16(cur[4 + cb], hb[kk], Y[cb]);
+            if (gi & 1) Y[cb] = mfma_bf16(fcur[cb], hb[kk], Y[cb]);
+            else X[cb] = mfma_bf16(fcur[cb], hb[kk], X[cb]);
         }
         sched_fence();
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) fcur[cb] = fnext[cb];
     }
-    s16x8 (&ft)[8] = fa;   // T fragments (the last k-step's "next" buffer)
 
-    // R = beta (V - gamma X) in place of X; gamma Y in place of Y
+    // T fragments, then R = beta (V - gm X) and Y <- gm Y for this lane's rows
+    s16x8 ft[6];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) ft[cb] = TPF(ST_T, cb, 0);
+    ft[4] = TPF(ST_T, 2, 1);
+    ft[5] = TPF(ST_T, 3, 1);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-        const float gmr[4] = {gm4[cb].x, gm4[cb].y, gm4[cb].z, gm4[cb].w};
-        const float btr[4] = {bt4[cb].x, bt4[cb].y, bt4[cb].z, bt4[cb].w};
-        const float vr[4] = {bf16_bits_to_f32((uint16_t)(vv[cb].x & 0xffffu)), bf16_bits_to_f32((uint16_t)(vv[cb].x >> 16)),
-                             bf16_bits_to_f32((uint16_t)(vv[cb].y & 0xffffu)), bf16_bits_to_f32((uint16_t)(vv[cb].y >> 16))};
+        const int row = sig_tile(cb) + 8 * g;
+        const float4 gm4 = *reinterpret_cast<const float4*>(gmv + row);
+        const float4 bt4 = *reinterpret_cast<const float4*>(btv + row);
+        const s16x4 vv = lds_read_tr(pv + ST_V + 64 * sig_tile(cb));
+        const float gmr[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
+        const float btr[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            X[cb][r] = btr[r] * (vr[r] - gmr[r] * X[cb][r]);
+            X[cb][r] = btr[r] * (bf16_bits_to_f32((uint16_t)vv[r]) - gmr[r] * X[cb][r]);
             Y[cb][r] *= gmr[r];
         }
     }
     const s16x8 rb0 = frag_b(X[0], X[1]), rb1 = frag_b(X[2], X[3]);
 
-    // Delta = T R (T lower triangular: rows < 32 need only k < 32); meanwhile
-    // fetch the first half of the K^T fragments
-    s16x8 fk[8];
+    // Delta = T R (T lower triangular: its first 32 rows need only k < 32)
+    s16x8 fk1[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        fk[2 * db] = frag_a(sb.Kt, LDC, 16 * db + n, 0, g);
-        fk[2 * db + 1] = frag_a(sb.Kt, LDC, 16 * db + n, 32, g);
-    }
+    for (int db = 0; db < 2; ++db) { fk1[2 * db] = KTF(db, 0); fk1[2 * db + 1] = KTF(db, 1); }
     sched_fence();
     f32x4 Dl[4];
     Dl[0] = mfma_bf16(ft[0], rb0, zero4());
@@ -575,42 +628,42 @@ __device__ __forceinline__ void spine_step(const SpineBuf& sb, f32x4 (&h)[8], vo
     const s16x8 db0 = frag_b(Dl[0], Dl[1]), db1 = frag_b(Dl[2], Dl[3]);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-        Dl[cb][0] *= el4[cb].x; Dl[cb][1] *= el4[cb].y;
-        Dl[cb][2] *= el4[cb].z; Dl[cb][3] *= el4[cb].w;
+        const float4 el4 = *reinterpret_cast<const float4*>(elv + sig_tile(cb) + 8 * g);
+        Dl[cb][0] *= el4.x; Dl[cb][1] *= el4.y; Dl[cb][2] *= el4.z; Dl[cb][3] *= el4.w;
     }
     const s16x8 ds0 = frag_b(Dl[0], Dl[1]), ds1 = frag_b(Dl[2], Dl[3]);
 
-    // h <- gamma_L h + K^T (exp(G_L - G) Delta): two groups of 4 row blocks
-    const float gl = sb.gamL;
-    s16x8 fk2[8];
+    // h <- gamma_L h + K^T (el Delta): 8 row blocks, two blocks ahead
+    const float gamL = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+        __builtin_bit_cast(int, *reinterpret_cast<const float*>(S + ST_SO))));
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        fk2[2 * db] = frag_a(sb.Kt, LDC, 16 * (db + 4) + n, 0, g);
-        fk2[2 * db + 1] = frag_a(sb.Kt, LDC, 16 * (db + 4) + n, 32, g);
-    }
-    sched_fence();
+    for (int db = 0; db < 8; ++db) h[db] = h[db] * gamL;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        f32x4 acc = h[db] * gl;
-        acc = mfma_bf16(fk[2 * db], ds0, acc);
-        h[db] = mfma_bf16(fk[2 * db + 1], ds1, acc);
+    for (int db = 0; db < 8; db += 2) {
+        s16x8 fk2[4];
+        if (db + 2 < 8) {
+            fk2[0] = KTF(db + 2, 0); fk2[1] = KTF(db + 2, 1);
+            fk2[2] = KTF(db + 3, 0); fk2[3] = KTF(db + 3, 1);
+        }
+        sched_fence();
+        h[db] = mfma_bf16(fk1[1], ds1, mfma_bf16(fk1[0], ds0, h[db]));
+        h[db + 1] = mfma_bf16(fk1[3], ds1, mfma_bf16(fk1[2], ds0, h[db + 1]));
+        sched_fence();
+        if (db + 2 < 8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fk1[i] = fk2[i];
+        }
     }
-    sched_fence();
+
+    // O = gm Y + P Delta
     s16x8 fp[6];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) fp[cb] = frag_a(sb.P, LDC, 16 * cb + n, 0, g);
-    fp[4] = frag_a(sb.P, LDC, 32 + n, 32, g);
-    fp[5] = frag_a(sb.P, LDC, 48 + n, 32, g);
-    sched_fence();
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        f32x4 acc = h[db + 4] * gl;
-        acc = mfma_bf16(fk2[2 * db], ds0, acc);
-        h[db + 4] = mfma_bf16(fk2[2 * db + 1], ds1, acc);
-    }
-    sched_fence();
-
-    // O = gamma Y + P Delta, for the rows of the chunk
+    for (int cb = 0; cb < 4; ++cb) fp[cb] = TPF(ST_P, cb, 0);
+    fp[4] = TPF(ST_P, 2, 1);
+    fp[5] = TPF(ST_P, 3, 1);
+#undef KQF
+#undef TPF
+#undef KTF
     f32x4 O[4];
     O[0] = mfma_bf16(fp[0], db0, Y[0]);
     O[1] = mfma_bf16(fp[1], db0, Y[1]);
@@ -618,52 +671,20 @@ __device__ __forceinline__ void spine_step(const SpineBuf& sb, f32x4 (&h)[8], vo
     O[3] = mfma_bf16(fp[3], db0, Y[3]);
     O[2] = mfma_bf16(fp[4], db1, O[2]);
     O[3] = mfma_bf16(fp[5], db1, O[3]);
-    // hardware RNE conversion; stores through a buffer resource covering the
-    // chunk's L rows, so rows beyond a partial chunk are dropped
-    constexpr uint32_t es = kOutF32 ? 4u : 2u;
-    const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)r0);
-    const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)r0 >> 32));
-    const size_t ru = ((size_t)rhi << 32) | rlo;
-    const rsrc_t ro = make_rsrc(reinterpret_cast<char*>(out) + (ru * Hv + vh) * D * es,
-                                __builtin_amdgcn_readfirstlane((uint32_t)L * Hv * D * es));
-    const uint32_t rs = (uint32_t)Hv * D * es;
-    const uint32_t lane_off = (uint32_t)(4 * g) * rs + (uint32_t)col * es;
+    // hardware RNE conversion; rows beyond a partial chunk fall outside `ro`
+    // and are dropped
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const uint32_t off = lane_off + (uint32_t)(16 * cb + r) * rs;
             const float val = O[cb][r];   // by value: never bit-cast a vector element in place
-            if (kOutF32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
-            else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_bits(val), ro, off, 0, 0);
+            if (kOutF32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, lane_off, soff[4 * cb + r], 0);
+            else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_bits(val), ro, lane_off, soff[4 * cb + r], 0);
         }
 }
 
-// Chunk c of the sequence at rows [row0, row0 + len): its buffer resources
-// (rows beyond the chunk read as 0), fetched into the loader's registers.
-__device__ __forceinline__ void spine_fetch_chunk(SpineRegs& R, const LoaderOffsets& lo,
-                                                  const uint16_t* q, const uint16_t* k,
-                                                  const uint16_t* v, const float* log_g,
-                                                  const float* beta, const uint16_t* slot_base,
-                                                  size_t slot_stride, long row0, long len, int c,
-                                                  int Hk, int Hv, int kh, int vh, int tile, int lt)
-{
-    // all of these are wave-uniform; say so, so the resources live in SGPRs
-    const long r = row0 + (long)c * C;
-    const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)r);
-    const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)r >> 32));
-    const size_t ru = ((size_t)rhi << 32) | rlo;
-    const uint32_t L = __builtin_amdgcn_readfirstlane((uint32_t)min((long)C, len - (long)c * C));
-    spine_fetch(R, lo, make_rsrc(k + (ru * Hk + kh) * D, L * Hk * D * 2u),
-                make_rsrc(q + (ru * Hk + kh) * D, L * Hk * D * 2u),
-                make_rsrc(v + (ru * Hv + vh) * D + tile * TILE_COLS, L * Hv * D * 2u),
-                make_rsrc(log_g + ru * Hv + vh, L * Hv * 4u), make_rsrc(beta + ru * Hv + vh, L * Hv * 4u),
-                make_rsrc(slot_base + (size_t)c * slot_stride, SLOT_ELEMS * 2u), lt);
-}
-
-// One workgroup per (sequence, v-head, 32 dv columns): waves 0-1 compute
-// (16 columns each, state in registers), waves 2-3 keep the next chunk in
-// LDS and the one after it in registers.
+// One workgroup per (sequence, v-head, 32 dv columns): waves 0 and 1 own 16
+// columns each of the state in MFMA accumulators; waves 2 and 3 load.
 template <bool kOutF32>
 __global__ void __launch_bounds__(256)
 gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -673,10 +694,11 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_base,
                  int nc_dense, long n_slots)
 {
-    __shared__ SpineBuf buf[2];
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[N_STAGES * ST_BYTES];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    // the wave index is wave-uniform; say so, so per-wave values live in SGPRs
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
     // Workgroup i runs on XCD i % 8.  Map the grid so that the workgroups of
     // one k-head (its v-heads and column tiles) share an XCD and its L2.
@@ -686,7 +708,6 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int tile = lin % N_TILES;
     const int b = blockIdx.y;
     const int kh = vh / (Hv / Hk);
-    const int col = tile * TILE_COLS + 16 * (w & 1) + n;   // compute lane's dv column
 
     long row0, len;
     seq_rows(cu, b, T, &row0, &len);
@@ -695,50 +716,75 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // Only a decreasing cu_seqlens (a broken precondition) can make this
     // bind; it keeps every read inside the workspace.
     if (slot0 + nc > n_slots) nc = (int)max(0L, n_slots - slot0);
-    auto rows_of = [&](int c) { return (int)min((long)C, len - (long)c * C); };
 
+    if (w >= 2) {   // loader waves
+        const int wl = w - 2;
+        const uint16_t* slot_base = slots + ((size_t)slot0 * Hv + vh) * SLOT_ELEMS;
+        const size_t slot_stride = (size_t)Hv * SLOT_ELEMS;
+        const LoadOffsets o = load_offsets(lane, Hk, Hv);
+        for (int c = 0; c < 2 && c < nc; ++c)
+            spine_load(ring + c * ST_BYTES, o, q, k, v, log_g, beta, slot_base + (size_t)c * slot_stride,
+                       row0, len, c, Hk, Hv, kh, vh, tile, wl);
+        if (nc > 0) {
+            wait_vmcnt(nc > 1 ? DMA_PER_WAVE : 0);
+            if (wl == 0) spine_scan(ring, lane);
+            wait_lgkm0();
+        }
+        for (int c = 0; c < nc; ++c) {
+            ring_barrier();   // chunk c is ready; stage (c+2)%3 is free
+            if (c + 2 < nc)
+                spine_load(ring + ((c + 2) % N_STAGES) * ST_BYTES, o, q, k, v, log_g, beta,
+                           slot_base + (size_t)(c + 2) * slot_stride, row0, len, c + 2, Hk, Hv, kh,
+                           vh, tile, wl);
+            if (c + 1 < nc) {
+                wait_vmcnt(c + 2 < nc ? DMA_PER_WAVE : 0);   // chunk c+1 has landed
+                if (wl == 0) spine_scan(ring + ((c + 1) % N_STAGES) * ST_BYTES, lane);
+                wait_lgkm0();
+            }
+        }
+        return;
+    }
+
+    const int col = tile * TILE_COLS + 16 * w + n;
     f32x4 h[8];
     const size_t hoff = ((size_t)b * Hv + vh) * D * D;
-    const uint16_t* slot_base = slots + ((size_t)slot0 * Hv + vh) * SLOT_ELEMS;
-    const size_t slot_stride = (size_t)Hv * SLOT_ELEMS;
-    const int lt = tid - 128;
-    SpineRegs R;
-    LoaderOffsets lo;
-    if (w < 2) {
+    // state row of h[db][r] in this lane: sig(db, 4g + r)
+    if (h0) {   // one uniform branch: all 32 loads in flight together
 #pragma unroll
         for (int db = 0; db < 8; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                h[db][r] = h0 ? h0[hoff + (size_t)(16 * db + 4 * g + r) * D + col] : 0.f;
-    } else if (nc > 0) {
-        lo = loader_offsets(lt, Hk, Hv);
-        spine_fetch_chunk(R, lo, q, k, v, log_g, beta, slot_base, slot_stride, row0, len, 0, Hk, Hv,
-                          kh, vh, tile, lt);
-        spine_store(buf[0], R, lt);
-        if (nc > 1)
-            spine_fetch_chunk(R, lo, q, k, v, log_g, beta, slot_base, slot_stride, row0, len, 1, Hk,
-                              Hv, kh, vh, tile, lt);
+                h[db][r] = h0[hoff + (size_t)(sig_tile(db) + 8 * g + r) * D + col];
+    } else {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) h[db] = zero4();
     }
-    __syncthreads();
-
+    const FragOffsets fo = frag_offsets(g, n, w);
+    // output rows: a per-chunk resource over the chunk's rows, advanced by C rows
+    constexpr uint32_t es = kOutF32 ? 4u : 2u;
+    const uint32_t rs = __builtin_amdgcn_readfirstlane((uint32_t)Hv * D * es);
+    const uint32_t lane_off = (uint32_t)(8 * g) * rs + (uint32_t)col * es;
+    uint32_t soff[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) soff[i] = (uint32_t)(sig_tile(i >> 2) + (i & 3)) * rs;
+    const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)row0);
+    const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)row0 >> 32));
+    char* obase = reinterpret_cast<char*>(out) + ((((size_t)rhi << 32) | rlo) * Hv + vh) * D * es;
+    long rem = len;
     for (int c = 0; c < nc; ++c) {
-        if (w < 2) {
-            spine_step<kOutF32>(buf[c & 1], h, out, row0 + (long)c * C, rows_of(c), Hv, vh, col, w, g, n);
-        } else if (c + 1 < nc) {
-            spine_store(buf[(c + 1) & 1], R, lt);       // chunk c + 1, fetched last iteration
-            if (c + 2 < nc)
-                spine_fetch_chunk(R, lo, q, k, v, log_g, beta, slot_base, slot_stride, row0, len, c + 2,
-                                  Hk, Hv, kh, vh, tile, lt);
-        }
-        __syncthreads();
+        ring_barrier();
+        const rsrc_t ro = make_rsrc(obase, (uint32_t)min((long)C, rem) * rs);
+        spine_step<kOutF32>(ring + (c % N_STAGES) * ST_BYTES, h, ro, lane_off, soff, g, fo);
+        obase += (size_t)C * rs;
+        rem -= C;
     }
 
-    if (w < 2 && h_final) {
+    if (h_final) {
 #pragma unroll
         for (int db = 0; db < 8; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                h_final[hoff + (size_t)(16 * db + 4 * g + r) * D + col] = h[db][r];
+                h_final[hoff + (size_t)(sig_tile(db) + 8 * g + r) * D + col] = h[db][r];
     }
 }
 
@@ -763,7 +809,7 @@ bool prefill_mfma_accepts(const PrefillArgs& a)
 Geometry prefill_mfma_geometry(const PrefillArgs& a)
 {
     Geometry g{"gdn_wy_prep_kernel+gdn_spine_kernel", {(unsigned)(a.Hv * N_TILES), (unsigned)a.B, 1u}, 256u,
-               (unsigned)(2 * sizeof(SpineBuf))};
+               (unsigned)(N_STAGES * ST_BYTES)};
     return g;
 }
 
