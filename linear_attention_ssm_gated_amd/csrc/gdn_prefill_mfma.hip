@@ -39,12 +39,6 @@ namespace {
 
 constexpr int C = 64;        // chunk rows
 constexpr int D = 128;       // dk = dv
-// LDS row strides.  A fragment read is 16 lanes x 8 bytes from 16 consecutive
-// rows; rows that start 8 bytes apart modulo 128 put those 16 reads on
-// distinct banks, so bf16 rows are padded by 4 elements (8 bytes).
-constexpr int LDK = D + 4;   // LDS row stride (bf16) of K and Q: 264 bytes
-constexpr int LDC = C + 4;   // LDS row stride (bf16) of T, P, K^T and V^T: 136 bytes
-constexpr int LDF = C + 4;   // LDS row stride (fp32) of A and the fp32 T
 constexpr int TILE_COLS = 32;            // dv columns per spine workgroup
 constexpr int N_TILES = D / TILE_COLS;   // 4
 constexpr int SLOT_ELEMS = 2 * C * C;    // T then P, bf16, per (chunk, v-head)
@@ -65,15 +59,6 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// A operand of one 32-wide k-step: row `row` of a bf16 LDS matrix, columns
-// k0 + 4g .. +3 and k0 + 16 + 4g .. +3.
-__device__ __forceinline__ s16x8 frag_a(const uint16_t* base, int ld, int row, int k0, int g) {
-    const uint16_t* p = base + row * ld + k0 + 4 * g;
-    s16x4 lo = *reinterpret_cast<const s16x4*>(p);
-    s16x4 hi = *reinterpret_cast<const s16x4*>(p + 16);
-    return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
 __device__ __forceinline__ short bf16_bits(float x) {
     return (short)__builtin_bit_cast(uint16_t, (__bf16)x);
 }
@@ -82,12 +67,6 @@ __device__ __forceinline__ short bf16_bits(float x) {
 __device__ __forceinline__ s16x8 frag_b(f32x4 lo, f32x4 hi) {
     return s16x8{bf16_bits(lo[0]), bf16_bits(lo[1]), bf16_bits(lo[2]), bf16_bits(lo[3]),
                  bf16_bits(hi[0]), bf16_bits(hi[1]), bf16_bits(hi[2]), bf16_bits(hi[3])};
-}
-
-// 16 bytes to an LDS row that is only 8-byte aligned.
-__device__ __forceinline__ void store16(uint16_t* dst, const uint4& v) {
-    reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
-    reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -145,49 +124,84 @@ gdn_chunk_table_kernel(const int32_t* __restrict__ cu, int B, int T, int32_t* __
     }
 }
 
-// Loads rows [row0, row0 + L) of one head of a [rows][H][128] bf16 tensor into
-// a [C][LDK] LDS tile, zero-filling rows >= L.  256 or 128 threads.
-template <int NT>
-__device__ __forceinline__ void load_rows_128(uint16_t* dst, const uint16_t* src, long row0, int L,
-                                              int H, int head, int tid)
-{
-    for (int idx = tid; idx < C * (D / 8); idx += NT) {
-        const int r = idx >> 4, c8 = (idx & 15) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < L) v = *reinterpret_cast<const uint4*>(src + ((size_t)(row0 + r) * H + head) * D + c8);
-        *reinterpret_cast<uint4*>(dst + r * LDK + c8) = v;
-    }
+// ---------------------------------------------------------------------------
+// Buffer resources (gfx9 family): a wave-uniform base in SGPRs, 32-bit lane
+// and SGPR byte offsets, and a byte range.  On gfx950 the range check covers
+// both offsets: reads beyond the range return 0 and writes beyond it are
+// dropped, which is how partial chunks are masked.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x8 buffer_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return __builtin_bit_cast(s16x8, v);
+}
+
+// Orders one wave's LDS writes before its later LDS reads of other lanes'
+// data (a compiler fence: the hardware keeps one wave's LDS operations in
+// order).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per (chunk, k-head): K K^T and Q K^T once, then for each
-// v-head of the group its decay, A, T and P.
-__global__ void __launch_bounds__(256)
+// WY prep: one wave per (chunk, v-head), no workgroup barriers.  It forms the
+// chunk's Gram matrices K K^T and Q K^T on MFMA from fragments read straight
+// from memory, then A = strict_lower(beta_r exp(G_r - G_s) (K K^T)_rs),
+// P = lower_incl(exp(G_r - G_s) (Q K^T)_rs) and T = (I + A)^-1, and writes T
+// and P as bf16 64 x 64 row-major matrices to the chunk's slot.
+//
+// A and T live in LDS as their 10 lower 16 x 16 fp32 blocks.  Row r of a
+// block starts at float 16 (r + r/4), so the four rows 4g + i that one
+// accumulator register spans lie in four different 16-bank windows, and
+// element c of the row sits at c ^ 4 (r/4); a block spans 304 floats.  Block
+// index b = i (i+1)/2 + j starts at float 352 b, plus 16 for b = 2 and 9,
+// which puts the four diagonal blocks (b = 0, 2, 5, 9) in four different
+// windows as well.  MFMA operand reads, accumulator writes and the column
+// writes of the diagonal solve are then free of bank conflicts.
+__host__ __device__ constexpr int blk_base_idx(int b) { return 352 * b + ((b == 2 || b == 9) ? 16 : 0); }
+__host__ __device__ constexpr int blk_base(int i, int j) { return blk_base_idx(i * (i + 1) / 2 + j); }
+__host__ __device__ constexpr int blk_elem(int r, int c) { return 16 * (r + (r >> 2)) + (c ^ (4 * (r >> 2))); }
+constexpr int PREP_MAT = blk_base(3, 3) + blk_elem(15, 0) + 16;   // floats per matrix
+constexpr int PREP_LDS_FLOATS = 2 * PREP_MAT + 2 * C;
+constexpr int P_STAGE = 72;   // bf16 row stride of P staged for the transposed store
+static_assert(C * P_STAGE * 2 <= PREP_MAT * 4, "P staging must fit in the T area");
+
+// fp32 16 x 16 x 16 product on MFMA, operands from LDS blocks laid out as above:
+// acc += X Y.  aoff / boff: this lane's A / B operand offsets per k-step.
+__device__ __forceinline__ f32x4 mm16(const float* X, const float* Y, f32x4 acc,
+                                      const int (&aoff)[4], const int (&boff)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma_f32(X[aoff[s]], Y[boff[s]], acc);
+    return acc;
+}
+// accumulator tile -> LDS block (this lane's rows 4g + i, column n)
+__device__ __forceinline__ void put16(float* Z, f32x4 v, int doff, float sign) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Z[doff + 16 * i] = sign * v[i];
+}
+
+__global__ void __launch_bounds__(64)
 gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const float* __restrict__ log_g, const float* __restrict__ beta,
                    uint16_t* __restrict__ slots, int B, int T, int Hk, int Hv,
                    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_base,
                    int nc_dense)
 {
-    // K and Q (bf16) while the Grams are formed; afterwards the same bytes
-    // hold A and T (fp32) of the v-head being solved.
-    constexpr size_t kRaw = 2 * C * LDF * sizeof(float) > 2 * C * LDK * sizeof(uint16_t)
-                                ? 2 * C * LDF * sizeof(float) : 2 * C * LDK * sizeof(uint16_t);
-    __shared__ __attribute__((aligned(16))) unsigned char sRaw[kRaw];
-    __shared__ __attribute__((aligned(16))) float sKK[C * LDF];
-    __shared__ __attribute__((aligned(16))) float sQK[C * LDF];
-    __shared__ float sG[C], sB[C];
-    uint16_t* sK = reinterpret_cast<uint16_t*>(sRaw);
-    uint16_t* sQ = sK + C * LDK;
-    float* sA = reinterpret_cast<float*>(sRaw);
-    float* sT = sA + C * LDF;
-    static_assert(2 * C * LDF * sizeof(float) <= sizeof(sRaw), "A and T must fit where K and Q were");
+    __shared__ __attribute__((aligned(16))) float lds[PREP_LDS_FLOATS];
+    float* sA = lds;
+    float* sT = lds + PREP_MAT;
+    float* sG = lds + 2 * PREP_MAT;   // G log2(e) per row
+    float* sBt = sG + C;              // beta per row
+    uint16_t* sP = reinterpret_cast<uint16_t*>(sT);   // P staged here before T is formed
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int g = lane >> 4, n = lane & 15;
-    const int x = blockIdx.x, kh = blockIdx.y;
-    const int G = Hv / Hk;
+    const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
+    const int x = blockIdx.x, vh = blockIdx.y;
+    const int kh = vh / (Hv / Hk);
 
     int b, c;
     if (!cu) {
@@ -206,147 +220,167 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     long row0, len;
     seq_rows(cu, b, T, &row0, &len);
     row0 += (long)c * C;
-    const int L = (int)min((long)C, len - (long)c * C);
+    const uint32_t L = __builtin_amdgcn_readfirstlane((uint32_t)min((long)C, len - (long)c * C));
+    const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)row0);
+    const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)row0 >> 32));
+    const size_t ru = ((size_t)rhi << 32) | rlo;
 
-    {   // K and Q rows, all loads in flight before any store
-        uint4 kr[4], qr[4];
+    // K and Q fragments: rows 16 rb + n, k-slots 32 kk + 8 g .. +7; rows >= L read as 0
+    const uint32_t rowK = (uint32_t)Hk * D * 2u;
+    const rsrc_t rk = make_rsrc(k + (ru * Hk + kh) * D, L * rowK);
+    const rsrc_t rq = make_rsrc(q + (ru * Hk + kh) * D, L * rowK);
+    const uint32_t voff = (uint32_t)n * rowK + 16u * g;
+    s16x8 kf[4][4], qf[4][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
-            kr[i] = qr[i] = make_uint4(0, 0, 0, 0);
-            if (r < L) {
-                const size_t off = ((size_t)(row0 + r) * Hk + kh) * D + c8;
-                kr[i] = *reinterpret_cast<const uint4*>(k + off);
-                qr[i] = *reinterpret_cast<const uint4*>(q + off);
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            kf[rb][kk] = buffer_load16(rk, voff + 64u * kk, 16u * rb * rowK);
+            qf[rb][kk] = buffer_load16(rq, voff + 64u * kk, 16u * rb * rowK);
+        }
+    const rsrc_t rg = make_rsrc(log_g + ru * Hv + vh, L * Hv * 4u);
+    const rsrc_t rb_ = make_rsrc(beta + ru * Hv + vh, L * Hv * 4u);
+    const float gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)lane * Hv * 4u, 0, 0));
+    const float bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb_, (uint32_t)lane * Hv * 4u, 0, 0));
+
+    // G = cumsum of log_g, kept as G log2(e) so that exp(G_r - G_s) is one exp2
+    const float Gs = wave_inclusive_sum(gv, lane);
+    sG[lane] = Gs * 1.4426950408889634f;
+    sBt[lane] = bv;
+
+    // Gram tiles (rb, cb), cb <= rb, in accumulators
+    f32x4 KK[10], QK[10];
+#pragma unroll
+    for (int rb = 0, t = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb <= rb; ++cb, ++t) {
+            f32x4 a = zero4(), p = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                a = mfma_bf16(kf[rb][kk], kf[cb][kk], a);
+                p = mfma_bf16(qf[rb][kk], kf[cb][kk], p);
             }
+            KK[t] = a;
+            QK[t] = p;
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
-            store16(sK + r * LDK + c8, kr[i]);
-            store16(sQ + r * LDK + c8, qr[i]);
-        }
-    }
-    __syncthreads();
+    wave_lds_sync();
 
-    // raw Grams, lower 16x16 tiles (diagonal tiles whole)
-    for (int t = w; t < 20; t += 4) {
-        const bool is_kk = t < 10;
-        int tt = is_kk ? t : t - 10, rb = 0;
-        while (tt > rb) { tt -= rb + 1; ++rb; }
-        const int cb = tt;
-        const uint16_t* a_src = is_kk ? sK : sQ;
-        f32x4 acc = zero4();
+    // A -> LDS blocks, P -> bf16 staging; this lane holds rows 16 rb + 4g + i, column 16 cb + n
+    float Gc[4];
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-            acc = mfma_bf16(frag_a(a_src, LDK, 16 * rb + n, 32 * kk, g),
-                            frag_a(sK, LDK, 16 * cb + n, 32 * kk, g), acc);
-        float* dst = is_kk ? sKK : sQK;
+    for (int cb = 0; cb < 4; ++cb) Gc[cb] = sG[16 * cb + n];
+    const int doff = 80 * g + (n ^ (4 * g));   // blk_elem(4g + i, n) - 16 i
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(16 * rb + 4 * g + r) * LDF + 16 * cb + n] = acc[r];
-    }
-    __syncthreads();
-
-    for (int gi = 0; gi < G; ++gi) {
-        const int vh = kh * G + gi;
-        if (w == 0) {
-            float gv = 0.f, bv = 0.f;
-            if (lane < L) {
-                gv = log_g[(size_t)(row0 + lane) * Hv + vh];
-                bv = beta[(size_t)(row0 + lane) * Hv + vh];
-            }
-            sG[lane] = wave_inclusive_sum(gv, lane);
-            sB[lane] = bv;
-        } else {
-            for (int e = tid - 64; e < C * LDF; e += 192) sT[e] = 0.f;
-        }
-        __syncthreads();
-
-        uint16_t* dstT = slots + ((size_t)x * Hv + vh) * SLOT_ELEMS;
-        uint16_t* dstP = dstT + C * C;
-        // A (fp32, LDS) and P (bf16, straight to the workspace), 8 entries per step
+    for (int rb = 0, t = 0; rb < 4; ++rb) {
+        const float4 gr4 = *reinterpret_cast<const float4*>(sG + 16 * rb + 4 * g);
+        const float4 br4 = *reinterpret_cast<const float4*>(sBt + 16 * rb + 4 * g);
+        const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
+        const float br[4] = {br4.x, br4.y, br4.z, br4.w};
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i, r = idx >> 3, s0 = (idx & 7) * 8;
-            const float gr = sG[r], br = sB[r];
-            s16x8 pv;
+        for (int cb = 0; cb <= rb; ++cb, ++t) {
+            float* Ablk = sA + blk_base(rb, cb);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s = s0 + e;
-                // upper-triangle Gram entries were never written: select, never multiply
-                const float gam = s <= r ? __expf(gr - sG[s]) : 0.f;
-                sA[r * LDF + s] = s < r ? br * gam * sKK[r * LDF + s] : 0.f;
-                pv[e] = s <= r ? bf16_bits(gam * sQK[r * LDF + s]) : (short)0;
-            }
-            *reinterpret_cast<s16x8*>(dstP + r * C + s0) = pv;
-        }
-        __syncthreads();
-
-        // T_ii = (I + A_ii)^-1: wave w, lane j walks column j of block w.
-        if (lane < 16) {
-            const int j = lane, o = 16 * w;
-            float xc[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) xc[r] = r == j ? 1.f : 0.f;
-#pragma unroll
-            for (int r = 1; r < 16; ++r) {
-                const float4* arow = reinterpret_cast<const float4*>(sA + (o + r) * LDF + o);
-                float a[16];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 t4 = arow[q4];
-                    a[4 * q4] = t4.x; a[4 * q4 + 1] = t4.y; a[4 * q4 + 2] = t4.z; a[4 * q4 + 3] = t4.w;
+            for (int i = 0; i < 4; ++i) {
+                const float e = __builtin_amdgcn_exp2f(gr[i] - Gc[cb]);
+                float av = br[i] * e * KK[t][i];
+                float pv = e * QK[t][i];
+                if (rb == cb) {   // diagonal tile: A strictly lower, P lower with the diagonal
+                    av = (4 * g + i > n) ? av : 0.f;
+                    pv = (4 * g + i >= n) ? pv : 0.f;
                 }
-                float s = 0.f;
-#pragma unroll
-                for (int m = 0; m < r; ++m) s += a[m] * xc[m];
-                if (r > j) xc[r] = -s;
+                Ablk[doff + 16 * i] = av;
+                sP[(16 * rb + 4 * g + i) * P_STAGE + 16 * cb + n] = (uint16_t)bf16_bits(pv);
             }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sT[(o + r) * LDF + o + j] = xc[r];
         }
-        __syncthreads();
-
-        // blocks below the diagonal, by distance d: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
-        for (int d = 1; d < 4; ++d) {
-            if (w < 4 - d) {
-                const int i = w + d, j = w;
-                f32x4 acc = zero4();
-                for (int m = j; m < i; ++m)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        acc = mfma_f32(sA[(16 * i + n) * LDF + 16 * m + 4 * s + g],
-                                       sT[(16 * m + 4 * s + g) * LDF + 16 * j + n], acc);
-                // acc (lane 16g+n, reg r) = M[4g + r][n]: the B operand with k = 4g + s at step s
-                f32x4 t = zero4();
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    t = mfma_f32(sT[(16 * i + n) * LDF + 16 * i + 4 * g + s], acc[s], t);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sT[(16 * i + 4 * g + r) * LDF + 16 * j + n] = -t[r];
-            }
-            __syncthreads();
-        }
-
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i, r = idx >> 3, c8 = (idx & 7) * 8;
-            s16x8 tv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tv[e] = bf16_bits(sT[r * LDF + c8 + e]);
-            *reinterpret_cast<s16x8*>(dstT + r * C + c8) = tv;
-        }
-        __syncthreads();   // sG, sA and sT are rewritten by the next v-head
     }
-}
+    wave_lds_sync();
 
-// ---------------------------------------------------------------------------
-// Buffer resources (gfx9 family): a wave-uniform base in SGPRs, 32-bit lane
-// byte offsets, and a byte range; reads beyond the range return 0 and writes
-// beyond it are dropped, which is how partial chunks are masked.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+    // P rows -> workspace (tiles above the diagonal are zero)
+    uint16_t* dstT = slots + ((size_t)x * Hv + vh) * SLOT_ELEMS;
+    uint16_t* dstP = dstT + C * C;
+    const int cg = lane & 7, jb = cg >> 1;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int r = (lane >> 3) + 8 * p, ib = p >> 1;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (jb <= ib) v = *reinterpret_cast<const uint4*>(sP + r * P_STAGE + 8 * cg);
+        *reinterpret_cast<uint4*>(dstP + r * C + 8 * cg) = v;
+    }
+    wave_lds_sync();
+
+    // T_ii = (I + A_ii)^-1 for the four diagonal blocks: lane (g, n) solves
+    // column n of block g by forward substitution.
+    {
+        const int dbase = blk_base_idx(g * (g + 3) / 2);
+        const float* Ad = sA + dbase;
+        float xc[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float s = 0.f;
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                if (4 * qd >= r) break;
+                const float4 a4 = *reinterpret_cast<const float4*>(Ad + 16 * (r + (r >> 2)) + 4 * (qd ^ (r >> 2)));
+                const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * qd + e < r) s = fmaf(a[e], xc[4 * qd + e], s);
+            }
+            xc[r] = (r == n ? 1.f : 0.f) - s;
+        }
+        float* Td = sT + dbase;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Td[16 * (r + (r >> 2)) + (n ^ (4 * (r >> 2)))] = xc[r];
+    }
+    wave_lds_sync();
+
+    // blocks below the diagonal, by distance: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
+    int aoff[4], boff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        aoff[s] = 16 * (n + (n >> 2)) + ((4 * s + g) ^ (4 * (n >> 2)));   // X[n][4s + g]
+        boff[s] = 16 * (4 * s + g + s) + (n ^ (4 * s));                   // Y[4s + g][n]
+    }
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+        f32x4 M[3];
+#pragma unroll
+        for (int j = 0; j + d < 4; ++j) {
+            const int i = j + d;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int m = j; m < i; ++m) acc = mm16(sA + blk_base(i, m), sT + blk_base(m, j), acc, aoff, boff);
+            M[j] = acc;
+        }
+#pragma unroll
+        for (int j = 0; j + d < 4; ++j) put16(sT + blk_base(j + d, j), M[j], doff, 1.f);
+        wave_lds_sync();
+#pragma unroll
+        for (int j = 0; j + d < 4; ++j) {
+            const int i = j + d;
+            M[j] = mm16(sT + blk_base(i, i), sT + blk_base(i, j), zero4(), aoff, boff);
+        }
+        wave_lds_sync();   // every read of M precedes its overwrite
+#pragma unroll
+        for (int j = 0; j + d < 4; ++j) put16(sT + blk_base(j + d, j), M[j], doff, -1.f);
+        wave_lds_sync();
+    }
+
+    // T rows -> workspace as bf16 (tiles above the diagonal are zero)
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int r = (lane >> 3) + 8 * p, ib = p >> 1, rr = r & 15;
+        s16x8 v = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (jb <= ib) {
+            const float* blk = sT + blk_base(ib, jb);
+            const int c0 = 2 * (cg & 1);   // first 4-column granule
+            const float4 a = *reinterpret_cast<const float4*>(blk + 16 * (rr + (rr >> 2)) + 4 * (c0 ^ (rr >> 2)));
+            const float4 e = *reinterpret_cast<const float4*>(blk + 16 * (rr + (rr >> 2)) + 4 * ((c0 + 1) ^ (rr >> 2)));
+            v = s16x8{bf16_bits(a.x), bf16_bits(a.y), bf16_bits(a.z), bf16_bits(a.w),
+                      bf16_bits(e.x), bf16_bits(e.y), bf16_bits(e.z), bf16_bits(e.w)};
+        }
+        *reinterpret_cast<s16x8*>(dstT + r * C + 8 * cg) = v;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -824,7 +858,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
         hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.B, a.T, base);
     }
     if (n_slots > 0) {
-        hipLaunchKernelGGL(gdn_wy_prep_kernel, dim3((unsigned)n_slots, a.Hk), dim3(256), 0, s,
+        hipLaunchKernelGGL(gdn_wy_prep_kernel, dim3((unsigned)n_slots, a.Hv), dim3(64), 0, s,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, a.log_g, a.beta, slots, a.B,
                            a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense);
     }
