@@ -149,59 +149,112 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ---------------------------------------------------------------------------
-// WY prep: one wave per (chunk, v-head), no workgroup barriers.  It forms the
-// chunk's Gram matrices K K^T and Q K^T on MFMA from fragments read straight
-// from memory, then A = strict_lower(beta_r exp(G_r - G_s) (K K^T)_rs),
-// P = lower_incl(exp(G_r - G_s) (Q K^T)_rs) and T = (I + A)^-1, and writes T
-// and P as bf16 64 x 64 row-major matrices to the chunk's slot.
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// Buffer->LDS DMA, written as inline assembly: the compiler would otherwise
+// make later LDS reads wait for every DMA in flight.  Completion is tracked
+// by hand (wait_vmcnt).  The range check that zero-fills rows beyond a chunk
+// covers the lane offset and the SGPR offset alike.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+struct Rsrc { u32x4 d; };
+__device__ __forceinline__ Rsrc make_dma_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    Rsrc r;
+    r.d = u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu),
+                (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+    return r;
+}
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)p;
+}
+__device__ __forceinline__ void dma16(const Rsrc& r, unsigned char* lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"((uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(lds))), "v"(voff), "s"(r.d),
+                    "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const Rsrc& r, unsigned char* lds, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"((uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(lds))), "v"(voff), "s"(r.d) : "memory", "m0");
+}
+__device__ __forceinline__ s16x8 lds_read16(const unsigned char* p) {
+    return *reinterpret_cast<const s16x8*>(p);
+}
+// ---------------------------------------------------------------------------
+// WY prep: one workgroup per (chunk, k-head, group of up to four of its
+// v-heads), one wave per v-head.  The workgroup stages the chunk's K and Q
+// rows in LDS once; each wave then forms, for its v-head,
+//   A = strict_lower(beta_r exp(G_r - G_s) (K K^T)_rs),
+//   P = lower_incl(exp(G_r - G_s) (Q K^T)_rs),   T = (I + A)^-1,
+// and writes T and P as bf16 64 x 64 row-major matrices to the chunk's slot.
+// The waves never wait for each other after the staging.
 //
-// A and T live in LDS as their 10 lower 16 x 16 fp32 blocks.  Row r of a
-// block starts at float 16 (r + r/4), so the four rows 4g + i that one
-// accumulator register spans lie in four different 16-bank windows, and
-// element c of the row sits at c ^ 4 (r/4); a block spans 304 floats.  Block
-// index b = i (i+1)/2 + j starts at float 352 b, plus 16 for b = 2 and 9,
-// which puts the four diagonal blocks (b = 0, 2, 5, 9) in four different
-// windows as well.  MFMA operand reads, accumulator writes and the column
-// writes of the diagonal solve are then free of bank conflicts.
-__host__ __device__ constexpr int blk_base_idx(int b) { return 352 * b + ((b == 2 || b == 9) ? 16 : 0); }
-__host__ __device__ constexpr int blk_base(int i, int j) { return blk_base_idx(i * (i + 1) / 2 + j); }
-__host__ __device__ constexpr int blk_elem(int r, int c) { return 16 * (r + (r >> 2)) + (c ^ (4 * (r >> 2))); }
-constexpr int PREP_MAT = blk_base(3, 3) + blk_elem(15, 0) + 16;   // floats per matrix
-constexpr int PREP_LDS_FLOATS = 2 * PREP_MAT + 2 * C;
-constexpr int P_STAGE = 72;   // bf16 row stride of P staged for the transposed store
-static_assert(C * P_STAGE * 2 <= PREP_MAT * 4, "P staging must fit in the T area");
-
-// fp32 16 x 16 x 16 product on MFMA, operands from LDS blocks laid out as above:
-// acc += X Y.  aoff / boff: this lane's A / B operand offsets per k-step.
-__device__ __forceinline__ f32x4 mm16(const float* X, const float* Y, f32x4 acc,
-                                      const int (&aoff)[4], const int (&boff)[4]) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma_f32(X[aoff[s]], Y[boff[s]], acc);
-    return acc;
+// Gram tiles are formed above the diagonal, tile (m, i) = K_m K_i^T and
+// K_m Q_i^T (16-row blocks, m <= i), so that lane (g, n) register s holds
+// the entry of row 16 i + n, column 16 m + 4g + s of K K^T and of Q K^T: the
+// decay factor of both is the same, a P tile leaves as four consecutive bf16
+// of one row, and an off-diagonal A tile is directly the A operand of an
+// fp32 MFMA whose k-slot of lane group g at step s is 4g + s.
+//
+// T is formed on 16 x 16 fp32 blocks: T_ii = (I + A_ii)^-1 by forward
+// substitution, then T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj by distance
+// i - j.  Block row r is stored at slot p(r) = 4 (r/4) + ((r + r/4) % 4) and
+// element c at c ^ 4 (r/4), so that the rows 4g + s that one MFMA operand or
+// accumulator register spans fall in four different 16-bank windows.  The
+// four diagonal blocks start at floats 272 i (four windows again), the six
+// below the diagonal after them.  A diagonal block holds A_ii transposed
+// until T_ii replaces it.
+__host__ __device__ constexpr int prow(int r) { return 4 * (r >> 2) + ((r + (r >> 2)) & 3); }
+__host__ __device__ constexpr int blk_elem(int r, int c) { return 16 * prow(r) + (c ^ (4 * (r >> 2))); }
+__host__ __device__ constexpr int t_blk(int i, int j) {
+    return i == j ? 272 * i : 1088 + 256 * ((i - 1) * i / 2 + j);
 }
-// accumulator tile -> LDS block (this lane's rows 4g + i, column n)
-__device__ __forceinline__ void put16(float* Z, f32x4 v, int doff, float sign) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Z[doff + 16 * i] = sign * v[i];
+constexpr int PREP_WAVE_FLOATS = 1088 + 6 * 256;          // per wave, over the K/Q staging
+constexpr int PREP_STAGE_BYTES = 2 * C * D * 2;           // K then Q, 256-byte rows
+// K/Q staging: granule q of row r at q ^ (r % 8), so that a fragment read (8
+// lanes, 8 consecutive rows, one granule) is free of bank conflicts.  After
+// the larger of the staging area and the per-wave regions come G log2(e) and
+// beta per row for each wave.
+__host__ __device__ constexpr int prep_gb_base(int nw) {   // floats
+    return PREP_STAGE_BYTES / 4 > nw * PREP_WAVE_FLOATS ? PREP_STAGE_BYTES / 4 : nw * PREP_WAVE_FLOATS;
+}
+__host__ __device__ constexpr size_t prep_lds_bytes(int nw) {
+    return (size_t)(prep_gb_base(nw) + nw * 2 * C) * sizeof(float);
 }
 
-__global__ void __launch_bounds__(64)
+// Inclusive prefix sum over the 64 lanes of a wave on DPP: shifts within
+// rows of 16 lanes, then each row adds the last lane of the rows before it.
+__device__ __forceinline__ float wave_scan_dpp(float x) {
+#define GDN_DPP_ADD(ctrl, rmask) \
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, rmask, 0xf, false))
+    GDN_DPP_ADD(0x111, 0xf);   // row_shr:1
+    GDN_DPP_ADD(0x112, 0xf);   // row_shr:2
+    GDN_DPP_ADD(0x114, 0xf);   // row_shr:4
+    GDN_DPP_ADD(0x118, 0xf);   // row_shr:8
+    GDN_DPP_ADD(0x142, 0xa);   // row_bcast:15 into rows 1 and 3
+    GDN_DPP_ADD(0x143, 0xc);   // row_bcast:31 into rows 2 and 3
+#undef GDN_DPP_ADD
+    return x;
+}
+
+extern __shared__ __attribute__((aligned(1024))) float prep_lds[];
+
+__global__ void __launch_bounds__(256, 3)
 gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const float* __restrict__ log_g, const float* __restrict__ beta,
                    uint16_t* __restrict__ slots, int B, int T, int Hk, int Hv,
                    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_base,
                    int nc_dense)
 {
-    __shared__ __attribute__((aligned(16))) float lds[PREP_LDS_FLOATS];
-    float* sA = lds;
-    float* sT = lds + PREP_MAT;
-    float* sG = lds + 2 * PREP_MAT;   // G log2(e) per row
-    float* sBt = sG + C;              // beta per row
-    uint16_t* sP = reinterpret_cast<uint16_t*>(sT);   // P staged here before T is formed
-
-    const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
-    const int x = blockIdx.x, vh = blockIdx.y;
-    const int kh = vh / (Hv / Hk);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), nw = blockDim.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    const int x = blockIdx.x, kh = blockIdx.y;
+    const int G = Hv / Hk;
+    const int h = blockIdx.z * nw + w;   // this wave's v-head within the k-head
+    const int vh = kh * G + h;
+    float* lds = prep_lds + w * PREP_WAVE_FLOATS;
+    float* sG = prep_lds + prep_gb_base(nw) + w * 2 * C;   // G log2(e) per row
+    float* sBt = sG + C;                                        // beta per row
 
     int b, c;
     if (!cu) {
@@ -225,157 +278,182 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)row0 >> 32));
     const size_t ru = ((size_t)rhi << 32) | rlo;
 
-    // K and Q fragments: rows 16 rb + n, k-slots 32 kk + 8 g .. +7; rows >= L read as 0
-    const uint32_t rowK = (uint32_t)Hk * D * 2u;
-    const rsrc_t rk = make_rsrc(k + (ru * Hk + kh) * D, L * rowK);
-    const rsrc_t rq = make_rsrc(q + (ru * Hk + kh) * D, L * rowK);
-    const uint32_t voff = (uint32_t)n * rowK + 16u * g;
-    s16x8 kf[4][4], qf[4][4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            kf[rb][kk] = buffer_load16(rk, voff + 64u * kk, 16u * rb * rowK);
-            qf[rb][kk] = buffer_load16(rq, voff + 64u * kk, 16u * rb * rowK);
-        }
-    const rsrc_t rg = make_rsrc(log_g + ru * Hv + vh, L * Hv * 4u);
-    const rsrc_t rb_ = make_rsrc(beta + ru * Hv + vh, L * Hv * 4u);
-    const float gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)lane * Hv * 4u, 0, 0));
-    const float bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb_, (uint32_t)lane * Hv * 4u, 0, 0));
-
-    // G = cumsum of log_g, kept as G log2(e) so that exp(G_r - G_s) is one exp2
-    const float Gs = wave_inclusive_sum(gv, lane);
-    sG[lane] = Gs * 1.4426950408889634f;
-    sBt[lane] = bv;
-
-    // Gram tiles (rb, cb), cb <= rb, in accumulators
-    f32x4 KK[10], QK[10];
-#pragma unroll
-    for (int rb = 0, t = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int cb = 0; cb <= rb; ++cb, ++t) {
-            f32x4 a = zero4(), p = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                a = mfma_bf16(kf[rb][kk], kf[cb][kk], a);
-                p = mfma_bf16(qf[rb][kk], kf[cb][kk], p);
-            }
-            KK[t] = a;
-            QK[t] = p;
-        }
-    wave_lds_sync();
-
-    // A -> LDS blocks, P -> bf16 staging; this lane holds rows 16 rb + 4g + i, column 16 cb + n
-    float Gc[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) Gc[cb] = sG[16 * cb + n];
-    const int doff = 80 * g + (n ^ (4 * g));   // blk_elem(4g + i, n) - 16 i
-#pragma unroll
-    for (int rb = 0, t = 0; rb < 4; ++rb) {
-        const float4 gr4 = *reinterpret_cast<const float4*>(sG + 16 * rb + 4 * g);
-        const float4 br4 = *reinterpret_cast<const float4*>(sBt + 16 * rb + 4 * g);
-        const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
-        const float br[4] = {br4.x, br4.y, br4.z, br4.w};
-#pragma unroll
-        for (int cb = 0; cb <= rb; ++cb, ++t) {
-            float* Ablk = sA + blk_base(rb, cb);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e = __builtin_amdgcn_exp2f(gr[i] - Gc[cb]);
-                float av = br[i] * e * KK[t][i];
-                float pv = e * QK[t][i];
-                if (rb == cb) {   // diagonal tile: A strictly lower, P lower with the diagonal
-                    av = (4 * g + i > n) ? av : 0.f;
-                    pv = (4 * g + i >= n) ? pv : 0.f;
-                }
-                Ablk[doff + 16 * i] = av;
-                sP[(16 * rb + 4 * g + i) * P_STAGE + 16 * cb + n] = (uint16_t)bf16_bits(pv);
-            }
+    // stage the chunk's K and Q rows (rows >= L read as 0): 32 DMAs of 4 rows
+    unsigned char* sKQ = reinterpret_cast<unsigned char*>(prep_lds);
+    {
+        const uint32_t rowK = (uint32_t)Hk * D * 2u;
+        const Rsrc rk = make_dma_rsrc(k + (ru * Hk + kh) * D, L * rowK);
+        const Rsrc rq = make_dma_rsrc(q + (ru * Hk + kh) * D, L * rowK);
+        const int rr = lane >> 4, p = lane & 15;
+        const uint32_t o0 = rr * rowK + 16u * (p ^ rr), o1 = rr * rowK + 16u * (p ^ (4 + rr));
+        for (int j = w; j < 32; j += nw) {
+            const int jj = j & 15;
+            dma16(j < 16 ? rk : rq, sKQ + (j >> 4) * (C * D * 2) + 1024 * jj, (jj & 1) ? o1 : o0,
+                  4u * jj * rowK);
         }
     }
-    wave_lds_sync();
+    // this v-head's log_g and beta (an empty range for a wave past the last
+    // v-head: it reads nothing); G = cumsum of log_g, kept as G log2(e) so
+    // that exp(G_r - G_s) is one exp2
+    {
+        const uint32_t gb_bytes = h < G ? L * Hv * 4u : 0u;
+        const rsrc_t rg = make_rsrc(log_g + ru * Hv + vh, gb_bytes);
+        const rsrc_t rb_ = make_rsrc(beta + ru * Hv + vh, gb_bytes);
+        const float gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)lane * Hv * 4u, 0, 0));
+        const float bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb_, (uint32_t)lane * Hv * 4u, 0, 0));
+        sG[lane] = wave_scan_dpp(gv) * 1.4426950408889634f;
+        sBt[lane] = bv;
+    }
+    // the DMA is inline assembly the compiler does not track: wait for it
+    // explicitly, then let every wave see every wave's rows
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
+    __syncthreads();
 
-    // P rows -> workspace (tiles above the diagonal are zero)
+    // decay factors of this lane's entries: row 16 i + n, column 16 m + 4g + s
+    float Gr[4], Bt[4];
+    f32x4 Gc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        Gr[i] = sG[16 * i + n];
+        Bt[i] = sBt[16 * i + n];
+        const float4 t4 = *reinterpret_cast<const float4*>(sG + 16 * i + 4 * g);
+        Gc[i] = f32x4{t4.x, t4.y, t4.z, t4.w};
+    }
+
+    // Gram tiles by block column i: P leaves at once, A stays in registers
     uint16_t* dstT = slots + ((size_t)x * Hv + vh) * SLOT_ELEMS;
     uint16_t* dstP = dstT + C * C;
-    const int cg = lane & 7, jb = cg >> 1;
+    const bool live = h < G;
+    s16x8 kf[4][4];
+    f32x4 Aoff[6];   // A_im, m < i, index (i - 1) i / 2 + m
+    f32x4 Adg[4];    // A_ii: register s = A_ii[n][4g + s]
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int r = (lane >> 3) + 8 * p, ib = p >> 1;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (jb <= ib) v = *reinterpret_cast<const uint4*>(sP + r * P_STAGE + 8 * cg);
-        *reinterpret_cast<uint4*>(dstP + r * C + 8 * cg) = v;
+    for (int i = 0; i < 4; ++i) {
+        s16x8 qf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const unsigned char* fr = sKQ + (16 * i + n) * 256 + 16 * ((4 * kk + g) ^ (n & 7));
+            kf[i][kk] = lds_read16(fr);
+            qf[kk] = lds_read16(fr + C * D * 2);
+        }
+#pragma unroll
+        for (int m = 0; m <= i; ++m) {
+            f32x4 kk_acc = zero4(), kq_acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                kk_acc = mfma_bf16(kf[m][kk], kf[i][kk], kk_acc);
+                kq_acc = mfma_bf16(kf[m][kk], qf[kk], kq_acc);
+            }
+            f32x4 av, pv;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const float e = __builtin_amdgcn_exp2f(Gr[i] - Gc[m][s2]);
+                av[s2] = Bt[i] * e * kk_acc[s2];
+                pv[s2] = e * kq_acc[s2];
+                if (m == i) {   // A strictly lower, P lower with the diagonal
+                    av[s2] = (n > 4 * g + s2) ? av[s2] : 0.f;
+                    pv[s2] = (n >= 4 * g + s2) ? pv[s2] : 0.f;
+                }
+            }
+            if (m == i) Adg[i] = av;
+            else Aoff[(i - 1) * i / 2 + m] = av;
+            const s16x4 pb = s16x4{bf16_bits(pv[0]), bf16_bits(pv[1]), bf16_bits(pv[2]), bf16_bits(pv[3])};
+            if (live) *reinterpret_cast<s16x4*>(dstP + (16 * i + n) * C + 16 * m + 4 * g) = pb;
+        }
+#pragma unroll
+        for (int m = i + 1; m < 4; ++m)   // above the diagonal
+            if (live) *reinterpret_cast<s16x4*>(dstP + (16 * i + n) * C + 16 * m + 4 * g) = s16x4{0, 0, 0, 0};
     }
+    __syncthreads();      // the staging area becomes the waves' own regions
+    if (!live) return;    // a partial last group of v-heads
+
+    // A_ii transposed into the diagonal blocks: element (4g + s, n) = A_ii[n][4g + s]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) lds[t_blk(i, i) + blk_elem(4 * g + s2, n)] = Adg[i][s2];
     wave_lds_sync();
 
     // T_ii = (I + A_ii)^-1 for the four diagonal blocks: lane (g, n) solves
-    // column n of block g by forward substitution.
+    // column n of block g, column-oriented: once x_m is final it is removed
+    // from every later row (a dependency chain of 15 steps).  All reads of
+    // A_gg^T come before the writes of T_gg over it.
     {
-        const int dbase = blk_base_idx(g * (g + 3) / 2);
-        const float* Ad = sA + dbase;
+        float* blk = lds + 272 * g;
+        float colm[15][16];
+#pragma unroll
+        for (int m = 0; m < 15; ++m)
+#pragma unroll
+            for (int qd = (m + 1) >> 2; qd < 4; ++qd) {
+                const float4 a4 = *reinterpret_cast<const float4*>(blk + 16 * prow(m) + 4 * (qd ^ (m >> 2)));
+                colm[m][4 * qd] = a4.x; colm[m][4 * qd + 1] = a4.y;
+                colm[m][4 * qd + 2] = a4.z; colm[m][4 * qd + 3] = a4.w;
+            }
         float xc[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float s = 0.f;
+        for (int r = 0; r < 16; ++r) xc[r] = (r == n) ? 1.f : 0.f;
 #pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                if (4 * qd >= r) break;
-                const float4 a4 = *reinterpret_cast<const float4*>(Ad + 16 * (r + (r >> 2)) + 4 * (qd ^ (r >> 2)));
-                const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+        for (int m = 0; m < 15; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * qd + e < r) s = fmaf(a[e], xc[4 * qd + e], s);
-            }
-            xc[r] = (r == n ? 1.f : 0.f) - s;
-        }
-        float* Td = sT + dbase;
+            for (int r = m + 1; r < 16; ++r) xc[r] = fmaf(-colm[m][r], xc[m], xc[r]);
+        wave_lds_sync();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Td[16 * (r + (r >> 2)) + (n ^ (4 * (r >> 2)))] = xc[r];
+        for (int r = 0; r < 16; ++r) blk[blk_elem(r, n)] = xc[r];
     }
     wave_lds_sync();
 
-    // blocks below the diagonal, by distance: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
-    int aoff[4], boff[4];
+    // blocks below the diagonal, by distance: M = sum_m A_im T_mj with A_im
+    // from registers (k-slot 4g + s at step s), one accumulator per m; then
+    // T_ij = -T_ii M with M's registers as the B operand.
+    int boff[4], toff[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        aoff[s] = 16 * (n + (n >> 2)) + ((4 * s + g) ^ (4 * (n >> 2)));   // X[n][4s + g]
-        boff[s] = 16 * (4 * s + g + s) + (n ^ (4 * s));                   // Y[4s + g][n]
+    for (int s2 = 0; s2 < 4; ++s2) {
+        boff[s2] = blk_elem(4 * g + s2, n);   // Y[4g + s][n]
+        toff[s2] = blk_elem(n, 4 * g + s2);   // T_ii[n][4g + s]
     }
 #pragma unroll
     for (int d = 1; d < 4; ++d) {
-        f32x4 M[3];
+        f32x4 R[3];
 #pragma unroll
         for (int j = 0; j + d < 4; ++j) {
             const int i = j + d;
-            f32x4 acc = zero4();
+            f32x4 Mp[3];
 #pragma unroll
-            for (int m = j; m < i; ++m) acc = mm16(sA + blk_base(i, m), sT + blk_base(m, j), acc, aoff, boff);
-            M[j] = acc;
+            for (int m = j; m < i; ++m) {
+                const float* Y = lds + t_blk(m, j);
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) acc = mfma_f32(Aoff[(i - 1) * i / 2 + m][s2], Y[boff[s2]], acc);
+                Mp[m - j] = acc;
+            }
+            f32x4 M = Mp[0];
+#pragma unroll
+            for (int m = 1; m < d; ++m) M = M + Mp[m];
+            const float* Ti = lds + t_blk(i, i);
+            f32x4 t = zero4();
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) t = mfma_f32(Ti[toff[s2]], M[s2], t);
+            R[j] = t;
         }
 #pragma unroll
-        for (int j = 0; j + d < 4; ++j) put16(sT + blk_base(j + d, j), M[j], doff, 1.f);
-        wave_lds_sync();
+        for (int j = 0; j + d < 4; ++j)
 #pragma unroll
-        for (int j = 0; j + d < 4; ++j) {
-            const int i = j + d;
-            M[j] = mm16(sT + blk_base(i, i), sT + blk_base(i, j), zero4(), aoff, boff);
-        }
-        wave_lds_sync();   // every read of M precedes its overwrite
-#pragma unroll
-        for (int j = 0; j + d < 4; ++j) put16(sT + blk_base(j + d, j), M[j], doff, -1.f);
+            for (int s2 = 0; s2 < 4; ++s2) lds[t_blk(j + d, j) + boff[s2]] = -R[j][s2];
         wave_lds_sync();
     }
 
     // T rows -> workspace as bf16 (tiles above the diagonal are zero)
+    const int cg = lane & 7, jb = cg >> 1;
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         const int r = (lane >> 3) + 8 * p, ib = p >> 1, rr = r & 15;
         s16x8 v = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
         if (jb <= ib) {
-            const float* blk = sT + blk_base(ib, jb);
+            const float* blk = lds + (jb == ib ? 272 * ib : 1088 + 256 * ((ib - 1) * ib / 2 + jb));
             const int c0 = 2 * (cg & 1);   // first 4-column granule
-            const float4 a = *reinterpret_cast<const float4*>(blk + 16 * (rr + (rr >> 2)) + 4 * (c0 ^ (rr >> 2)));
-            const float4 e = *reinterpret_cast<const float4*>(blk + 16 * (rr + (rr >> 2)) + 4 * ((c0 + 1) ^ (rr >> 2)));
+            const float* row = blk + 16 * prow(rr);
+            const float4 a = *reinterpret_cast<const float4*>(row + 4 * (c0 ^ (rr >> 2)));
+            const float4 e = *reinterpret_cast<const float4*>(row + 4 * ((c0 + 1) ^ (rr >> 2)));
             v = s16x8{bf16_bits(a.x), bf16_bits(a.y), bf16_bits(a.z), bf16_bits(a.w),
                       bf16_bits(e.x), bf16_bits(e.y), bf16_bits(e.z), bf16_bits(e.w)};
         }
@@ -421,34 +499,7 @@ constexpr int ST_BYTES = 54288;
 constexpr int N_STAGES = 3;
 constexpr int DMA_PER_WAVE = 27;   // 16 K or Q + 8 T or P + 2 V + 1 log_g or beta
 
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Buffer->LDS DMA, written as inline assembly: the compiler would otherwise
-// make later LDS reads wait for every DMA in flight.  Completion is tracked
-// by hand (wait_vmcnt).  The range check that zero-fills rows beyond a chunk
-// covers the lane offset and the SGPR offset alike.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-struct Rsrc { u32x4 d; };
-__device__ __forceinline__ Rsrc make_dma_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    Rsrc r;
-    r.d = u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
-                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu),
-                (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
-    return r;
-}
-__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)p;
-}
-__device__ __forceinline__ void dma16(const Rsrc& r, unsigned char* lds, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"((uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(lds))), "v"(voff), "s"(r.d),
-                    "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const Rsrc& r, unsigned char* lds, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"((uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(lds))), "v"(voff), "s"(r.d) : "memory", "m0");
-}
 // A workgroup barrier without the fences of __syncthreads, whose vmcnt(0)
 // would wait for the DMA of later chunks too.  Producers wait for their own
 // writes (wait_vmcnt, wait_lgkm0) before they arrive.
@@ -462,9 +513,6 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-__device__ __forceinline__ s16x8 lds_read16(const unsigned char* p) {
-    return *reinterpret_cast<const s16x8*>(p);
-}
 __device__ __forceinline__ s16x4 lds_read_tr(const unsigned char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
@@ -858,7 +906,10 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
         hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.B, a.T, base);
     }
     if (n_slots > 0) {
-        hipLaunchKernelGGL(gdn_wy_prep_kernel, dim3((unsigned)n_slots, a.Hv), dim3(64), 0, s,
+        const int G = a.Hv / a.Hk, nw = G < 4 ? G : 4;
+        const size_t shmem = prep_lds_bytes(nw);
+        hipLaunchKernelGGL(gdn_wy_prep_kernel, dim3((unsigned)n_slots, a.Hk, (unsigned)((G + nw - 1) / nw)),
+                           dim3(64 * nw), shmem, s,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, a.log_g, a.beta, slots, a.B,
                            a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense);
     }
