@@ -462,11 +462,22 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// The spine's LDS ring: three stages, each holding one chunk's operands.  Two
-// loader waves fill stage c+2 by buffer->LDS DMA (a 64-lane DMA writes lane
-// l's 16 bytes at base + 16 l, and lanes beyond the buffer's range write
-// zeros, which pads a partial chunk) and prepare the chunk's decay factors,
-// while two compute waves walk chunk c.
+// The state spine.  One workgroup per (sequence, v-head, 32 dv columns), six
+// waves in three roles:
+//   recurrence waves (2, 3): each owns 16 columns of the state h in MFMA
+//     accumulators and walks the chunks in order: X = K h,
+//     R = beta (V - gm X), Delta = T R, h <- gamma_L h + K^T (el Delta).
+//     It hands the chunk's bf16 state (before the update) and Delta to its
+//     output wave through a double-buffered LDS exchange.
+//   output waves (0, 1): one chunk behind, O = gm (Q h) + P Delta for the
+//     same 16 columns.  The output path does not feed back into the state,
+//     so it leaves the recurrence waves' critical path.
+//   loader waves (4, 5): fill the recurrence waves' three-stage LDS ring two
+//     chunks ahead, and the output waves' two-slot ring of Q and P one
+//     chunk ahead, by buffer->LDS DMA (a 64-lane DMA writes lane l's 16 bytes
+//     at base + 16 l; lanes beyond the buffer's range write zeros, which pads
+//     a partial chunk), and prepare the chunk's decay factors.
+// All six waves meet at one barrier per chunk.
 //
 // MFMA k-slots.  Lane group g (lanes 16g .. 16g+15) supplies k-values
 // 8g .. 8g+7 of each 32-wide k-step, so every A fragment is one 16-byte read.
@@ -480,36 +491,53 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 // Stage layout.  Rows are dense; the 16-byte granules of a row are permuted
 // so that every fragment read is free of bank conflicts (64 banks of 4
 // bytes; a 16-byte read serves 8 lanes per pass, an 8-byte read 16):
-//   K, Q (64 rows x 256 B): granule q of row r at q ^ fK(r), fK(r) = 4 (r%4) + (r/8)%2
-//   T, P (64 rows x 128 B): granule q of row r at q ^ fT(r), fT(r) = (r/2)%2 + 2 ((r/8)%2)
-//   V    (64 rows x  64 B: the workgroup's 32 columns)
+//   K (64 rows x 256 B): granule q of row r at q ^ fK(r), fK(r) = 4 (r%4) + (r/8)%2
+//   T (64 rows x 128 B): granule q of row r at q ^ fT(r), fT(r) = (r/2)%2 + 2 ((r/8)%2)
+//   V (64 rows x  64 B: the workgroup's 32 columns)
 //   log_g, beta as loaded (64 fp32 each), then the prepared decay factors
 //   gm_r = exp(G_r) and el_r = exp(G_L - G_r), and gamma_L = exp(G_L).
 constexpr int ST_K = 0;
-constexpr int ST_Q = 16384;
-constexpr int ST_T = 32768;
-constexpr int ST_P = 40960;
-constexpr int ST_V = 49152;
-constexpr int ST_G = 53248;
-constexpr int ST_B = 53504;
-constexpr int ST_GM = 53760;
-constexpr int ST_EL = 54016;
-constexpr int ST_SO = 54272;
-constexpr int ST_BYTES = 54288;
+constexpr int ST_T = 16384;
+constexpr int ST_V = 24576;
+constexpr int ST_G = 28672;
+constexpr int ST_B = 28928;
+constexpr int ST_GM = 29184;
+constexpr int ST_EL = 29440;
+constexpr int ST_SO = 29696;
+constexpr int ST_BYTES = 29712;
 constexpr int N_STAGES = 3;
-constexpr int DMA_PER_WAVE = 27;   // 16 K or Q + 8 T or P + 2 V + 1 log_g or beta
-
+constexpr int DMA_K_WAVE = 17;    // loader 0: 16 K + 1 log_g (then 8 P for the output ring)
+constexpr int DMA_TV_WAVE = 13;   // loader 1: 8 T + 4 V + 1 beta (then 16 Q for the output ring)
+// The exchange: per output/recurrence pair and parity of the chunk, the
+// bf16 state fragments (4 x 1 KB) and the bf16 Delta fragments (2 x 1 KB),
+// each stored lane-major (lane l's 16 bytes at 16 l).  Then 256 bytes of
+// decay factors per output wave.
+// The output ring: per slot Q (64 rows x 256 B, laid out as K) and P (64
+// rows x 128 B, laid out as T).
+constexpr int EX_BASE = 89344;                 // N_STAGES * ST_BYTES rounded up to 1 KB
+constexpr int EX_SLOT = 6144;
+constexpr int OR_BASE = EX_BASE + 4 * EX_SLOT;
+constexpr int OR_Q = 0;
+constexpr int OR_P = 16384;
+constexpr int OR_SLOT = 24576;
+constexpr int OUT_SCR = OR_BASE + 2 * OR_SLOT;
+constexpr int SPINE_LDS = OUT_SCR + 2 * 256;
+static_assert(SPINE_LDS <= 160 * 1024, "the spine's LDS");
+static_assert(EX_BASE >= N_STAGES * ST_BYTES, "exchange after the ring");
 
 // A workgroup barrier without the fences of __syncthreads, whose vmcnt(0)
 // would wait for the DMA of later chunks too.  Producers wait for their own
 // writes (wait_vmcnt, wait_lgkm0) before they arrive.
 __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
-// s_waitcnt with one counter constrained (gfx9 encoding: vmcnt in bits 3:0
-// and 15:14, expcnt 6:4, lgkmcnt 11:8).
+// s_waitcnt vmcnt(n) for the DMA counts used here, other counters free (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+#define GDN_VMCNT(N) (((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
 __device__ __forceinline__ void wait_vmcnt(int n) {
-    if (n == 0) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-    else __builtin_amdgcn_s_waitcnt((DMA_PER_WAVE & 15) | ((DMA_PER_WAVE >> 4) << 14) | (7 << 4) | (15 << 8));
+    if (n == DMA_K_WAVE) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_K_WAVE));
+    else if (n == DMA_TV_WAVE) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_TV_WAVE));
+    else __builtin_amdgcn_s_waitcnt(GDN_VMCNT(0));
 }
+#undef GDN_VMCNT
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
@@ -524,31 +552,31 @@ __device__ __forceinline__ constexpr int sig_tile(int t) { return 32 * (t >> 1) 
 
 // Per-lane DMA byte offsets of a loader wave (chunk-independent).
 struct LoadOffsets {
-    uint32_t kq[2];   // K / Q rows, by (j/2)%2 of the 4-row block j
-    uint32_t tp[2];   // T / P rows, by j%2 of the 8-row block j
+    uint32_t k[2];    // K rows, by (j/2)%2 of the 4-row block j
+    uint32_t t[2];    // T rows, by j%2 of the 8-row block j
     uint32_t v;       // V
     uint32_t gb;      // log_g / beta
 };
 
 __device__ __forceinline__ LoadOffsets load_offsets(int lane, int Hk, int Hv) {
     LoadOffsets o;
-    const uint32_t kq_row = (uint32_t)Hk * D * 2u, v_row = (uint32_t)Hv * D * 2u;
+    const uint32_t k_row = (uint32_t)Hk * D * 2u, v_row = (uint32_t)Hv * D * 2u;
     const int rr = lane >> 4, p = lane & 15, p8 = lane & 7, hb = (lane >> 4) & 1;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        o.kq[s] = rr * kq_row + (uint32_t)((p ^ (4 * rr + s)) * 16);
-        o.tp[s] = (uint32_t)((lane >> 3) * 128 + ((p8 ^ (hb | (s << 1))) * 16));
+        o.k[s] = rr * k_row + (uint32_t)((p ^ (4 * rr + s)) * 16);
+        o.t[s] = (uint32_t)((lane >> 3) * 128 + ((p8 ^ (hb | (s << 1))) * 16));
     }
     o.v = (uint32_t)(lane >> 2) * v_row + (uint32_t)((lane & 3) * 16);
     o.gb = (uint32_t)lane * Hv * 4u;
     return o;
 }
 
-// Loader wave wl's share of chunk c's DMA into `stage`: K (wl = 0) or Q
-// (wl = 1), T or P, half of V, log_g or beta.  Rows beyond the chunk read as
-// zero.  Exactly DMA_PER_WAVE operations.
+// Loader wave wl's share of chunk c's DMA into `stage`: K and log_g
+// (wl = 0, DMA_K_WAVE operations) or T, V and beta (wl = 1, DMA_TV_WAVE).
+// Rows beyond the chunk read as zero.
 __device__ __forceinline__ void spine_load(unsigned char* stage, const LoadOffsets& o,
-                                           const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                           const uint16_t* k, const uint16_t* v,
                                            const float* log_g, const float* beta,
                                            const uint16_t* slot, long row0, long len, int c, int Hk,
                                            int Hv, int kh, int vh, int tile, int wl)
@@ -558,44 +586,66 @@ __device__ __forceinline__ void spine_load(unsigned char* stage, const LoadOffse
     const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)r >> 32));
     const size_t ru = ((size_t)rhi << 32) | rlo;
     const uint32_t L = __builtin_amdgcn_readfirstlane((uint32_t)min((long)C, len - (long)c * C));
-    const uint32_t kq_row = (uint32_t)Hk * D * 2u, v_row = (uint32_t)Hv * D * 2u;
-
-    const Rsrc rkq = make_dma_rsrc((wl == 0 ? k : q) + (ru * Hk + kh) * D, L * kq_row);
-    unsigned char* dkq = stage + (wl == 0 ? ST_K : ST_Q);
+    if (wl == 0) {
+        const uint32_t k_row = (uint32_t)Hk * D * 2u;
+        const Rsrc rk = make_dma_rsrc(k + (ru * Hk + kh) * D, L * k_row);
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-        dma16(rkq, dkq + 1024 * j, o.kq[(j >> 1) & 1], (uint32_t)(4 * j) * kq_row);
-    const Rsrc rtp = make_dma_rsrc(slot + (wl == 0 ? 0 : C * C), C * C * 2u);
-    unsigned char* dtp = stage + (wl == 0 ? ST_T : ST_P);
+        for (int j = 0; j < 16; ++j) dma16(rk, stage + ST_K + 1024 * j, o.k[(j >> 1) & 1], (uint32_t)(4 * j) * k_row);
+        const Rsrc rg = make_dma_rsrc(log_g + ru * Hv + vh, L * Hv * 4u);
+        dma4(rg, stage + ST_G, o.gb);
+    } else {
+        const uint32_t v_row = (uint32_t)Hv * D * 2u;
+        const Rsrc rt = make_dma_rsrc(slot, C * C * 2u);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(rtp, dtp + 1024 * j, o.tp[j & 1], (uint32_t)(1024 * j));
-    const Rsrc rv = make_dma_rsrc(v + (ru * Hv + vh) * D + tile * TILE_COLS, L * v_row);
+        for (int j = 0; j < 8; ++j) dma16(rt, stage + ST_T + 1024 * j, o.t[j & 1], (uint32_t)(1024 * j));
+        const Rsrc rv = make_dma_rsrc(v + (ru * Hv + vh) * D + tile * TILE_COLS, L * v_row);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int jj = 2 * wl + j;
-        dma16(rv, stage + ST_V + 1024 * jj, o.v, (uint32_t)(16 * jj) * v_row);
+        for (int j = 0; j < 4; ++j) dma16(rv, stage + ST_V + 1024 * j, o.v, (uint32_t)(16 * j) * v_row);
+        const Rsrc rb = make_dma_rsrc(beta + ru * Hv + vh, L * Hv * 4u);
+        dma4(rb, stage + ST_B, o.gb);
     }
-    const Rsrc rg = make_dma_rsrc((wl == 0 ? log_g : beta) + ru * Hv + vh, L * Hv * 4u);
-    dma4(rg, stage + (wl == 0 ? ST_G : ST_B), o.gb);
+}
+
+// Loader wave wl's share of chunk c's output-ring DMA into `slot_lds`: P
+// (wl = 0, 8 operations) or Q (wl = 1, 16 operations).
+__device__ __forceinline__ void spine_load_out(unsigned char* slot_lds, const LoadOffsets& o,
+                                               const uint16_t* q, const uint16_t* pslot, long row0,
+                                               long len, int c, int Hk, int kh, int wl)
+{
+    if (wl == 0) {
+        const Rsrc rp = make_dma_rsrc(pslot, C * C * 2u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma16(rp, slot_lds + OR_P + 1024 * j, o.t[j & 1], (uint32_t)(1024 * j));
+    } else {
+        const long r = row0 + (long)c * C;
+        const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)r);
+        const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)r >> 32));
+        const size_t ru = ((size_t)rhi << 32) | rlo;
+        const uint32_t L = __builtin_amdgcn_readfirstlane((uint32_t)min((long)C, len - (long)c * C));
+        const uint32_t q_row = (uint32_t)Hk * D * 2u;
+        const Rsrc rq = make_dma_rsrc(q + (ru * Hk + kh) * D, L * q_row);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dma16(rq, slot_lds + OR_Q + 1024 * j, o.k[(j >> 1) & 1], (uint32_t)(4 * j) * q_row);
+    }
 }
 
 // Decay factors of the chunk in `stage` (its log_g has landed): G = cumsum
 // of log_g within the chunk.  One wave, lane = row.
 __device__ __forceinline__ void spine_scan(unsigned char* stage, int lane) {
     const float gv = reinterpret_cast<const float*>(stage + ST_G)[lane];
-    const float G = wave_inclusive_sum(gv, lane);
+    const float G = wave_scan_dpp(gv);
     const float GL = __shfl(G, 63, 64);
     reinterpret_cast<float*>(stage + ST_GM)[lane] = __expf(G);
     reinterpret_cast<float*>(stage + ST_EL)[lane] = __expf(GL - G);
     if (lane == 0) *reinterpret_cast<float*>(stage + ST_SO) = __expf(GL);
 }
 
-// Per-lane byte offsets of the compute waves' operand reads inside a stage
-// (chunk- and stage-independent).  Each chunk then needs 10 base additions;
-// the tile and k-step parts of every address are immediates.
+// Per-lane byte offsets of a recurrence wave's operand reads inside a stage
+// (chunk- and stage-independent).  Each chunk then needs a few base
+// additions; the tile and k-step parts of every address are immediates.
 struct FragOffsets {
-    uint32_t kq[4];   // K / Q fragments, by k-step
-    uint32_t tp;      // T / P fragments
+    uint32_t k[4];    // K fragments, by k-step
+    uint32_t t;       // T fragments
     uint32_t kt[4];   // K^T (transposing) fragments, by db / 2
     uint32_t v;       // V (transposing)
 };
@@ -606,8 +656,8 @@ __device__ __forceinline__ FragOffsets frag_offsets(int g, int n, int w) {
     const int fKn = 4 * (n & 3) + ((n >> 2) & 1);            // fK(sig(t, n)), any t
     const int fTn = ((n >> 1) & 1) | (((n >> 2) & 1) << 1);  // fT(sig(t, n)), any t
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) o.kq[kk] = (uint32_t)(sig0 * 256 + 16 * ((4 * kk + g) ^ fKn));
-    o.tp = (uint32_t)(sig0 * 128 + 16 * (g ^ fTn));
+    for (int kk = 0; kk < 4; ++kk) o.k[kk] = (uint32_t)(sig0 * 256 + 16 * ((4 * kk + g) ^ fKn));
+    o.t = (uint32_t)(sig0 * 128 + 16 * (g ^ fTn));
     // transposing reads: this lane sources row 8g + kr (+ 32 kk + 4 half) and
     // the 4 columns of quarter qq of the 8-column group
     const int kr = n >> 2, qq = n & 3;
@@ -618,14 +668,11 @@ __device__ __forceinline__ FragOffsets frag_offsets(int g, int n, int w) {
     return o;
 }
 
-// One compute wave, one chunk, 16 columns (wave w of the workgroup) from
-// stage S.  The chunk's outputs go through `ro`, a buffer resource that
-// covers exactly its rows: `lane_off` is the lane's byte offset (row 8g,
-// column col) and soff[4 cb + r] the uniform offset of row sig_tile(cb) + r.
-template <bool kOutF32>
-__device__ __forceinline__ void spine_step(const unsigned char* S, f32x4 (&h)[8], rsrc_t ro,
-                                           uint32_t lane_off, const uint32_t (&soff)[16], int g,
-                                           const FragOffsets& fo)
+// One recurrence wave, one chunk, 16 columns (column half w of the
+// workgroup) from stage S; hands its bf16 state and Delta fragments to the
+// output wave through exchange slot E.
+__device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char* E, f32x4 (&h)[8],
+                                           int g, int lane, const FragOffsets& fo)
 {
     const float* gmv = reinterpret_cast<const float*>(S + ST_GM);
     const float* elv = reinterpret_cast<const float*>(S + ST_EL);
@@ -633,51 +680,50 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, f32x4 (&h)[8]
     const unsigned char* pk[4];
     const unsigned char* pz[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { pk[i] = S + fo.kq[i]; pz[i] = S + fo.kt[i]; }
-    const unsigned char* pt = S + fo.tp;
+    for (int i = 0; i < 4; ++i) { pk[i] = S + fo.k[i]; pz[i] = S + fo.kt[i]; }
+    const unsigned char* pt = S + fo.t;
     const unsigned char* pv = S + fo.v;
-#define KQF(sec, cb, kk) lds_read16(pk[kk] + (sec) + 256 * sig_tile(cb))
-#define TPF(sec, cb, kk) lds_read16(pt + (sec) + 128 * sig_tile(cb) + 64 * (kk))
+#define KF(cb, kk) lds_read16(pk[kk] + ST_K + 256 * sig_tile(cb))
+#define TF(cb, kk) lds_read16(pt + ST_T + 128 * sig_tile(cb) + 64 * (kk))
 #define KTF(db, kk) join(lds_read_tr(pz[(db) >> 1] + ST_K + 8192 * (kk) + 8 * ((db) & 1)), \
                          lds_read_tr(pz[(db) >> 1] + ST_K + 8192 * (kk) + 1024 + 8 * ((db) & 1)))
 
     s16x8 hb[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) hb[kk] = frag_b(h[2 * kk], h[2 * kk + 1]);
-
-    // X = K h, Y = Q h: per k-step, 4 K fragments then 4 Q fragments, each
-    // group loaded one group ahead
-    f32x4 X[4], Y[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) X[cb] = Y[cb] = zero4();
-    s16x8 fcur[4], fnext[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) fcur[cb] = KQF(ST_K, cb, 0);
-#pragma unroll
-    for (int gi = 0; gi < 8; ++gi) {   // group gi: k-step gi/2, K (even) or Q (odd)
-        const int kk = gi >> 1;
-        if (gi + 1 < 8) {
-            const int kn = (gi + 1) >> 1;
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) fnext[cb] = ((gi + 1) & 1) ? KQF(ST_Q, cb, kn) : KQF(ST_K, cb, kn);
-        }
-        sched_fence();
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            if (gi & 1) Y[cb] = mfma_bf16(fcur[cb], hb[kk], Y[cb]);
-            else X[cb] = mfma_bf16(fcur[cb], hb[kk], X[cb]);
-        }
-        sched_fence();
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) fcur[cb] = fnext[cb];
+    for (int kk = 0; kk < 4; ++kk) {
+        hb[kk] = frag_b(h[2 * kk], h[2 * kk + 1]);
+        *reinterpret_cast<s16x8*>(E + 1024 * kk + 16 * lane) = hb[kk];
     }
 
-    // T fragments, then R = beta (V - gm X) and Y <- gm Y for this lane's rows
+    // X = K h: per k-step 4 K fragments, loaded one k-step ahead
+    f32x4 X[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) X[cb] = zero4();
+    s16x8 fcur[4], fnext[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) fcur[cb] = KF(cb, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        if (kk + 1 < 4) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) fnext[cb] = KF(cb, kk + 1);
+        }
+        sched_fence();
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) X[cb] = mfma_bf16(fcur[cb], hb[kk], X[cb]);
+        sched_fence();
+        if (kk + 1 < 4) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) fcur[cb] = fnext[cb];
+        }
+    }
+
+    // T fragments, then R = beta (V - gm X) for this lane's rows
     s16x8 ft[6];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) ft[cb] = TPF(ST_T, cb, 0);
-    ft[4] = TPF(ST_T, 2, 1);
-    ft[5] = TPF(ST_T, 3, 1);
+    for (int cb = 0; cb < 4; ++cb) ft[cb] = TF(cb, 0);
+    ft[4] = TF(2, 1);
+    ft[5] = TF(3, 1);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         const int row = sig_tile(cb) + 8 * g;
@@ -687,10 +733,8 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, f32x4 (&h)[8]
         const float gmr[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
         const float btr[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 4; ++r)
             X[cb][r] = btr[r] * (bf16_bits_to_f32((uint16_t)vv[r]) - gmr[r] * X[cb][r]);
-            Y[cb][r] *= gmr[r];
-        }
     }
     const s16x8 rb0 = frag_b(X[0], X[1]), rb1 = frag_b(X[2], X[3]);
 
@@ -707,7 +751,8 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, f32x4 (&h)[8]
     Dl[2] = mfma_bf16(ft[4], rb1, Dl[2]);
     Dl[3] = mfma_bf16(ft[5], rb1, Dl[3]);
     sched_fence();
-    const s16x8 db0 = frag_b(Dl[0], Dl[1]), db1 = frag_b(Dl[2], Dl[3]);
+    *reinterpret_cast<s16x8*>(E + 4096 + 16 * lane) = frag_b(Dl[0], Dl[1]);
+    *reinterpret_cast<s16x8*>(E + 5120 + 16 * lane) = frag_b(Dl[2], Dl[3]);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         const float4 el4 = *reinterpret_cast<const float4*>(elv + sig_tile(cb) + 8 * g);
@@ -736,23 +781,58 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, f32x4 (&h)[8]
             for (int i = 0; i < 4; ++i) fk1[i] = fk2[i];
         }
     }
-
-    // O = gm Y + P Delta
-    s16x8 fp[6];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) fp[cb] = TPF(ST_P, cb, 0);
-    fp[4] = TPF(ST_P, 2, 1);
-    fp[5] = TPF(ST_P, 3, 1);
-#undef KQF
-#undef TPF
+#undef KF
+#undef TF
 #undef KTF
+    wait_lgkm0();   // the exchange writes are complete before the barrier
+}
+
+// One output wave, one chunk: O = gm (Q h) + P Delta for its 16 columns,
+// with Q and P from output-ring slot Sq, the bf16 state and Delta from the
+// exchange slot E the recurrence wave filled, and lg this lane's log_g
+// (lane = row).  `ro` covers exactly the chunk's output rows; `lane_off` is
+// the lane's byte offset (row 8g, column col) and soff[4 cb + r] the uniform
+// offset of row sig_tile(cb) + r.
+template <bool kOutF32>
+__device__ __forceinline__ void out_step(const unsigned char* Sq, const unsigned char* E, float* scr,
+                                         float lg, const FragOffsets& fo, rsrc_t ro,
+                                         uint32_t lane_off, const uint32_t (&soff)[16], int g,
+                                         int lane)
+{
+    scr[lane] = __expf(wave_scan_dpp(lg));   // gm_r = exp(G_r)
+    s16x8 hb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) hb[kk] = lds_read16(E + 1024 * kk + 16 * lane);
+    const s16x8 db0 = lds_read16(E + 4096 + 16 * lane), db1 = lds_read16(E + 5120 + 16 * lane);
+    f32x4 Y[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) Y[cb] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        s16x8 qf[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) qf[cb] = lds_read16(Sq + fo.k[kk] + OR_Q + 256 * sig_tile(cb));
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) Y[cb] = mfma_bf16(qf[cb], hb[kk], Y[cb]);
+    }
+    s16x8 pf[6];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) pf[cb] = lds_read16(Sq + fo.t + OR_P + 128 * sig_tile(cb));
+    pf[4] = lds_read16(Sq + fo.t + OR_P + 128 * sig_tile(2) + 64);
+    pf[5] = lds_read16(Sq + fo.t + OR_P + 128 * sig_tile(3) + 64);
+    wave_lds_sync();
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const float4 gm4 = *reinterpret_cast<const float4*>(scr + sig_tile(cb) + 8 * g);
+        Y[cb][0] *= gm4.x; Y[cb][1] *= gm4.y; Y[cb][2] *= gm4.z; Y[cb][3] *= gm4.w;
+    }
     f32x4 O[4];
-    O[0] = mfma_bf16(fp[0], db0, Y[0]);
-    O[1] = mfma_bf16(fp[1], db0, Y[1]);
-    O[2] = mfma_bf16(fp[2], db0, Y[2]);
-    O[3] = mfma_bf16(fp[3], db0, Y[3]);
-    O[2] = mfma_bf16(fp[4], db1, O[2]);
-    O[3] = mfma_bf16(fp[5], db1, O[3]);
+    O[0] = mfma_bf16(pf[0], db0, Y[0]);
+    O[1] = mfma_bf16(pf[1], db0, Y[1]);
+    O[2] = mfma_bf16(pf[2], db0, Y[2]);
+    O[3] = mfma_bf16(pf[3], db0, Y[3]);
+    O[2] = mfma_bf16(pf[4], db1, O[2]);
+    O[3] = mfma_bf16(pf[5], db1, O[3]);
     // hardware RNE conversion; rows beyond a partial chunk fall outside `ro`
     // and are dropped
 #pragma unroll
@@ -763,12 +843,11 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, f32x4 (&h)[8]
             if (kOutF32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, lane_off, soff[4 * cb + r], 0);
             else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_bits(val), ro, lane_off, soff[4 * cb + r], 0);
         }
+    wave_lds_sync();   // the decay scratch is rewritten by the next chunk
 }
 
-// One workgroup per (sequence, v-head, 32 dv columns): waves 0 and 1 own 16
-// columns each of the state in MFMA accumulators; waves 2 and 3 load.
 template <bool kOutF32>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(384)
 gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const float* __restrict__ log_g,
                  const float* __restrict__ beta, const float* h0, void* __restrict__ out,
@@ -776,7 +855,8 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_base,
                  int nc_dense, long n_slots)
 {
-    __shared__ __attribute__((aligned(1024))) unsigned char ring[N_STAGES * ST_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[SPINE_LDS];
+    unsigned char* ring = lds;
 
     const int tid = threadIdx.x;
     // the wave index is wave-uniform; say so, so per-wave values live in SGPRs
@@ -798,51 +878,77 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // Only a decreasing cu_seqlens (a broken precondition) can make this
     // bind; it keeps every read inside the workspace.
     if (slot0 + nc > n_slots) nc = (int)max(0L, n_slots - slot0);
+    const uint16_t* slot_base = slots + ((size_t)slot0 * Hv + vh) * SLOT_ELEMS;
+    const size_t slot_stride = (size_t)Hv * SLOT_ELEMS;
 
-    if (w >= 2) {   // loader waves
-        const int wl = w - 2;
-        const uint16_t* slot_base = slots + ((size_t)slot0 * Hv + vh) * SLOT_ELEMS;
-        const size_t slot_stride = (size_t)Hv * SLOT_ELEMS;
+    if (w >= 4) {   // loader waves
+        const int wl = w - 4;
+        const int cnt = wl == 0 ? DMA_K_WAVE : DMA_TV_WAVE;
         const LoadOffsets o = load_offsets(lane, Hk, Hv);
         for (int c = 0; c < 2 && c < nc; ++c)
-            spine_load(ring + c * ST_BYTES, o, q, k, v, log_g, beta, slot_base + (size_t)c * slot_stride,
+            spine_load(ring + c * ST_BYTES, o, k, v, log_g, beta, slot_base + (size_t)c * slot_stride,
                        row0, len, c, Hk, Hv, kh, vh, tile, wl);
         if (nc > 0) {
-            wait_vmcnt(nc > 1 ? DMA_PER_WAVE : 0);
+            wait_vmcnt(nc > 1 ? cnt : 0);
             if (wl == 0) spine_scan(ring, lane);
             wait_lgkm0();
         }
-        for (int c = 0; c < nc; ++c) {
-            ring_barrier();   // chunk c is ready; stage (c+2)%3 is free
+        for (int c = 0; c <= nc; ++c) {
+            // chunk c is ready in the recurrence ring; stage (c+2)%3 and
+            // output slot c%2 are free
+            ring_barrier();
+            if (c < nc)
+                spine_load_out(lds + OR_BASE + (c & 1) * OR_SLOT, o, q,
+                               slot_base + (size_t)c * slot_stride + C * C, row0, len, c, Hk, kh, wl);
             if (c + 2 < nc)
-                spine_load(ring + ((c + 2) % N_STAGES) * ST_BYTES, o, q, k, v, log_g, beta,
+                spine_load(ring + ((c + 2) % N_STAGES) * ST_BYTES, o, k, v, log_g, beta,
                            slot_base + (size_t)(c + 2) * slot_stride, row0, len, c + 2, Hk, Hv, kh,
                            vh, tile, wl);
-            if (c + 1 < nc) {
-                wait_vmcnt(c + 2 < nc ? DMA_PER_WAVE : 0);   // chunk c+1 has landed
-                if (wl == 0) spine_scan(ring + ((c + 1) % N_STAGES) * ST_BYTES, lane);
+            if (c < nc) {
+                // chunk c's output operands and chunk c+1 have landed
+                wait_vmcnt(c + 2 < nc ? cnt : 0);
+                if (c + 1 < nc && wl == 0) spine_scan(ring + ((c + 1) % N_STAGES) * ST_BYTES, lane);
                 wait_lgkm0();
             }
         }
         return;
     }
 
-    const int col = tile * TILE_COLS + 16 * w + n;
-    f32x4 h[8];
-    const size_t hoff = ((size_t)b * Hv + vh) * D * D;
-    // state row of h[db][r] in this lane: sig(db, 4g + r)
-    if (h0) {   // one uniform branch: all 32 loads in flight together
+    const int half = w & 1;   // which 16 of the workgroup's 32 columns
+    const int col = tile * TILE_COLS + 16 * half + n;
+    unsigned char* ex = lds + EX_BASE + half * 2 * EX_SLOT;
+
+    if (w >= 2) {   // recurrence waves
+        f32x4 h[8];
+        const size_t hoff = ((size_t)b * Hv + vh) * D * D;
+        // state row of h[db][r] in this lane: sig(db, 4g + r)
+        if (h0) {   // one uniform branch: all 32 loads in flight together
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
+            for (int db = 0; db < 8; ++db)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                h[db][r] = h0[hoff + (size_t)(sig_tile(db) + 8 * g + r) * D + col];
-    } else {
+                for (int r = 0; r < 4; ++r)
+                    h[db][r] = h0[hoff + (size_t)(sig_tile(db) + 8 * g + r) * D + col];
+        } else {
 #pragma unroll
-        for (int db = 0; db < 8; ++db) h[db] = zero4();
+            for (int db = 0; db < 8; ++db) h[db] = zero4();
+        }
+        const FragOffsets fo = frag_offsets(g, n, half);
+        for (int c = 0; c <= nc; ++c) {
+            ring_barrier();
+            if (c < nc) spine_step(ring + (c % N_STAGES) * ST_BYTES, ex + (c & 1) * EX_SLOT, h, g, lane, fo);
+        }
+        if (h_final) {
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    h_final[hoff + (size_t)(sig_tile(db) + 8 * g + r) * D + col] = h[db][r];
+        }
+        return;
     }
-    const FragOffsets fo = frag_offsets(g, n, w);
-    // output rows: a per-chunk resource over the chunk's rows, advanced by C rows
+
+    // output waves: chunk c - 1 at step c
+    float* scr = reinterpret_cast<float*>(lds + OUT_SCR + 256 * half);
     constexpr uint32_t es = kOutF32 ? 4u : 2u;
     const uint32_t rs = __builtin_amdgcn_readfirstlane((uint32_t)Hv * D * es);
     const uint32_t lane_off = (uint32_t)(8 * g) * rs + (uint32_t)col * es;
@@ -852,21 +958,28 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)row0);
     const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)row0 >> 32));
     char* obase = reinterpret_cast<char*>(out) + ((((size_t)rhi << 32) | rlo) * Hv + vh) * D * es;
-    long rem = len;
-    for (int c = 0; c < nc; ++c) {
+    const FragOffsets fo = frag_offsets(g, n, half);
+    float lg = 0.f;
+    auto load_lg = [&](int c) {   // this chunk's log_g, lane = row
+        const long r = row0 + (long)c * C;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)r);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)r >> 32));
+        const size_t ru = ((size_t)hi << 32) | lo;
+        const uint32_t L = __builtin_amdgcn_readfirstlane((uint32_t)min((long)C, len - (long)c * C));
+        const rsrc_t rg = make_rsrc(log_g + ru * Hv + vh, L * Hv * 4u);
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)lane * Hv * 4u, 0, 0));
+    };
+    if (nc > 0) lg = load_lg(0);
+    for (int c = 0; c <= nc; ++c) {
         ring_barrier();
-        const rsrc_t ro = make_rsrc(obase, (uint32_t)min((long)C, rem) * rs);
-        spine_step<kOutF32>(ring + (c % N_STAGES) * ST_BYTES, h, ro, lane_off, soff, g, fo);
-        obase += (size_t)C * rs;
-        rem -= C;
-    }
-
-    if (h_final) {
-#pragma unroll
-        for (int db = 0; db < 8; ++db)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                h_final[hoff + (size_t)(sig_tile(db) + 8 * g + r) * D + col] = h[db][r];
+        if (c >= 1) {   // chunk c - 1
+            const long rem = len - (long)(c - 1) * C;
+            const rsrc_t ro = make_rsrc(obase + (size_t)(c - 1) * C * rs, (uint32_t)min((long)C, rem) * rs);
+            const float lg_c = lg;
+            if (c < nc) lg = load_lg(c);
+            out_step<kOutF32>(lds + OR_BASE + ((c - 1) & 1) * OR_SLOT, ex + ((c - 1) & 1) * EX_SLOT,
+                              scr, lg_c, fo, ro, lane_off, soff, g, lane);
+        }
     }
 }
 
@@ -890,8 +1003,8 @@ bool prefill_mfma_accepts(const PrefillArgs& a)
 
 Geometry prefill_mfma_geometry(const PrefillArgs& a)
 {
-    Geometry g{"gdn_wy_prep_kernel+gdn_spine_kernel", {(unsigned)(a.Hv * N_TILES), (unsigned)a.B, 1u}, 256u,
-               (unsigned)(N_STAGES * ST_BYTES)};
+    Geometry g{"gdn_wy_prep_kernel+gdn_spine_kernel", {(unsigned)(a.Hv * N_TILES), (unsigned)a.B, 1u}, 384u,
+               (unsigned)SPINE_LDS};
     return g;
 }
 
@@ -915,11 +1028,11 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
     }
     dim3 grid(a.Hv * N_TILES, a.B);
     if (a.out_dtype == 0)
-        hipLaunchKernelGGL((gdn_spine_kernel<true>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
+        hipLaunchKernelGGL((gdn_spine_kernel<true>), grid, dim3(384), 0, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, a.log_g, a.beta, a.h0, a.out,
                            a.h_final, slots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense, n_slots);
     else
-        hipLaunchKernelGGL((gdn_spine_kernel<false>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
+        hipLaunchKernelGGL((gdn_spine_kernel<false>), grid, dim3(384), 0, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, a.log_g, a.beta, a.h0, a.out,
                            a.h_final, slots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense, n_slots);
     return hipGetLastError();

@@ -60,7 +60,7 @@ def prefill_plan(lib, **kw):
 def test_prefill_routes(lib):
     assert prefill_plan(lib) == 0
     r = gdn.last_route()
-    assert r.startswith("gdn_wy_prep_kernel+gdn_spine_kernel grid=[192,1,1] block=256"), r
+    assert r.startswith("gdn_wy_prep_kernel+gdn_spine_kernel grid=[192,1,1] block=384"), r
     assert "lds=" in r
     # fp32 I/O goes to the generic kernel and the line says why
     assert prefill_plan(lib, io=0, od=0, dk=32, dv=32, chunk=32, Hk=1, Hv=1) == 0
