@@ -134,6 +134,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ s16x8 buffer_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
     const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
     return __builtin_bit_cast(s16x8, v);
@@ -688,6 +689,29 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char
 #define KTF(db, kk) join(lds_read_tr(pz[(db) >> 1] + ST_K + 8192 * (kk) + 8 * ((db) & 1)), \
                          lds_read_tr(pz[(db) >> 1] + ST_K + 8192 * (kk) + 1024 + 8 * ((db) & 1)))
 
+    // every read of the chunk's scalars, V and T comes before the exchange
+    // writes (which the compiler cannot prove disjoint from them), so all are
+    // in flight while X is formed
+    float4 gm4[4], bt4[4];
+    s16x4 vv[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const int row = sig_tile(cb) + 8 * g;
+        gm4[cb] = *reinterpret_cast<const float4*>(gmv + row);
+        bt4[cb] = *reinterpret_cast<const float4*>(btv + row);
+        vv[cb] = lds_read_tr(pv + ST_V + 64 * sig_tile(cb));
+    }
+    s16x8 ft[6];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) ft[cb] = TF(cb, 0);
+    ft[4] = TF(2, 1);
+    ft[5] = TF(3, 1);
+    const float gamL = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+        __builtin_bit_cast(int, *reinterpret_cast<const float*>(S + ST_SO))));
+    s16x8 fcur[4], fnext[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) fcur[cb] = KF(cb, 0);
+
     s16x8 hb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -699,9 +723,6 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char
     f32x4 X[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) X[cb] = zero4();
-    s16x8 fcur[4], fnext[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) fcur[cb] = KF(cb, 0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         if (kk + 1 < 4) {
@@ -718,23 +739,14 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char
         }
     }
 
-    // T fragments, then R = beta (V - gm X) for this lane's rows
-    s16x8 ft[6];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) ft[cb] = TF(cb, 0);
-    ft[4] = TF(2, 1);
-    ft[5] = TF(3, 1);
+    // R = beta (V - gm X) for this lane's rows
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-        const int row = sig_tile(cb) + 8 * g;
-        const float4 gm4 = *reinterpret_cast<const float4*>(gmv + row);
-        const float4 bt4 = *reinterpret_cast<const float4*>(btv + row);
-        const s16x4 vv = lds_read_tr(pv + ST_V + 64 * sig_tile(cb));
-        const float gmr[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
-        const float btr[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+        const float gmr[4] = {gm4[cb].x, gm4[cb].y, gm4[cb].z, gm4[cb].w};
+        const float btr[4] = {bt4[cb].x, bt4[cb].y, bt4[cb].z, bt4[cb].w};
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            X[cb][r] = btr[r] * (bf16_bits_to_f32((uint16_t)vv[r]) - gmr[r] * X[cb][r]);
+            X[cb][r] = btr[r] * (bf16_bits_to_f32((uint16_t)vv[cb][r]) - gmr[r] * X[cb][r]);
     }
     const s16x8 rb0 = frag_b(X[0], X[1]), rb1 = frag_b(X[2], X[3]);
 
@@ -761,8 +773,6 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char
     const s16x8 ds0 = frag_b(Dl[0], Dl[1]), ds1 = frag_b(Dl[2], Dl[3]);
 
     // h <- gamma_L h + K^T (el Delta): 8 row blocks, two blocks ahead
-    const float gamL = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-        __builtin_bit_cast(int, *reinterpret_cast<const float*>(S + ST_SO))));
 #pragma unroll
     for (int db = 0; db < 8; ++db) h[db] = h[db] * gamL;
 #pragma unroll
@@ -790,13 +800,18 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char
 // One output wave, one chunk: O = gm (Q h) + P Delta for its 16 columns,
 // with Q and P from output-ring slot Sq, the bf16 state and Delta from the
 // exchange slot E the recurrence wave filled, and lg this lane's log_g
-// (lane = row).  `ro` covers exactly the chunk's output rows; `lane_off` is
-// the lane's byte offset (row 8g, column col) and soff[4 cb + r] the uniform
-// offset of row sig_tile(cb) + r.
+// (lane = row).  The products are formed transposed, O^T = gm (h^T Q^T) +
+// Delta^T P^T: a B-operand fragment of h or Delta is the A operand of its
+// transpose and an A-operand fragment of Q or P the B operand of its
+// transpose, so the same fragments serve, and lane (g, n) register r of tile
+// cb ends up holding O[sig(cb, n)][4g + r]: four consecutive columns of one
+// row, stored at once.  `ro` covers exactly the chunk's output rows;
+// `lane_off` is the lane's byte offset for row sig(0, n) and column 4g, and
+// soff[cb] the uniform offset of tile cb's rows.
 template <bool kOutF32>
 __device__ __forceinline__ void out_step(const unsigned char* Sq, const unsigned char* E, float* scr,
                                          float lg, const FragOffsets& fo, rsrc_t ro,
-                                         uint32_t lane_off, const uint32_t (&soff)[16], int g,
+                                         uint32_t lane_off, const uint32_t (&soff)[4], int n,
                                          int lane)
 {
     scr[lane] = __expf(wave_scan_dpp(lg));   // gm_r = exp(G_r)
@@ -813,7 +828,7 @@ __device__ __forceinline__ void out_step(const unsigned char* Sq, const unsigned
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) qf[cb] = lds_read16(Sq + fo.k[kk] + OR_Q + 256 * sig_tile(cb));
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) Y[cb] = mfma_bf16(qf[cb], hb[kk], Y[cb]);
+        for (int cb = 0; cb < 4; ++cb) Y[cb] = mfma_bf16(hb[kk], qf[cb], Y[cb]);
     }
     s16x8 pf[6];
 #pragma unroll
@@ -821,28 +836,31 @@ __device__ __forceinline__ void out_step(const unsigned char* Sq, const unsigned
     pf[4] = lds_read16(Sq + fo.t + OR_P + 128 * sig_tile(2) + 64);
     pf[5] = lds_read16(Sq + fo.t + OR_P + 128 * sig_tile(3) + 64);
     wave_lds_sync();
+    const int sig0 = 8 * (n >> 2) + (n & 3);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        const float4 gm4 = *reinterpret_cast<const float4*>(scr + sig_tile(cb) + 8 * g);
-        Y[cb][0] *= gm4.x; Y[cb][1] *= gm4.y; Y[cb][2] *= gm4.z; Y[cb][3] *= gm4.w;
-    }
+    for (int cb = 0; cb < 4; ++cb) Y[cb] = Y[cb] * scr[sig_tile(cb) + sig0];   // row factor of this lane's row
     f32x4 O[4];
-    O[0] = mfma_bf16(pf[0], db0, Y[0]);
-    O[1] = mfma_bf16(pf[1], db0, Y[1]);
-    O[2] = mfma_bf16(pf[2], db0, Y[2]);
-    O[3] = mfma_bf16(pf[3], db0, Y[3]);
-    O[2] = mfma_bf16(pf[4], db1, O[2]);
-    O[3] = mfma_bf16(pf[5], db1, O[3]);
+    O[0] = mfma_bf16(db0, pf[0], Y[0]);
+    O[1] = mfma_bf16(db0, pf[1], Y[1]);
+    O[2] = mfma_bf16(db0, pf[2], Y[2]);
+    O[3] = mfma_bf16(db0, pf[3], Y[3]);
+    O[2] = mfma_bf16(db1, pf[4], O[2]);
+    O[3] = mfma_bf16(db1, pf[5], O[3]);
     // hardware RNE conversion; rows beyond a partial chunk fall outside `ro`
     // and are dropped
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float val = O[cb][r];   // by value: never bit-cast a vector element in place
-            if (kOutF32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, lane_off, soff[4 * cb + r], 0);
-            else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_bits(val), ro, lane_off, soff[4 * cb + r], 0);
+    for (int cb = 0; cb < 4; ++cb) {
+        const f32x4 o = O[cb];
+        if (kOutF32) {
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(o[0]), __float_as_uint(o[1]),
+                                                          __float_as_uint(o[2]), __float_as_uint(o[3])},
+                                                   ro, lane_off, soff[cb], 0);
+        } else {
+            const uint32_t lo = (uint16_t)bf16_bits(o[0]) | ((uint32_t)(uint16_t)bf16_bits(o[1]) << 16);
+            const uint32_t hi = (uint16_t)bf16_bits(o[2]) | ((uint32_t)(uint16_t)bf16_bits(o[3]) << 16);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2v{lo, hi}, ro, lane_off, soff[cb], 0);
         }
+    }
     wave_lds_sync();   // the decay scratch is rewritten by the next chunk
 }
 
@@ -951,10 +969,11 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     float* scr = reinterpret_cast<float*>(lds + OUT_SCR + 256 * half);
     constexpr uint32_t es = kOutF32 ? 4u : 2u;
     const uint32_t rs = __builtin_amdgcn_readfirstlane((uint32_t)Hv * D * es);
-    const uint32_t lane_off = (uint32_t)(8 * g) * rs + (uint32_t)col * es;
-    uint32_t soff[16];
+    const uint32_t lane_off = (uint32_t)(8 * (n >> 2) + (n & 3)) * rs +
+                              (uint32_t)(tile * TILE_COLS + 16 * half + 4 * g) * es;
+    uint32_t soff[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) soff[i] = (uint32_t)(sig_tile(i >> 2) + (i & 3)) * rs;
+    for (int cb = 0; cb < 4; ++cb) soff[cb] = (uint32_t)sig_tile(cb) * rs;
     const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)row0);
     const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)row0 >> 32));
     char* obase = reinterpret_cast<char*>(out) + ((((size_t)rhi << 32) | rlo) * Hv + vh) * D * es;
@@ -978,7 +997,7 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             const float lg_c = lg;
             if (c < nc) lg = load_lg(c);
             out_step<kOutF32>(lds + OR_BASE + ((c - 1) & 1) * OR_SLOT, ex + ((c - 1) & 1) * EX_SLOT,
-                              scr, lg_c, fo, ro, lane_off, soff, g, lane);
+                              scr, lg_c, fo, ro, lane_off, soff, n, lane);
         }
     }
 }
