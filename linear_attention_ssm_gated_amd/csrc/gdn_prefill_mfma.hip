@@ -526,6 +526,39 @@ constexpr int SPINE_LDS = OUT_SCR + 2 * 256;
 static_assert(SPINE_LDS <= 160 * 1024, "the spine's LDS");
 static_assert(EX_BASE >= N_STAGES * ST_BYTES, "exchange after the ring");
 
+// Batches of buffer->LDS DMAs into consecutive 1 KB pieces of LDS starting
+// at the LDS byte address `lds`: M0 is set once and advanced by one scalar
+// add per piece, and every lane and SGPR offset is precomputed.
+__device__ __forceinline__ void dma_x4(const Rsrc& r, uint32_t lds, uint32_t v0, uint32_t v1,
+                                       uint32_t v2, uint32_t v3, uint32_t s0, uint32_t s1,
+                                       uint32_t s2, uint32_t s3) {
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "buffer_load_dwordx4 %2, %1, %6 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %3, %1, %7 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %4, %1, %8 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %5, %1, %9 offen lds"
+                 :: "s"(lds), "s"(r.d), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(s0), "s"(s1), "s"(s2), "s"(s3)
+                 : "memory", "m0", "scc");
+}
+__device__ __forceinline__ void dma_x8(const Rsrc& r, uint32_t lds, const uint32_t (&v)[8], const uint32_t (&so)[8]) {
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "buffer_load_dwordx4 %2, %1, %10 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %3, %1, %11 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %4, %1, %12 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %5, %1, %13 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %6, %1, %14 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %7, %1, %15 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %8, %1, %16 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %9, %1, %17 offen lds"
+                 :: "s"(lds), "s"(r.d), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]),
+                    "v"(v[6]), "v"(v[7]), "s"(so[0]), "s"(so[1]), "s"(so[2]), "s"(so[3]), "s"(so[4]),
+                    "s"(so[5]), "s"(so[6]), "s"(so[7])
+                 : "memory", "m0", "scc");
+}
+__device__ __forceinline__ uint32_t lds_u32(const unsigned char* p) {
+    return __builtin_amdgcn_readfirstlane(lds_addr(p));
+}
+
 // A workgroup barrier without the fences of __syncthreads, whose vmcnt(0)
 // would wait for the DMA of later chunks too.  Producers wait for their own
 // writes (wait_vmcnt, wait_lgkm0) before they arrive.
@@ -557,6 +590,10 @@ struct LoadOffsets {
     uint32_t t[2];    // T rows, by j%2 of the 8-row block j
     uint32_t v;       // V
     uint32_t gb;      // log_g / beta
+    // per 1 KB piece j: lane offsets and (uniform) SGPR offsets
+    uint32_t kv[8], ks[16];   // K and Q pieces 0..15 (lane offsets repeat every 8)
+    uint32_t tv[8], ts[8];    // T and P pieces 0..7
+    uint32_t vs[4];           // V pieces 0..3
 };
 
 __device__ __forceinline__ LoadOffsets load_offsets(int lane, int Hk, int Hv) {
@@ -570,6 +607,16 @@ __device__ __forceinline__ LoadOffsets load_offsets(int lane, int Hk, int Hv) {
     }
     o.v = (uint32_t)(lane >> 2) * v_row + (uint32_t)((lane & 3) * 16);
     o.gb = (uint32_t)lane * Hv * 4u;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o.ks[j] = __builtin_amdgcn_readfirstlane((uint32_t)(4 * j) * k_row);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        o.kv[j] = o.k[(j >> 1) & 1];
+        o.tv[j] = o.t[j & 1];
+        o.ts[j] = 1024u * j;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.vs[j] = __builtin_amdgcn_readfirstlane((uint32_t)(16 * j) * v_row);
     return o;
 }
 
@@ -587,21 +634,20 @@ __device__ __forceinline__ void spine_load(unsigned char* stage, const LoadOffse
     const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)r >> 32));
     const size_t ru = ((size_t)rhi << 32) | rlo;
     const uint32_t L = __builtin_amdgcn_readfirstlane((uint32_t)min((long)C, len - (long)c * C));
+    const uint32_t base = lds_u32(stage);
     if (wl == 0) {
         const uint32_t k_row = (uint32_t)Hk * D * 2u;
         const Rsrc rk = make_dma_rsrc(k + (ru * Hk + kh) * D, L * k_row);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) dma16(rk, stage + ST_K + 1024 * j, o.k[(j >> 1) & 1], (uint32_t)(4 * j) * k_row);
+        dma_x8(rk, base + ST_K, o.kv, *reinterpret_cast<const uint32_t(*)[8]>(&o.ks[0]));
+        dma_x8(rk, base + ST_K + 8192, o.kv, *reinterpret_cast<const uint32_t(*)[8]>(&o.ks[8]));
         const Rsrc rg = make_dma_rsrc(log_g + ru * Hv + vh, L * Hv * 4u);
         dma4(rg, stage + ST_G, o.gb);
     } else {
         const uint32_t v_row = (uint32_t)Hv * D * 2u;
         const Rsrc rt = make_dma_rsrc(slot, C * C * 2u);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dma16(rt, stage + ST_T + 1024 * j, o.t[j & 1], (uint32_t)(1024 * j));
+        dma_x8(rt, base + ST_T, o.tv, o.ts);
         const Rsrc rv = make_dma_rsrc(v + (ru * Hv + vh) * D + tile * TILE_COLS, L * v_row);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(rv, stage + ST_V + 1024 * j, o.v, (uint32_t)(16 * j) * v_row);
+        dma_x4(rv, base + ST_V, o.v, o.v, o.v, o.v, o.vs[0], o.vs[1], o.vs[2], o.vs[3]);
         const Rsrc rb = make_dma_rsrc(beta + ru * Hv + vh, L * Hv * 4u);
         dma4(rb, stage + ST_B, o.gb);
     }
@@ -613,10 +659,10 @@ __device__ __forceinline__ void spine_load_out(unsigned char* slot_lds, const Lo
                                                const uint16_t* q, const uint16_t* pslot, long row0,
                                                long len, int c, int Hk, int kh, int wl)
 {
+    const uint32_t base = lds_u32(slot_lds);
     if (wl == 0) {
         const Rsrc rp = make_dma_rsrc(pslot, C * C * 2u);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dma16(rp, slot_lds + OR_P + 1024 * j, o.t[j & 1], (uint32_t)(1024 * j));
+        dma_x8(rp, base + OR_P, o.tv, o.ts);
     } else {
         const long r = row0 + (long)c * C;
         const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)r);
@@ -625,8 +671,9 @@ __device__ __forceinline__ void spine_load_out(unsigned char* slot_lds, const Lo
         const uint32_t L = __builtin_amdgcn_readfirstlane((uint32_t)min((long)C, len - (long)c * C));
         const uint32_t q_row = (uint32_t)Hk * D * 2u;
         const Rsrc rq = make_dma_rsrc(q + (ru * Hk + kh) * D, L * q_row);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) dma16(rq, slot_lds + OR_Q + 1024 * j, o.k[(j >> 1) & 1], (uint32_t)(4 * j) * q_row);
+        (void)q_row;   // the Q rows share K's precomputed offsets (same k-head layout)
+        dma_x8(rq, base + OR_Q, o.kv, *reinterpret_cast<const uint32_t(*)[8]>(&o.ks[0]));
+        dma_x8(rq, base + OR_Q + 8192, o.kv, *reinterpret_cast<const uint32_t(*)[8]>(&o.ks[8]));
     }
 }
 
