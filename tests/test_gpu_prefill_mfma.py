@@ -6,7 +6,9 @@ Full-size workloads run through the same entry point and launch
 configuration bench.py times: the 1168-token and 4576-token calls are checked
 on every v-head; the packed 8-sequence workload on a sample of v-heads.
 Edge cases: sequences of 1, 63, 64, 65 and 130 tokens, empty packed
-sequences, fp32 outputs, in-place states.  Bitwise properties: repeated runs,
+sequences, fp32 outputs, in-place states, and 1, 2, 4, 5 and 8 v-heads per
+k-head (the WY kernel runs one wave per v-head in groups of up to four, so 5
+leaves a partial last group).  Bitwise properties: repeated runs,
 a state carried across a chunk-aligned split, and packed vs separate runs.
 """
 import numpy as np
@@ -55,6 +57,15 @@ def test_packed_workload_sampled_heads():
 def test_short_and_ragged(T):
     inp = synth.prefill_inputs(2, T, 1, 3, 128, 128, h0=True, seed=100 + T)
     say("ragged", T)
+    out, hf, route = gpu_prefill(inp, 64)
+    assert route.startswith(ROUTE)
+    check(inp, out, hf)
+
+
+@pytest.mark.parametrize("Hk,Hv", [(3, 3), (2, 4), (1, 4), (2, 10), (1, 8)])
+def test_vheads_per_khead(Hk, Hv):
+    inp = synth.prefill_inputs(1, 150, Hk, Hv, 128, 128, h0=True, seed=200 + 10 * Hk + Hv)
+    say("v-heads per k-head", Hk, Hv)
     out, hf, route = gpu_prefill(inp, 64)
     assert route.startswith(ROUTE)
     check(inp, out, hf)
