@@ -75,7 +75,7 @@ gdn_verify_k4_kernel(float* const* __restrict__ h_table, const TIn* __restrict__
 #pragma unroll
         for (int m = 0; m < 2 * kRows; ++m) acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int i = sl; i < dk; i += kSlices) {
-            const float4 h = *reinterpret_cast<const float4*>(h0 + (size_t)i * dv + 4 * cg);
+            const float4 h = load_global4(h0 + (size_t)i * dv + 4 * cg);
 #pragma unroll
             for (int r = 0; r < kRows; ++r) {
                 const float kk = sk[r][i], qq = sq[r][i];
@@ -185,163 +185,282 @@ gdn_fold_k4_kernel(float* const* __restrict__ h_table, const float* __restrict__
     const float gam = sc[na];
     for (int e = tid; e < dk * ncg; e += kThreads) {
         const int i = e / ncg, c4 = (e % ncg) * 4;
-        float4 x = *reinterpret_cast<float4*>(h + (size_t)i * dv + c4);
+        float4 x = load_global4(h + (size_t)i * dv + c4);
         x.x *= gam; x.y *= gam; x.z *= gam; x.w *= gam;
         for (int s = 0; s < na; ++s) {
             const float ks = sc[s] * sk[s][i];
             x.x += ks * sd[s][c4]; x.y += ks * sd[s][c4 + 1];
             x.z += ks * sd[s][c4 + 2]; x.w += ks * sd[s][c4 + 3];
         }
-        *reinterpret_cast<float4*>(h + (size_t)i * dv + c4) = x;
+        store_global4(h + (size_t)i * dv + c4, x);
     }
 }
 
-// dk = dv = 128 verify: one workgroup per (v-head, sequence), every state load
-// issued before any use.  Thread t reads rows 16 (t/32) .. +15 of column group
-// t%32 (4 columns); a wave's load covers two 512-byte row segments.  The 16
-// k.k / q.k dot products are split over all 256 threads and finished with lane
-// shuffles; the 8 slice partials are summed in two LDS passes.  (Splitting a
-// head over several workgroups measured slower: the per-workgroup key loads,
-// dot products and barriers repeat.)
+// dk = dv = 128 verify: one workgroup per (v-head, sequence), three per
+// compute unit.  Thread t owns rows t/32 + 8 m (m = 0..15) of column group
+// t%32 (4 columns): a wave's row load covers two adjacent rows (1 KiB) and the
+// workgroup's m-th load step the 4 KiB of rows 8m .. 8m+7, so the state is
+// read front to back.
+//
+// While the memory system is saturated, a wave cannot issue a load until the
+// queue in front of it drains, so a wave that issues all of its loads first
+// sits at the last issue for most of the stream and only then computes.  The
+// state loads are therefore software-pipelined: the small rows (keys,
+// queries, values, gates) and the first kLookahead state rows go out first,
+// and each later step issues row m + kLookahead and then takes row m, so the
+// dot products run between issues.  The 16 k.k / q.k products and the 4x4
+// scalars are formed while the first rows are in flight.  The two row slices
+// of a wave are added with a cross-half lane swap, the four wave partials
+// through LDS.  The state is read with nontemporal loads (it is read once).
+constexpr int kLookahead = 8;   // state rows in flight per thread
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// Empty fences that fix the order of the pipelined loads and arithmetic: the
+// first keeps memory operations on their side of it, the second makes the
+// accumulators complete before it (so their arithmetic cannot sink past the
+// next load issue).
+__device__ __forceinline__ void mem_fence_here() { asm volatile("" ::: "memory"); }
+__device__ __forceinline__ void pin(float4& a, float4& b)
+{
+    asm volatile("" : "+v"(a.x), "+v"(a.y), "+v"(a.z), "+v"(a.w), "+v"(b.x), "+v"(b.y), "+v"(b.z), "+v"(b.w));
+}
+
+__device__ __forceinline__ float4 state_row(rsrc_t r, int row, int cg)
+{
+    const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(
+        r, (uint32_t)((row * 128 + 4 * cg) * sizeof(float)), 0u, /*nontemporal*/ 2);
+    return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                       __uint_as_float(x.w));
+}
+
+// (q, k, v, gate and beta are not declared __restrict__: the order fences
+// then keep their loads ahead of the state's.)
 template <typename TIn, typename TOut>
 __global__ void __launch_bounds__(kThreads)
-gdn_verify_k4_d128_kernel(float* const* __restrict__ h_table, const TIn* __restrict__ q,
-                          const TIn* __restrict__ k, const TIn* __restrict__ v,
-                          const float* __restrict__ gate, const float* __restrict__ beta,
+gdn_verify_k4_d128_kernel(float* const* __restrict__ h_table, const TIn* q, const TIn* k,
+                          const TIn* v, const float* gate, const float* beta,
                           TOut* __restrict__ out, float* __restrict__ stash, int Hk, int Hv,
                           int qk_stride, int v_stride, int gb_stride, int stash_seq_floats,
                           uint32_t* __restrict__ engaged_flag)
 {
     constexpr int D = 128;
-    __shared__ __attribute__((aligned(16))) float sk[kRows][D];
-    __shared__ __attribute__((aligned(16))) float sq[kRows][D];
+    // keys and queries by row, rows padded to 144 floats so that the four
+    // rows read together by the k.k / q.k products fall in different banks
+    constexpr int KP = D + 16;
+    __shared__ __attribute__((aligned(16))) float sk[kRows][KP];
+    __shared__ __attribute__((aligned(16))) float sq[kRows][KP];
+    // the same keys and queries in the order one thread consumes them: row
+    // s + 8 m at [s][m] (16 rows of slice s, padded to 20)
+    constexpr int SP = 20;
+    __shared__ __attribute__((aligned(16))) float sk2[kRows][kSlices * SP];
+    __shared__ __attribute__((aligned(16))) float sq2[kRows][kSlices * SP];
     __shared__ __attribute__((aligned(16))) float sv[kRows][D];
-    __shared__ float4 part[kSlices][2 * kRows][kColGroups];
+    __shared__ float4 part[kThreads / 64][2 * kRows][kColGroups];
     __shared__ __attribute__((aligned(16))) float red[2 * kRows][D];
     __shared__ float sG[kRows], sBeta[kRows], sA[kRows][kRows], sQK[kRows][kRows];
 
     const int tid = threadIdx.x;
+    const int sl = tid >> 5, cg = tid & 31;
     const int vh = blockIdx.x, b = blockIdx.y;
     const int kh = vh / (Hv / Hk);
-    const int sl = tid >> 5, cg = tid & 31;
+    const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(h_table[b] + (size_t)vh * D * D, (short)0,
+                                                        D * D * (int)sizeof(float), 0x00020000);
 
-    const float* h0 = h_table[b] + (size_t)vh * D * D;
-    float4 hv[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m)
-        hv[m] = *reinterpret_cast<const float4*>(h0 + (size_t)(16 * sl + m) * D + 4 * cg);
-
+    // small rows, as raw elements (widened later): element tid + 256 u of
+    // [k | q | v] (4 rows of 128 each); every thread reads a gate and a beta
+    // so that the loads stay outside any branch
+    TIn small[6];
 #pragma unroll
     for (int u = 0; u < 6; ++u) {
         const int idx = tid + 256 * u, which = idx >> 9, r = (idx >> 7) & 3, i = idx & 127;
         const size_t row = (size_t)b * kRows + r;
-        if (which == 0) sk[r][i] = Elem<TIn>::load(k + row * qk_stride + (size_t)kh * D + i);
-        else if (which == 1) sq[r][i] = Elem<TIn>::load(q + row * qk_stride + (size_t)kh * D + i);
-        else sv[r][i] = Elem<TIn>::load(v + row * v_stride + (size_t)vh * D + i);
+        const TIn* src = which == 0 ? k + row * qk_stride + (size_t)kh * D + i
+                       : which == 1 ? q + row * qk_stride + (size_t)kh * D + i
+                                    : v + row * v_stride + (size_t)vh * D + i;
+        small[u] = *src;
     }
-    if (tid < kRows) {
-        const size_t off = ((size_t)b * kRows + tid) * gb_stride + vh;
-        sG[tid] = gate[off];
-        sBeta[tid] = beta[off];
+    const size_t goff = ((size_t)b * kRows + (tid & 3)) * gb_stride + vh;
+    const float g_in = gate[goff], b_in = beta[goff];
+    mem_fence_here();
+
+    float4 hv[16];
+#pragma unroll
+    for (int m = 0; m < kLookahead; ++m) hv[m] = state_row(rs, sl + 8 * m, cg);
+    mem_fence_here();
+
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+        const int idx = tid + 256 * u, which = idx >> 9, r = (idx >> 7) & 3, i = idx & 127;
+        const float x = Elem<TIn>::load(&small[u]);
+        const int i2 = (i & 7) * SP + (i >> 3);
+        if (which == 2) sv[r][i] = x;
+        else if (which == 1) { sq[r][i] = x; sq2[r][i2] = x; }
+        else { sk[r][i] = x; sk2[r][i2] = x; }
     }
+    if (tid < kRows) { sG[tid] = g_in; sBeta[tid] = b_in; }
     __syncthreads();
 
-    // partial h0^T k_r and h0^T q_r over this thread's 16 rows
-    float4 acc[2 * kRows];
-#pragma unroll
-    for (int m = 0; m < 2 * kRows; ++m) acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-#pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) {
-            const float4 kk4 = *reinterpret_cast<const float4*>(&sk[r][16 * sl + 4 * m4]);
-            const float4 qq4 = *reinterpret_cast<const float4*>(&sq[r][16 * sl + 4 * m4]);
-            const float kk[4] = {kk4.x, kk4.y, kk4.z, kk4.w};
-            const float qq[4] = {qq4.x, qq4.y, qq4.z, qq4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float4 h = hv[4 * m4 + e];
-                acc[r].x += h.x * kk[e]; acc[r].y += h.y * kk[e]; acc[r].z += h.z * kk[e]; acc[r].w += h.w * kk[e];
-                acc[kRows + r].x += h.x * qq[e]; acc[kRows + r].y += h.y * qq[e];
-                acc[kRows + r].z += h.z * qq[e]; acc[kRows + r].w += h.w * qq[e];
-            }
-        }
-    }
-#pragma unroll
-    for (int m = 0; m < 2 * kRows; ++m) part[sl][m][cg] = acc[m];
-
-    // k_r . k_s and q_r . k_s: pair tid/16, 8-element segment tid%16
+    // k_r . k_s and q_r . k_s: pair tid/16 sums elements tid%16 + 16 e; the
+    // 4x4 decay-weighted scalars are finished by the 16 lane-0 threads of the
+    // pairs
     {
         const int pr = tid >> 4, seg = tid & 15, r = pr >> 2, s2 = pr & 3;
         float kk = 0.f, qk = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float ks = sk[s2][8 * seg + e];
-            kk += sk[r][8 * seg + e] * ks;
-            qk += sq[r][8 * seg + e] * ks;
+            const int i = seg + 16 * e;
+            const float ks = sk[s2][i];
+            kk += sk[r][i] * ks;
+            qk += sq[r][i] * ks;
         }
 #pragma unroll
         for (int off = 8; off > 0; off >>= 1) {
             kk += __shfl_xor(kk, off, 16);
             qk += __shfl_xor(qk, off, 16);
         }
-        if (seg == 0) { sA[r][s2] = kk; sQK[r][s2] = qk; }
+        if (seg == 0) {
+            float Gr = 0.f, Gs = 0.f;
+            for (int t = 0; t < kRows; ++t) {
+                if (t <= r) Gr += sG[t];
+                if (t <= s2) Gs += sG[t];
+            }
+            const float gam = s2 <= r ? __expf(Gr - Gs) : 0.f;
+            sA[r][s2] = s2 < r ? sBeta[r] * gam * kk : 0.f;
+            sQK[r][s2] = gam * qk;
+        }
+    }
+
+    // partial h0^T k_r and h0^T q_r over this thread's 16 rows, 4 rows a step,
+    // each step first issuing the rows kLookahead ahead
+    float4 acc[2 * kRows];
+#pragma unroll
+    for (int m = 0; m < 2 * kRows; ++m) acc[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int m4 = 0; m4 < 4; ++m4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = 4 * m4 + e + kLookahead;
+            if (m < 16) hv[m] = state_row(rs, sl + 8 * m, cg);
+        }
+        mem_fence_here();
+        float kk[kRows][4], qq[kRows][4];
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const float4 a4 = *reinterpret_cast<const float4*>(&sk2[r][sl * SP + 4 * m4]);
+            const float4 c4 = *reinterpret_cast<const float4*>(&sq2[r][sl * SP + 4 * m4]);
+            kk[r][0] = a4.x; kk[r][1] = a4.y; kk[r][2] = a4.z; kk[r][3] = a4.w;
+            qq[r][0] = c4.x; qq[r][1] = c4.y; qq[r][2] = c4.z; qq[r][3] = c4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float4 h = hv[4 * m4 + e];
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                const float a = kk[r][e], c = qq[r][e];
+                acc[r].x += h.x * a; acc[r].y += h.y * a; acc[r].z += h.z * a; acc[r].w += h.w * a;
+                acc[kRows + r].x += h.x * c; acc[kRows + r].y += h.y * c;
+                acc[kRows + r].z += h.z * c; acc[kRows + r].w += h.w * c;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) pin(acc[r], acc[kRows + r]);
+    }
+    // add the wave's two slices (lanes l and l+32): after the swap, lanes
+    // 0..31 hold the k-vector sums (acc 0..3), lanes 32..63 the q-vector sums
+    {
+        const int hi = (tid >> 5) & 1;
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            float* a = &acc[r].x;
+            float* c = &acc[kRows + r].x;
+            float4 s4;
+            float* sp = &s4.x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[e]), __float_as_uint(c[e]),
+                                                                 false, false);
+                sp[e] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            }
+            part[tid >> 6][hi * kRows + r][cg] = s4;
+        }
     }
     __syncthreads();
 
-    // sum the 8 slices: thread -> (vector tid/32, column group tid%32)
+    // sum the 4 wave partials: thread -> (vector tid/32, column group tid%32)
     {
         const int vec = tid >> 5;
         float4 t = part[0][vec][cg];
 #pragma unroll
-        for (int s2 = 1; s2 < kSlices; ++s2) {
-            const float4 u4 = part[s2][vec][cg];
+        for (int w = 1; w < kThreads / 64; ++w) {
+            const float4 u4 = part[w][vec][cg];
             t.x += u4.x; t.y += u4.y; t.z += u4.z; t.w += u4.w;
         }
         *reinterpret_cast<float4*>(&red[vec][4 * cg]) = t;
     }
-    if (tid == 0) {
-        float a = 0.f;
-        for (int r = 0; r < kRows; ++r) { a += sG[r]; sG[r] = a; }
-        for (int r = 0; r < kRows; ++r)
-            for (int s2 = 0; s2 < kRows; ++s2) {
-                const float gam = s2 <= r ? __expf(sG[r] - sG[s2]) : 0.f;
-                sA[r][s2] = s2 < r ? sBeta[r] * gam * sA[r][s2] : 0.f;
-                sQK[r][s2] = s2 <= r ? gam * sQK[r][s2] : 0.f;
-            }
-    }
     __syncthreads();
 
-    float* st = stash + (size_t)b * stash_seq_floats + (size_t)vh * stash_head_floats(D, D, sizeof(TIn) == 2);
-    if (tid < D) {
-        const int j = tid;
-        float d[kRows];
+    // Outputs and stash: every thread solves column tid%128 (the two halves
+    // of the workgroup redundantly) and issues the same 7 buffer stores, with
+    // no branch; lanes with nothing to write use an offset past the range.
+    {
+        const int j = tid & (D - 1), half = tid >> 7;
+        const size_t hs = stash_head_floats(D, D, sizeof(TIn) == 2);
+        const size_t row_out = (size_t)Hv * D;   // out elements between rows r and r+1
+        const rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            out + ((size_t)b * kRows * Hv + vh) * D, (short)0,
+            (int)(((kRows - 1) * row_out + D) * sizeof(TOut)), 0x00020000);
+        const rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
+            stash + (size_t)b * stash_seq_floats + (size_t)vh * hs, (short)0, (int)(hs * sizeof(float)),
+            0x00020000);
+        float G[kRows], a = 0.f;
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) { a += sG[r]; G[r] = a; }
+        float d[kRows], o[kRows];
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
-            float x = sBeta[r] * (sv[r][j] - __expf(sG[r]) * red[r][j]);
+            float x = sBeta[r] * (sv[r][j] - __expf(G[r]) * red[r][j]);
 #pragma unroll
             for (int m = 0; m < r; ++m) x -= sA[r][m] * d[m];
             d[r] = x;
         }
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
-            float o = __expf(sG[r]) * red[kRows + r][j];
+            float y = __expf(G[r]) * red[kRows + r][j];
 #pragma unroll
-            for (int s2 = 0; s2 <= r; ++s2) o += sQK[r][s2] * d[s2];
-            Elem<TOut>::store(out + (((size_t)b * kRows + r) * Hv + vh) * D + j, o);
-            st[r * D + j] = d[r];
+            for (int s2 = 0; s2 <= r; ++s2) y += sQK[r][s2] * d[s2];
+            o[r] = y;
         }
-    } else {
-        const int t2 = tid - D;   // 128 threads: G and the keys
-        if (t2 < kRows) st[kRows * D + t2] = sG[t2];
-        float* sk_out = st + kRows * D + kRows;
-        for (int e = t2; e < kRows * D; e += kThreads - D) {
-            const int r = e / D, i = e % D;
-            if (sizeof(TIn) == 2)
-                reinterpret_cast<uint16_t*>(sk_out)[e] =
-                    *reinterpret_cast<const uint16_t*>(k + ((size_t)b * kRows + r) * qk_stride + (size_t)kh * D + i);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int r = 2 * half + u;
+            const float ov = half ? o[2 + u] : o[u];
+            const float dv_ = half ? d[2 + u] : d[u];
+            const uint32_t oo = (uint32_t)((r * row_out + j) * sizeof(TOut));
+            if (sizeof(TOut) == 2)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(ov), ro, oo, 0u, 0);
             else
-                sk_out[e] = sk[r][i];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), ro, oo, 0u, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dv_), rst,
+                                                  (uint32_t)((r * D + j) * sizeof(float)), 0u, 0);
+        }
+        // the cumulative log decay G_0..G_3 (threads 0..3)
+        const float gsel = (tid & 3) == 0 ? G[0] : (tid & 3) == 1 ? G[1] : (tid & 3) == 2 ? G[2] : G[3];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gsel), rst,
+                                              tid < kRows ? (uint32_t)((kRows * D + tid) * sizeof(float)) : 0x7fffffffu,
+                                              0u, 0);
+        // the keys, element tid + 256 u of [4][dk]
+        const uint32_t kbase = (uint32_t)((kRows * D + kRows) * sizeof(float));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = tid + kThreads * u, r = e / D, i = e % D;
+            const float x = sk[r][i];
+            if (sizeof(TIn) == 2)   // the widened bf16 key: its high half is the bits as read
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(__float_as_uint(x) >> 16), rst,
+                                                      kbase + 2u * e, 0u, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rst, kbase + 4u * e, 0u, 0);
         }
     }
     if (vh == 0 && b == 0 && tid == 0) engaged_flag[0] = 1u;
@@ -378,7 +497,7 @@ gdn_fold_k4_d128_kernel(float* const* __restrict__ h_table, const float* __restr
     float* h = h_table[b] + (size_t)vh * D * D + c0;
     float4 hv[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) hv[m] = *reinterpret_cast<const float4*>(h + (size_t)(4 * sl + m) * D + 4 * cg);
+    for (int m = 0; m < 4; ++m) hv[m] = load_global4(h + (size_t)(4 * sl + m) * D + 4 * cg);
 
     const float* st = stash + (size_t)b * stash_seq_floats + (size_t)vh * stash_head_floats(D, D, kBf16Keys);
     if (tid < na * kQCols) sd[tid / kQCols][tid % kQCols] = st[(tid / kQCols) * D + c0 + tid % kQCols];
@@ -409,7 +528,7 @@ gdn_fold_k4_d128_kernel(float* const* __restrict__ h_table, const float* __restr
                 x.x += ks * dv4.x; x.y += ks * dv4.y; x.z += ks * dv4.z; x.w += ks * dv4.w;
             }
         }
-        *reinterpret_cast<float4*>(h + (size_t)i * D + 4 * cg) = x;
+        store_global4(h + (size_t)i * D + 4 * cg, x);
     }
 }
 
@@ -441,8 +560,9 @@ Geometry verify_geometry(const VerifyArgs& a)
 {
     if (a.dk == 128 && a.dv == 128) {
         Geometry g{"gdn_verify_k4_d128_kernel", {(unsigned)a.Hv, (unsigned)a.B, 1u}, kThreads,
-                   (unsigned)(sizeof(float) * (3 * kRows * 128 + 2 * kRows * 128 + 2 * kRows + 2 * kRows * kRows) +
-                              sizeof(float4) * kSlices * 2 * kRows * kColGroups)};
+                   (unsigned)(sizeof(float) * (2 * kRows * 144 + 2 * kRows * kSlices * 20 + kRows * 128 +
+                                               2 * kRows * 128 + 2 * kRows + 2 * kRows * kRows) +
+                              sizeof(float4) * (kThreads / 64) * 2 * kRows * kColGroups)};
         return g;
     }
     Geometry g{"gdn_verify_k4_kernel", {(unsigned)a.Hv, (unsigned)a.B, 1u}, kThreads,

@@ -91,6 +91,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// States reached through a device pointer table are plain (generic) pointers
+// to the compiler, which then issues flat loads and stores; flat accesses count
+// on the LDS counter as well, so every LDS wait would also wait for them.
+// Naming the global address space gives global accesses.
+#define GDN_GLOBAL __attribute__((address_space(1)))
+typedef float gdn_f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_global4(const float* p) {
+    const gdn_f4 x = *(const GDN_GLOBAL gdn_f4*)p;
+    return make_float4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ void store_global4(float* p, float4 v) {
+    *(GDN_GLOBAL gdn_f4*)p = gdn_f4{v.x, v.y, v.z, v.w};
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
     __device__ __forceinline__ static float load(const float* p) { return *p; }

@@ -120,6 +120,33 @@ def test_verify_fold_workload(io, out_dtype, tol, pad):
         assert torch.equal(x.cpu(), y), "a slot outside the table changed"
 
 
+@pytest.mark.parametrize("B,Hk,Hv", [(3, 2, 6), (87, 1, 3), (13, 1, 5)])
+def test_d128_shapes_and_stash_bounds(B, Hk, Hv):
+    """dk = dv = 128 verify at several batch and head counts, with padded
+    rows and a padded stash whose padding must stay untouched."""
+    inp = synth.decode_inputs(B, K, Hk, Hv, 128, 128, io=torch.bfloat16, seed=60 + B)
+    say("decode d128 shapes", B, Hk, Hv)
+    s = Setup(inp, torch.bfloat16, torch.float32, qk_pad=8, stash_pad=16)
+    before = s.states()
+    s.clear()
+    route = s.verify()
+    torch.cuda.synchronize()
+    assert route.startswith(f"gdn_verify_k4_d128_kernel grid=[{Hv},{B},1]"), route
+    stash = s.stash.view(B, s.ssf).cpu()
+    assert torch.isnan(stash[:, s.ssf - 16:]).all(), "the stash padding must stay untouched"
+    ro, after = oracle_decode(inp)
+    assert rel_err(s.out, ro) <= 1e-4
+    s.fold()
+    torch.cuda.synchronize()
+    got = s.states()
+    for b in range(B):
+        na = int(inp["na"][b])
+        if na == 0:
+            assert torch.equal(got[b], before[b])
+        else:
+            assert rel_err(got[b], after[b, na]) <= 1e-4, (b, na)
+
+
 @pytest.mark.parametrize("dk,dv", [(64, 96), (128, 64), (32, 128)])
 def test_generic_shapes(dk, dv):
     """Head sizes other than 128 take the generic verify/fold kernels."""
