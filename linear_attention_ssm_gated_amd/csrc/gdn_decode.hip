@@ -466,69 +466,100 @@ gdn_verify_k4_d128_kernel(float* const* __restrict__ h_table, const TIn* q, cons
     if (vh == 0 && b == 0 && tid == 0) engaged_flag[0] = 1u;
 }
 
-// The fold splits each state into 32-column quarters (four workgroups per
-// (v-head, sequence)): it has no per-workgroup reduction to repeat, and the
-// extra workgroups overlap one another's loads and stores.
-constexpr int kQuarters = 4;
-constexpr int kQCols = 128 / kQuarters;   // 32 columns
-
-// dk = dv = 128 fold: one workgroup per (v-head, sequence, 32-column quarter);
-// each thread issues its four state loads before anything else.
+// dk = dv = 128 fold: one workgroup per (v-head, sequence), laid out like the
+// verify (thread t updates rows t/32 + 8 m of column group t%32, so each load
+// step of the workgroup covers 4 KiB front to back).  The stash reads (deltas,
+// decays, keys) go out first, then the state rows, pipelined kLookahead rows
+// ahead of the update; each row is written back as soon as it is updated.
+// The state is read and written with nontemporal accesses.
 template <bool kBf16Keys>
 __global__ void __launch_bounds__(kThreads)
-gdn_fold_k4_d128_kernel(float* const* __restrict__ h_table, const float* __restrict__ stash,
+gdn_fold_k4_d128_kernel(float* const* __restrict__ h_table, const float* stash,
                         const int32_t* __restrict__ na_tab, const uint32_t* __restrict__ engaged_flag,
                         int stash_seq_floats)
 {
     constexpr int D = 128;
-    __shared__ __attribute__((aligned(16))) float sk[kRows][D];
-    __shared__ __attribute__((aligned(16))) float sd[kRows][kQCols];
-    __shared__ float sc[kRows + 1];
+    constexpr int SP = 20;   // keys of slice s at [s][m] = row s + 8 m, padded
+    __shared__ __attribute__((aligned(16))) float sk2[kRows][kSlices * SP];
 
     if (engaged_flag[0] == 0u) return;   // the write-on-accept verify did not run
-    const int vh = blockIdx.x / kQuarters, qc = blockIdx.x % kQuarters;
-    const int b = blockIdx.y;
+    const int vh = blockIdx.x, b = blockIdx.y;
     const int na = min(max(na_tab[b], 0), kRows);
     if (na == 0) return;                 // nothing accepted: the state keeps its bytes
     const int tid = threadIdx.x;
-    const int sl = tid >> 3, cg = tid & 7;
-    const int c0 = qc * kQCols;
-
-    float* h = h_table[b] + (size_t)vh * D * D + c0;
-    float4 hv[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) hv[m] = load_global4(h + (size_t)(4 * sl + m) * D + 4 * cg);
-
+    const int sl = tid >> 5, cg = tid & 31;
     const float* st = stash + (size_t)b * stash_seq_floats + (size_t)vh * stash_head_floats(D, D, kBf16Keys);
-    if (tid < na * kQCols) sd[tid / kQCols][tid % kQCols] = st[(tid / kQCols) * D + c0 + tid % kQCols];
-    const float* sk_in = st + kRows * D + kRows;
-    for (int e = tid; e < na * D; e += kThreads) {
-        float x;
-        if (kBf16Keys) x = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sk_in)[e]);
-        else x = sk_in[e];
-        sk[e / D][e % D] = x;
+    const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(h_table[b] + (size_t)vh * D * D, (short)0,
+                                                        D * D * (int)sizeof(float), 0x00020000);
+
+    // stash: this thread's 4 delta columns of every row, the 4 decays, and
+    // key elements tid and tid + 256 of [4][dk]
+    float dl[kRows][4];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dl[r][c] = st[r * D + 4 * cg + c];
+    float G[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) G[r] = st[kRows * D + r];
+    float kraw[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int e = tid + kThreads * u;
+        if (kBf16Keys) kraw[u] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(st + kRows * D + kRows)[e]);
+        else kraw[u] = st[kRows * D + kRows + e];
     }
-    if (tid <= na) {
-        const float gl = st[kRows * D + na - 1];
-        sc[tid] = tid < na ? __expf(gl - st[kRows * D + tid]) : __expf(gl);
+    mem_fence_here();
+
+    float4 hv[16];
+#pragma unroll
+    for (int m = 0; m < kLookahead; ++m) hv[m] = state_row(rs, sl + 8 * m, cg);
+    mem_fence_here();
+
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int e = tid + kThreads * u, r = e / D, i = e % D;
+        sk2[r][(i & 7) * SP + (i >> 3)] = kraw[u];
     }
+    // c_s = exp(G_{na-1} - G_s) for the accepted rows, gamma = exp(G_{na-1})
+    const float gl = G[na - 1];
+    float cs[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) cs[r] = r < na ? __expf(gl - G[r]) : 0.f;
+    const float gam = __expf(gl);
     __syncthreads();
 
-    const float gam = sc[na];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int i = 4 * sl + m;
-        float4 x = hv[m];
-        x.x *= gam; x.y *= gam; x.z *= gam; x.w *= gam;
+    for (int m4 = 0; m4 < 4; ++m4) {
 #pragma unroll
-        for (int s2 = 0; s2 < kRows; ++s2) {
-            if (s2 < na) {
-                const float ks = sc[s2] * sk[s2][i];
-                const float4 dv4 = *reinterpret_cast<const float4*>(&sd[s2][4 * cg]);
-                x.x += ks * dv4.x; x.y += ks * dv4.y; x.z += ks * dv4.z; x.w += ks * dv4.w;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const int m = 4 * m4 + e + kLookahead;
+            if (m < 16) hv[m] = state_row(rs, sl + 8 * m, cg);
         }
-        store_global4(h + (size_t)i * D + 4 * cg, x);
+        mem_fence_here();
+        float kk[kRows][4];
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const float4 a4 = *reinterpret_cast<const float4*>(&sk2[r][sl * SP + 4 * m4]);
+            kk[r][0] = a4.x; kk[r][1] = a4.y; kk[r][2] = a4.z; kk[r][3] = a4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = 4 * m4 + e;
+            float4 x = hv[m];
+            x.x *= gam; x.y *= gam; x.z *= gam; x.w *= gam;
+#pragma unroll
+            for (int s2 = 0; s2 < kRows; ++s2) {
+                if (s2 < na) {
+                    const float ks = cs[s2] * kk[s2][e];
+                    x.x += ks * dl[s2][0]; x.y += ks * dl[s2][1]; x.z += ks * dl[s2][2]; x.w += ks * dl[s2][3];
+                }
+            }
+            const u32x4v o = {__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)};
+            __builtin_amdgcn_raw_buffer_store_b128(o, rs, (uint32_t)(((sl + 8 * m) * D + 4 * cg) * sizeof(float)),
+                                                   0u, /*nontemporal*/ 2);
+        }
+        mem_fence_here();
     }
 }
 
@@ -574,8 +605,8 @@ Geometry verify_geometry(const VerifyArgs& a)
 Geometry fold_geometry(const FoldArgs& a)
 {
     if (a.dk == 128 && a.dv == 128) {
-        Geometry g{"gdn_fold_k4_d128_kernel", {(unsigned)(a.Hv * kQuarters), (unsigned)a.B, 1u}, kThreads,
-                   (unsigned)(sizeof(float) * (kRows * 128 + kRows * kQCols + kRows + 1))};
+        Geometry g{"gdn_fold_k4_d128_kernel", {(unsigned)a.Hv, (unsigned)a.B, 1u}, kThreads,
+                   (unsigned)(sizeof(float) * kRows * kSlices * 20)};
         return g;
     }
     Geometry g{"gdn_fold_k4_kernel", {(unsigned)a.Hv, (unsigned)a.B, 1u}, kThreads,
@@ -601,10 +632,10 @@ hipError_t launch_fold(const FoldArgs& a, hipStream_t s)
 {
     if (a.dk == 128 && a.dv == 128) {
         if (a.io_dtype == 1)
-            hipLaunchKernelGGL((gdn_fold_k4_d128_kernel<true>), dim3(a.Hv * kQuarters, a.B), dim3(kThreads), 0, s,
+            hipLaunchKernelGGL((gdn_fold_k4_d128_kernel<true>), dim3(a.Hv, a.B), dim3(kThreads), 0, s,
                                a.h_table, a.stash, a.na_tab, a.engaged_flag, a.stash_seq_floats);
         else
-            hipLaunchKernelGGL((gdn_fold_k4_d128_kernel<false>), dim3(a.Hv * kQuarters, a.B), dim3(kThreads), 0, s,
+            hipLaunchKernelGGL((gdn_fold_k4_d128_kernel<false>), dim3(a.Hv, a.B), dim3(kThreads), 0, s,
                                a.h_table, a.stash, a.na_tab, a.engaged_flag, a.stash_seq_floats);
         return hipGetLastError();
     }

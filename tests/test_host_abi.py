@@ -150,7 +150,7 @@ def fold_plan(lib, **kw):
 
 def test_fold_plan(lib):
     assert fold_plan(lib) == 0
-    assert gdn.last_route().startswith("gdn_fold_k4_d128_kernel grid=[192,16,1] block=256")
+    assert gdn.last_route().startswith("gdn_fold_k4_d128_kernel grid=[48,16,1] block=256")
 
 
 @pytest.mark.parametrize("kw,status", [
