@@ -66,6 +66,13 @@ def fold_bytes(na, Hv, dk, dv, K=4):
     return sum(Hv * (2 * dk * dv * 4 + n * (dv * 4 + dk * 2) + K * 4) for n in na if n > 0)
 
 
+def step_bytes(B, Hk, Hv, dk, dv, s_io=2, s_out=2):
+    """Read and write each state once; read one row of q, k, v, gate, beta per
+    sequence; write one output row."""
+    return (B * Hv * dk * dv * 4 * 2 + B * (2 * Hk * dk + Hv * dv) * s_io + B * Hv * 8
+            + B * Hv * dv * s_out)
+
+
 def kernel_source_sha():
     import glob
     h = hashlib.sha256()
@@ -288,6 +295,51 @@ def bench_verify(w, args, torch):
     }
 
 
+def bench_step(w, args, torch):
+    import linear_attention_ssm_gated_amd as gdn
+    import synth
+    d = torch.device("cuda:0")
+    inp = synth.decode_inputs(w.B, 1, w.Hk, w.Hv, w.dk, w.dv, seed=w.seed)
+    byt = step_bytes(w.B, w.Hk, w.Hv, w.dk, w.dv)
+    n_sets = max(3, int(ROTATE_BYTES // byt) + 1)
+    sets = []
+    for _ in range(n_sets):
+        slots = [inp["states"][b].to(d).clone() for b in range(w.B)]
+        sets.append(dict(
+            slots=slots,
+            table=torch.tensor([s.data_ptr() for s in slots], dtype=torch.int64, device=d),
+            q=inp["q"].reshape(w.B, -1).to(d), k=inp["k"].reshape(w.B, -1).to(d),
+            v=inp["v"].reshape(w.B, -1).to(d), gate=inp["gate"].reshape(w.B, -1).to(d),
+            beta=inp["beta"].reshape(w.B, -1).to(d),
+            out=torch.empty((w.B, w.Hv, w.dv), dtype=torch.bfloat16, device=d)))
+    route = []
+
+    def launch(i):   # on the current stream (the capture stream while a graph is recorded)
+        g = sets[i]
+        r = gdn.gdn_decode_step(g["table"], g["q"], g["k"], g["v"], g["gate"], g["beta"], g["out"],
+                                w.B, w.Hk, w.Hv, w.dk, w.dv, w.Hk * w.dk, w.Hv * w.dv, w.Hv,
+                                stream=None)
+        if not route:
+            route.append(r)
+
+    total_ms, kern_ms, eager_ms = time_launches(launch, n_sets, args.warmup, args.steps, torch)
+    ach = byt / (kern_ms * 1e-3) / 1e9
+    return {
+        "metric": "GDN K=1 decode step, achieved HBM GB/s (B=16, Hv=48, d=128)",
+        "value": ach, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 state, bf16 q/k/v", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "K": 1, "Hk": w.Hk, "Hv": w.Hv, "dk": w.dk, "dv": w.dv},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
+                     "algorithmic_bytes": byt, "kernel_ms": kern_ms, "eager_launch_ms": eager_ms},
+        "timing": "HIP events around one replay of a graph of the K launches",
+        "tokens_per_s": w.B / (kern_ms * 1e-3),
+        "route": route[0] if route else None,
+        "input_sets_rotated": n_sets,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,7 +370,12 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
         return
     w = synth.WORKLOADS[args.workload]
-    rec = bench_prefill(w, args, torch) if w.kind == "prefill" else bench_verify(w, args, torch)
+    if w.kind == "prefill":
+        rec = bench_prefill(w, args, torch)
+    elif w.kind == "decode_step":
+        rec = bench_step(w, args, torch)
+    else:
+        rec = bench_verify(w, args, torch)
     print(json.dumps(rec), flush=True)
 
 

@@ -124,38 +124,48 @@ int gdn_chunk_prefill_plan(const void* q, const void* k, const void* v,
                            void* workspace, size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------ */
-/* K = 4 write-on-accept decode verify, its fold, and the engaged word
+/* Write-on-accept decode verify of K draft rows (the pages' K = 4, and any K
+ * in 1..8 from the same chunk algebra), its fold, and the engaged word
  * (ssm_gdn_woa.rs: docs of gdn_decode_wy4_woa, gdn_wy4_fold and
  * gdn_wy4_flag_clear).  Protocol, on one stream: gdn_flag_clear, then
- * gdn_decode_verify_k4 (writes outputs and the stash, marks the word, writes
- * NO state), then the caller writes na_tab, then gdn_fold (if the word is
- * set, applies the first na_tab[b] stashed rows to each state, reading and
- * writing it once).
+ * gdn_decode_verify (or gdn_decode_verify_k4) (writes outputs and the stash,
+ * marks the word, writes NO state), then the caller writes na_tab, then
+ * gdn_fold with the same k_rows (if the word is set, applies the first
+ * na_tab[b] stashed rows to each state, reading and writing it once).
  *
- * Verify rows: row r (0..3) of sequence b is global row b*4 + r.
- *   q, k : row at q + (b*4 + r)*qk_stride, k-head kh at + kh*dk   (io_dtype)
- *   v    : row at v + (b*4 + r)*v_stride,  v-head vh at + vh*dv   (io_dtype)
- *   gate, beta: fp32 at (b*4 + r)*gb_stride + vh; gate is log-space like log_g
- *   out  : dense [B][4][Hv][dv] (out_dtype)
+ * Verify rows: row r (0..K-1) of sequence b is global row b*K + r.
+ *   q, k : row at q + (b*K + r)*qk_stride, k-head kh at + kh*dk   (io_dtype)
+ *   v    : row at v + (b*K + r)*v_stride,  v-head vh at + vh*dv   (io_dtype)
+ *   gate, beta: fp32 at (b*K + r)*gb_stride + vh; gate is log-space like log_g
+ *   out  : dense [B][K][Hv][dv] (out_dtype)
  *   h_table[b]: device pointer to sequence b's states [Hv][dk][dv] fp32
  *   stash: sequence b at stash + b*stash_seq_floats; per v-head vh, at
- *          vh*(4*dv + 4 + kfl) floats: delta [4][dv] fp32, G [4] fp32 (the
- *          within-verify cumulative log decay), then the 4 keys [4][dk] as
- *          kfl = 4*dk floats (fp32 io) or 2*dk floats of packed bf16 bits (bf16
- *          io).  The fold receives no q/k/v/gate, so the stash carries them.
+ *          vh*(K*dv + K + kfl) floats: delta [K][dv] fp32, G [K] fp32 (the
+ *          within-verify cumulative log decay), then the K keys [K][dk] as
+ *          kfl = K*dk floats (fp32 io) or ceil(K*dk/2) floats of packed bf16
+ *          bits (bf16 io).  The fold receives no q/k/v/gate, so the stash
+ *          carries them.
  *   engaged_flag: one device uint32; verify sets it to 1.
  * Fold:
- *   na_tab: device int32 [B], accepted rows per sequence, clamped to 0..4;
+ *   na_tab: device int32 [B], accepted rows per sequence, clamped to 0..K;
  *           na = 0 leaves the state's bytes unchanged.
  *   hi_tables / slab_entries: the restore branch of a non-write-on-accept
  *           verify (word not set).  Not built here: hi_tables must be NULL,
  *           and with the word clear the fold changes nothing.
- *   k_rows: must be 4.
+ *   k_rows: K of the verify that filled the stash, 1..8.
+ * Errors: GDN_ERR_K_ROWS for k_rows outside 1..8; the others as below.
  */
 size_t gdn_stash_seq_floats(int Hv, int dk, int dv, int k_rows, int io_dtype);
 
 int gdn_flag_clear(uint32_t* engaged_flag, hipStream_t stream);
 
+int gdn_decode_verify(float* const* h_table, const void* q, const void* k, const void* v,
+                      const float* gate, const float* beta, void* out, float* stash,
+                      int B, int Hk, int Hv, int dk, int dv, int k_rows,
+                      int qk_stride, int v_stride, int gb_stride, int stash_seq_floats,
+                      uint32_t* engaged_flag, int io_dtype, int out_dtype, hipStream_t stream);
+
+/* gdn_decode_verify with k_rows = 4 (the pages' K). */
 int gdn_decode_verify_k4(float* const* h_table, const void* q, const void* k, const void* v,
                          const float* gate, const float* beta, void* out, float* stash,
                          int B, int Hk, int Hv, int dk, int dv,
@@ -167,7 +177,13 @@ int gdn_fold(float* const* h_table, const float* stash, const int32_t* na_tab,
              int k_rows, int B, int Hk, int Hv, int dk, int dv, int stash_seq_floats,
              int io_dtype, hipStream_t stream);
 
-/* Validation of the two calls above without launching (same return codes). */
+/* Validation of the calls above without launching (same return codes). */
+int gdn_decode_verify_plan(float* const* h_table, const void* q, const void* k,
+                           const void* v, const float* gate, const float* beta, void* out,
+                           float* stash, int B, int Hk, int Hv, int dk, int dv, int k_rows,
+                           int qk_stride, int v_stride, int gb_stride, int stash_seq_floats,
+                           uint32_t* engaged_flag, int io_dtype, int out_dtype);
+
 int gdn_decode_verify_k4_plan(float* const* h_table, const void* q, const void* k,
                               const void* v, const float* gate, const float* beta, void* out,
                               float* stash, int B, int Hk, int Hv, int dk, int dv,
@@ -178,6 +194,29 @@ int gdn_fold_plan(float* const* h_table, const float* stash, const int32_t* na_t
                   float* const* hi_tables, int slab_entries, const uint32_t* engaged_flag,
                   int k_rows, int B, int Hk, int Hv, int dk, int dv, int stash_seq_floats,
                   int io_dtype);
+
+/* ------------------------------------------------------------------------ */
+/* Single-token decode step (K = 1), in place: the chunk algebra with L = 1
+ * (one row of the token recurrence) applied to each state,
+ *   alpha = exp(gate), delta = beta (v - alpha h^T k),
+ *   out = alpha h^T q + (q . k) delta,  h <- alpha h + k delta^T,
+ * so out is the new state applied to q.  Row b of q, k, v, gate, beta is
+ * sequence b's token (layouts as in the verify with K = 1); out is dense
+ * [B][Hv][dv]; h_table[b] points at sequence b's states [Hv][dk][dv] fp32,
+ * which are read and written once.  dk, dv <= 128, dv a multiple of 4.
+ * Returns GDN_OK or one of the GDN_ERR_* codes (nothing launched on error).
+ */
+int gdn_decode_step(float* const* h_table, const void* q, const void* k, const void* v,
+                    const float* gate, const float* beta, void* out,
+                    int B, int Hk, int Hv, int dk, int dv,
+                    int qk_stride, int v_stride, int gb_stride,
+                    int io_dtype, int out_dtype, hipStream_t stream);
+
+int gdn_decode_step_plan(float* const* h_table, const void* q, const void* k, const void* v,
+                         const float* gate, const float* beta, void* out,
+                         int B, int Hk, int Hv, int dk, int dv,
+                         int qk_stride, int v_stride, int gb_stride,
+                         int io_dtype, int out_dtype);
 
 #ifdef __cplusplus
 }

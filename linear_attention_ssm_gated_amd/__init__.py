@@ -36,10 +36,14 @@ SIGNATURES = {
     "gdn_chunk_prefill_plan": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, I, I, P, Z]),
     "gdn_stash_seq_floats": (Z, [I, I, I, I, I]),
     "gdn_flag_clear": (I, [P, P]),
+    "gdn_decode_verify": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, I, I, P]),
+    "gdn_decode_verify_plan": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, I, I]),
     "gdn_decode_verify_k4": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, I, I, P]),
     "gdn_decode_verify_k4_plan": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, I, I]),
     "gdn_fold": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, I, P]),
     "gdn_fold_plan": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, I]),
+    "gdn_decode_step": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P]),
+    "gdn_decode_step_plan": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I]),
 }
 
 _lib = None
@@ -138,6 +142,23 @@ def gdn_decode_verify_k4(h_table, q, k, v, gate, beta, out, stash, B, Hk, Hv, dk
         _ptr(h_table), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(out), _ptr(stash),
         B, Hk, Hv, dk, dv, qk_stride, v_stride, gb_stride, stash_seq_floats, _ptr(engaged_flag),
         _dtype_code(q), _dtype_code(out), _stream(stream)))
+    return last_route()
+
+
+def gdn_decode_verify(h_table, q, k, v, gate, beta, out, stash, B, Hk, Hv, dk, dv, k_rows,
+                      qk_stride, v_stride, gb_stride, stash_seq_floats, engaged_flag, stream=None):
+    _check(library().gdn_decode_verify(
+        _ptr(h_table), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(out), _ptr(stash),
+        B, Hk, Hv, dk, dv, k_rows, qk_stride, v_stride, gb_stride, stash_seq_floats,
+        _ptr(engaged_flag), _dtype_code(q), _dtype_code(out), _stream(stream)))
+    return last_route()
+
+
+def gdn_decode_step(h_table, q, k, v, gate, beta, out, B, Hk, Hv, dk, dv, qk_stride, v_stride,
+                    gb_stride, stream=None):
+    _check(library().gdn_decode_step(
+        _ptr(h_table), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(out), B, Hk, Hv,
+        dk, dv, qk_stride, v_stride, gb_stride, _dtype_code(q), _dtype_code(out), _stream(stream)))
     return last_route()
 
 

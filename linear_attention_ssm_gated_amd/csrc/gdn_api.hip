@@ -87,16 +87,19 @@ int check_verify(const gdn::VerifyArgs& a)
     if ((long)a.qk_stride < (long)a.Hk * a.dk || (long)a.v_stride < (long)a.Hv * a.dv ||
         (long)a.gb_stride < (long)a.Hv)
         return refuse(GDN_ERR_STRIDE, who, "a row stride is shorter than its row");
-    if ((size_t)a.stash_seq_floats < gdn_stash_seq_floats(a.Hv, a.dk, a.dv, 4, a.io_dtype))
+    if (a.k_rows < 1 || a.k_rows > gdn::kMaxVerifyRows)
+        return refuse(GDN_ERR_K_ROWS, who, "k_rows must be 1..8");
+    if ((size_t)a.stash_seq_floats < gdn_stash_seq_floats(a.Hv, a.dk, a.dv, a.k_rows, a.io_dtype))
         return refuse(GDN_ERR_STASH, who, "stash_seq_floats < gdn_stash_seq_floats()");
     return GDN_OK;
 }
 
-int check_fold(const gdn::FoldArgs& a, float* const* hi_tables, int k_rows)
+int check_fold(const gdn::FoldArgs& a, float* const* hi_tables)
 {
     const char* who = "gdn_fold";
     if (bad_dtype(a.io_dtype)) return refuse(GDN_ERR_DTYPE, who, "io_dtype must be GDN_F32 or GDN_BF16");
-    if (k_rows != 4) return refuse(GDN_ERR_K_ROWS, who, "k_rows must be 4");
+    if (a.k_rows < 1 || a.k_rows > gdn::kMaxVerifyRows)
+        return refuse(GDN_ERR_K_ROWS, who, "k_rows must be 1..8");
     if (hi_tables)
         return refuse(GDN_ERR_UNSUPPORTED, who, "the restore branch of a non-write-on-accept verify is not built; pass hi_tables = NULL");
     if (!a.h_table || !a.stash || !a.na_tab || !a.engaged_flag)
@@ -107,8 +110,27 @@ int check_fold(const gdn::FoldArgs& a, float* const* hi_tables, int k_rows)
     if (a.Hv % a.Hk != 0) return refuse(GDN_ERR_HEAD_GROUPS, who, "Hv must be a multiple of Hk");
     if (a.dk > 128 || a.dv > 128 || a.dv % 4 != 0)
         return refuse(GDN_ERR_DIM_LIMIT, who, "dk <= 128, dv <= 128 and dv a multiple of 4");
-    if ((size_t)a.stash_seq_floats < gdn_stash_seq_floats(a.Hv, a.dk, a.dv, 4, a.io_dtype))
+    if ((size_t)a.stash_seq_floats < gdn_stash_seq_floats(a.Hv, a.dk, a.dv, a.k_rows, a.io_dtype))
         return refuse(GDN_ERR_STASH, who, "stash_seq_floats < gdn_stash_seq_floats()");
+    return GDN_OK;
+}
+
+int check_step(const gdn::StepArgs& a)
+{
+    const char* who = "gdn_decode_step";
+    if (bad_dtype(a.io_dtype) || bad_dtype(a.out_dtype))
+        return refuse(GDN_ERR_DTYPE, who, "io_dtype/out_dtype must be GDN_F32 or GDN_BF16");
+    if (!a.h_table || !a.q || !a.k || !a.v || !a.gate || !a.beta || !a.out)
+        return refuse(GDN_ERR_NULL, who, "h_table, q, k, v, gate, beta and out are required");
+    if (a.B < 1 || a.Hk < 1 || a.Hv < 1 || a.dk < 1 || a.dv < 1)
+        return refuse(GDN_ERR_SHAPE, who, "need B, Hk, Hv, dk, dv >= 1");
+    if (a.B > 65535) return refuse(GDN_ERR_SHAPE, who, "B > 65535 (grid y limit)");
+    if (a.Hv % a.Hk != 0) return refuse(GDN_ERR_HEAD_GROUPS, who, "Hv must be a multiple of Hk");
+    if (a.dk > 128 || a.dv > 128 || a.dv % 4 != 0)
+        return refuse(GDN_ERR_DIM_LIMIT, who, "dk <= 128, dv <= 128 and dv a multiple of 4");
+    if ((long)a.qk_stride < (long)a.Hk * a.dk || (long)a.v_stride < (long)a.Hv * a.dv ||
+        (long)a.gb_stride < (long)a.Hv)
+        return refuse(GDN_ERR_STRIDE, who, "a row stride is shorter than its row");
     return GDN_OK;
 }
 
@@ -149,7 +171,7 @@ const char* gdn_status_string(int status)
     case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unknown dtype code";
     case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace too small";
     case GDN_ERR_STASH: return "GDN_ERR_STASH: stash_seq_floats too small";
-    case GDN_ERR_K_ROWS: return "GDN_ERR_K_ROWS: k_rows must be 4";
+    case GDN_ERR_K_ROWS: return "GDN_ERR_K_ROWS: k_rows must be 1..8";
     case GDN_ERR_STRIDE: return "GDN_ERR_STRIDE: a row stride is shorter than its row";
     case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: branch not built";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: the HIP runtime refused a launch";
@@ -205,8 +227,8 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* 
 
 size_t gdn_stash_seq_floats(int Hv, int dk, int dv, int k_rows, int io_dtype)
 {
-    if (Hv < 1 || dk < 1 || dv < 1 || k_rows != 4) return 0;
-    return (size_t)Hv * gdn::stash_head_floats(dk, dv, io_dtype == GDN_BF16 ? 1 : 0);
+    if (Hv < 1 || dk < 1 || dv < 1 || k_rows < 1 || k_rows > gdn::kMaxVerifyRows) return 0;
+    return (size_t)Hv * gdn::stash_head_floats(dk, dv, io_dtype == GDN_BF16 ? 1 : 0, k_rows);
 }
 
 int gdn_flag_clear(uint32_t* engaged_flag, hipStream_t stream)
@@ -218,11 +240,12 @@ int gdn_flag_clear(uint32_t* engaged_flag, hipStream_t stream)
 
 static gdn::VerifyArgs make_verify(float* const* h_table, const void* q, const void* k, const void* v,
                                    const float* gate, const float* beta, void* out, float* stash,
-                                   int B, int Hk, int Hv, int dk, int dv, int qk_stride,
-                                   int v_stride, int gb_stride, int stash_seq_floats,
+                                   int B, int Hk, int Hv, int dk, int dv, int k_rows,
+                                   int qk_stride, int v_stride, int gb_stride, int stash_seq_floats,
                                    uint32_t* engaged_flag, int io_dtype, int out_dtype)
 {
     gdn::VerifyArgs a;
+    a.k_rows = k_rows;
     a.h_table = h_table; a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta; a.out = out;
     a.stash = stash; a.B = B; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.qk_stride = qk_stride;
     a.v_stride = v_stride; a.gb_stride = gb_stride; a.stash_seq_floats = stash_seq_floats;
@@ -230,13 +253,13 @@ static gdn::VerifyArgs make_verify(float* const* h_table, const void* q, const v
     return a;
 }
 
-int gdn_decode_verify_k4_plan(float* const* h_table, const void* q, const void* k, const void* v,
-                              const float* gate, const float* beta, void* out, float* stash, int B,
-                              int Hk, int Hv, int dk, int dv, int qk_stride, int v_stride,
-                              int gb_stride, int stash_seq_floats, uint32_t* engaged_flag,
-                              int io_dtype, int out_dtype)
+int gdn_decode_verify_plan(float* const* h_table, const void* q, const void* k, const void* v,
+                           const float* gate, const float* beta, void* out, float* stash, int B,
+                           int Hk, int Hv, int dk, int dv, int k_rows, int qk_stride, int v_stride,
+                           int gb_stride, int stash_seq_floats, uint32_t* engaged_flag, int io_dtype,
+                           int out_dtype)
 {
-    gdn::VerifyArgs a = make_verify(h_table, q, k, v, gate, beta, out, stash, B, Hk, Hv, dk, dv,
+    gdn::VerifyArgs a = make_verify(h_table, q, k, v, gate, beta, out, stash, B, Hk, Hv, dk, dv, k_rows,
                                     qk_stride, v_stride, gb_stride, stash_seq_floats, engaged_flag,
                                     io_dtype, out_dtype);
     int st = check_verify(a);
@@ -245,13 +268,13 @@ int gdn_decode_verify_k4_plan(float* const* h_table, const void* q, const void* 
     return GDN_OK;
 }
 
-int gdn_decode_verify_k4(float* const* h_table, const void* q, const void* k, const void* v,
-                         const float* gate, const float* beta, void* out, float* stash, int B,
-                         int Hk, int Hv, int dk, int dv, int qk_stride, int v_stride, int gb_stride,
-                         int stash_seq_floats, uint32_t* engaged_flag, int io_dtype, int out_dtype,
-                         hipStream_t stream)
+int gdn_decode_verify(float* const* h_table, const void* q, const void* k, const void* v,
+                      const float* gate, const float* beta, void* out, float* stash, int B, int Hk,
+                      int Hv, int dk, int dv, int k_rows, int qk_stride, int v_stride, int gb_stride,
+                      int stash_seq_floats, uint32_t* engaged_flag, int io_dtype, int out_dtype,
+                      hipStream_t stream)
 {
-    gdn::VerifyArgs a = make_verify(h_table, q, k, v, gate, beta, out, stash, B, Hk, Hv, dk, dv,
+    gdn::VerifyArgs a = make_verify(h_table, q, k, v, gate, beta, out, stash, B, Hk, Hv, dk, dv, k_rows,
                                     qk_stride, v_stride, gb_stride, stash_seq_floats, engaged_flag,
                                     io_dtype, out_dtype);
     int st = check_verify(a);
@@ -260,11 +283,34 @@ int gdn_decode_verify_k4(float* const* h_table, const void* q, const void* k, co
     return launched(gdn::launch_verify(a, stream));
 }
 
+int gdn_decode_verify_k4_plan(float* const* h_table, const void* q, const void* k, const void* v,
+                              const float* gate, const float* beta, void* out, float* stash, int B,
+                              int Hk, int Hv, int dk, int dv, int qk_stride, int v_stride,
+                              int gb_stride, int stash_seq_floats, uint32_t* engaged_flag,
+                              int io_dtype, int out_dtype)
+{
+    return gdn_decode_verify_plan(h_table, q, k, v, gate, beta, out, stash, B, Hk, Hv, dk, dv, 4,
+                                  qk_stride, v_stride, gb_stride, stash_seq_floats, engaged_flag,
+                                  io_dtype, out_dtype);
+}
+
+int gdn_decode_verify_k4(float* const* h_table, const void* q, const void* k, const void* v,
+                         const float* gate, const float* beta, void* out, float* stash, int B,
+                         int Hk, int Hv, int dk, int dv, int qk_stride, int v_stride, int gb_stride,
+                         int stash_seq_floats, uint32_t* engaged_flag, int io_dtype, int out_dtype,
+                         hipStream_t stream)
+{
+    return gdn_decode_verify(h_table, q, k, v, gate, beta, out, stash, B, Hk, Hv, dk, dv, 4, qk_stride,
+                             v_stride, gb_stride, stash_seq_floats, engaged_flag, io_dtype, out_dtype,
+                             stream);
+}
+
 static gdn::FoldArgs make_fold(float* const* h_table, const float* stash, const int32_t* na_tab,
-                               const uint32_t* engaged_flag, int B, int Hk, int Hv, int dk, int dv,
-                               int stash_seq_floats, int io_dtype)
+                               const uint32_t* engaged_flag, int k_rows, int B, int Hk, int Hv,
+                               int dk, int dv, int stash_seq_floats, int io_dtype)
 {
     gdn::FoldArgs a;
+    a.k_rows = k_rows;
     a.h_table = h_table; a.stash = stash; a.na_tab = na_tab; a.engaged_flag = engaged_flag;
     a.B = B; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.stash_seq_floats = stash_seq_floats;
     a.io_dtype = io_dtype;
@@ -277,9 +323,9 @@ int gdn_fold_plan(float* const* h_table, const float* stash, const int32_t* na_t
                   int io_dtype)
 {
     (void)slab_entries;
-    gdn::FoldArgs a = make_fold(h_table, stash, na_tab, engaged_flag, B, Hk, Hv, dk, dv,
+    gdn::FoldArgs a = make_fold(h_table, stash, na_tab, engaged_flag, k_rows, B, Hk, Hv, dk, dv,
                                 stash_seq_floats, io_dtype);
-    int st = check_fold(a, hi_tables, k_rows);
+    int st = check_fold(a, hi_tables);
     if (st != GDN_OK) return st;
     route_geometry(gdn::fold_geometry(a), "");
     return GDN_OK;
@@ -291,12 +337,50 @@ int gdn_fold(float* const* h_table, const float* stash, const int32_t* na_tab,
              hipStream_t stream)
 {
     (void)slab_entries;
-    gdn::FoldArgs a = make_fold(h_table, stash, na_tab, engaged_flag, B, Hk, Hv, dk, dv,
+    gdn::FoldArgs a = make_fold(h_table, stash, na_tab, engaged_flag, k_rows, B, Hk, Hv, dk, dv,
                                 stash_seq_floats, io_dtype);
-    int st = check_fold(a, hi_tables, k_rows);
+    int st = check_fold(a, hi_tables);
     if (st != GDN_OK) return st;
     route_geometry(gdn::fold_geometry(a), "");
     return launched(gdn::launch_fold(a, stream));
+}
+
+static gdn::StepArgs make_step(float* const* h_table, const void* q, const void* k, const void* v,
+                               const float* gate, const float* beta, void* out, int B, int Hk, int Hv,
+                               int dk, int dv, int qk_stride, int v_stride, int gb_stride,
+                               int io_dtype, int out_dtype)
+{
+    gdn::StepArgs a;
+    a.h_table = h_table; a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta; a.out = out;
+    a.B = B; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.qk_stride = qk_stride;
+    a.v_stride = v_stride; a.gb_stride = gb_stride; a.io_dtype = io_dtype; a.out_dtype = out_dtype;
+    return a;
+}
+
+int gdn_decode_step_plan(float* const* h_table, const void* q, const void* k, const void* v,
+                         const float* gate, const float* beta, void* out, int B, int Hk, int Hv,
+                         int dk, int dv, int qk_stride, int v_stride, int gb_stride, int io_dtype,
+                         int out_dtype)
+{
+    gdn::StepArgs a = make_step(h_table, q, k, v, gate, beta, out, B, Hk, Hv, dk, dv, qk_stride,
+                                v_stride, gb_stride, io_dtype, out_dtype);
+    int st = check_step(a);
+    if (st != GDN_OK) return st;
+    route_geometry(gdn::step_geometry(a), "");
+    return GDN_OK;
+}
+
+int gdn_decode_step(float* const* h_table, const void* q, const void* k, const void* v,
+                    const float* gate, const float* beta, void* out, int B, int Hk, int Hv, int dk,
+                    int dv, int qk_stride, int v_stride, int gb_stride, int io_dtype, int out_dtype,
+                    hipStream_t stream)
+{
+    gdn::StepArgs a = make_step(h_table, q, k, v, gate, beta, out, B, Hk, Hv, dk, dv, qk_stride,
+                                v_stride, gb_stride, io_dtype, out_dtype);
+    int st = check_step(a);
+    if (st != GDN_OK) return st;
+    route_geometry(gdn::step_geometry(a), "");
+    return launched(gdn::launch_step(a, stream));
 }
 
 }  // extern "C"

@@ -38,6 +38,7 @@ struct VerifyArgs {
     int qk_stride, v_stride, gb_stride, stash_seq_floats;
     uint32_t* engaged_flag;
     int io_dtype, out_dtype;
+    int k_rows;
 };
 
 struct FoldArgs {
@@ -47,7 +48,23 @@ struct FoldArgs {
     const uint32_t* engaged_flag;
     int B, Hk, Hv, dk, dv, stash_seq_floats;
     int io_dtype;
+    int k_rows;
 };
+
+struct StepArgs {
+    float* const* h_table;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* gate;
+    const float* beta;
+    void* out;
+    int B, Hk, Hv, dk, dv;
+    int qk_stride, v_stride, gb_stride;
+    int io_dtype, out_dtype;
+};
+
+constexpr int kMaxVerifyRows = 8;   // draft rows a verify takes
 
 // Launch geometry a launcher reports for the route line.
 struct Geometry {
@@ -64,17 +81,22 @@ Geometry prefill_generic_geometry(const PrefillArgs& a);
 Geometry prefill_mfma_geometry(const PrefillArgs& a);
 Geometry verify_geometry(const VerifyArgs& a);
 Geometry fold_geometry(const FoldArgs& a);
+Geometry step_geometry(const StepArgs& a);
 Geometry flag_clear_geometry();
 
 hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
+hipError_t launch_step(const StepArgs& a, hipStream_t s);
 hipError_t launch_flag_clear(uint32_t* flag, hipStream_t s);
 
-// Per-v-head stash floats of the 4-row verify (delta, G, keys).
-__host__ __device__ inline size_t stash_head_floats(int dk, int dv, int io_dtype) {
-    return (size_t)4 * dv + 4 + (io_dtype == 1 ? (size_t)2 * dk : (size_t)4 * dk);
+// Per-v-head stash floats of a k_rows-row verify: delta [k_rows][dv] fp32,
+// G [k_rows] fp32, then the keys [k_rows][dk] as fp32 or as packed bf16 bits
+// (rounded up to whole floats).
+__host__ __device__ inline size_t stash_head_floats(int dk, int dv, int io_dtype, int k_rows) {
+    const size_t kd = (size_t)k_rows * dk;
+    return (size_t)k_rows * dv + k_rows + (io_dtype == 1 ? (kd + 1) / 2 : kd);
 }
 
 // ---- element helpers ------------------------------------------------------

@@ -80,6 +80,9 @@ WORKLOADS = {
         Workload("verify_k4_b16", "decode", B=16, T=4, Hk=16, Hv=48, dk=128, dv=128,
                  io=torch.bfloat16, h0=True, seed=1004, k_rows=4,
                  note="K=4 draft verify of 16 sequences, states behind a pointer table"),
+        Workload("step_b16", "decode_step", B=16, T=1, Hk=16, Hv=48, dk=128, dv=128,
+                 io=torch.bfloat16, h0=True, seed=1005, k_rows=1,
+                 note="single-token decode step of 16 sequences, states updated in place"),
     ]
 }
 

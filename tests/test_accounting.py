@@ -31,3 +31,11 @@ def test_verify_bytes():
 def test_fold_bytes():
     # two sequences folded (na = 1 and 4), one not (na = 0)
     assert bench.fold_bytes([0, 1, 4], 48, 128, 128) == 48 * (131072 + 1 * 768 + 16) + 48 * (131072 + 4 * 768 + 16)  # state 64 KiB read + write
+
+
+def test_step_bytes():
+    # 16 sequences x 48 v-heads: state 64 KiB read + write; one row of q, k (2 x 16 x 128 bf16),
+    # v (48 x 128 bf16), gate and beta (48 x 8 B); out (48 x 128 bf16)
+    b = bench.step_bytes(16, 16, 48, 128, 128)
+    assert b == 16 * 48 * 131072 + 16 * (8192 + 12288) + 16 * 384 + 16 * 12288
+    assert 101e6 < b < 101.3e6

@@ -1,4 +1,5 @@
-"""GPU parity and bookkeeping of the K = 4 write-on-accept verify and its fold.
+"""GPU parity and bookkeeping of the write-on-accept verify (K = 4, and any K in
+1..8), its fold, and the in-place K = 1 decode step.
 
 States sit in separately allocated slots, allocated in shuffled order and
 interleaved with spare slots that are not in the pointer table.  Checks:
@@ -11,7 +12,12 @@ interleaved with spare slots that are not in the pointer table.  Checks:
   * one-hot keys with no decay and beta = 1 make the accepted rows
     identifiable: exactly rows 0..na-1 of each state change, bit for bit;
   * with the word cleared (no verify since the clear) the fold changes nothing;
-  * repeated runs are bitwise identical.
+  * repeated runs are bitwise identical;
+  * K = 1..8 on both kernel paths: outputs and folded states against the
+    oracle, the stash padding untouched;
+  * the K = 1 step: outputs and updated states against the oracle, slots
+    outside the table untouched, and two steps in a row equal the oracle's
+    two-row chunk.
 """
 import numpy as np
 import pytest
@@ -32,6 +38,7 @@ class Setup:
         st = inp["states"]
         self.B, self.Hv, self.dk, self.dv = st.shape
         self.Hk = inp["q"].shape[2]
+        self.K = K = inp["q"].shape[1]
         B, Hv, dk, dv, Hk = self.B, self.Hv, self.dk, self.dv, self.Hk
         self.io = io
         # separately allocated states, in shuffled order, with spare slots between
@@ -59,6 +66,7 @@ class Setup:
         self.out = torch.empty((B, K, Hv, dv), dtype=out_dtype, device=d)
         self.io_code = gdn.GDN_BF16 if io == torch.bfloat16 else gdn.GDN_F32
         self.ssf = gdn.gdn_stash_seq_floats(Hv, dk, dv, K, self.io_code) + stash_pad
+        self.stash_pad = stash_pad
         self.stash = torch.full((B * self.ssf,), float("nan"), device=d)
         self.flag = torch.full((1,), 7, dtype=torch.int32, device=d)
         self.na = inp["na"].to(d)
@@ -70,14 +78,26 @@ class Setup:
         gdn.gdn_flag_clear(self.flag)
 
     def verify(self):
-        return gdn.gdn_decode_verify_k4(self.h_table, self.q, self.k, self.v, self.gate, self.beta,
-                                        self.out, self.stash, self.B, self.Hk, self.Hv, self.dk,
-                                        self.dv, self.qk_stride, self.v_stride, self.gb_stride,
-                                        self.ssf, self.flag)
+        if self.K == 4:   # the pages' entry point
+            return gdn.gdn_decode_verify_k4(self.h_table, self.q, self.k, self.v, self.gate, self.beta,
+                                            self.out, self.stash, self.B, self.Hk, self.Hv, self.dk,
+                                            self.dv, self.qk_stride, self.v_stride, self.gb_stride,
+                                            self.ssf, self.flag)
+        return gdn.gdn_decode_verify(self.h_table, self.q, self.k, self.v, self.gate, self.beta,
+                                     self.out, self.stash, self.B, self.Hk, self.Hv, self.dk, self.dv,
+                                     self.K, self.qk_stride, self.v_stride, self.gb_stride, self.ssf,
+                                     self.flag)
 
     def fold(self):
-        return gdn.gdn_fold(self.h_table, self.stash, self.na, None, 0, self.flag, K, self.B,
+        return gdn.gdn_fold(self.h_table, self.stash, self.na, None, 0, self.flag, self.K, self.B,
                             self.Hk, self.Hv, self.dk, self.dv, self.ssf, self.io_code)
+
+    def step(self):
+        """The K = 1 step on row 0 of each sequence (the rows are K = 1 rows)."""
+        assert self.K == 1
+        return gdn.gdn_decode_step(self.h_table, self.q, self.k, self.v, self.gate, self.beta,
+                                   self.out, self.B, self.Hk, self.Hv, self.dk, self.dv,
+                                   self.qk_stride, self.v_stride, self.gb_stride)
 
 
 def oracle_decode(inp):
@@ -102,7 +122,7 @@ def test_verify_fold_workload(io, out_dtype, tol, pad):
     assert int(s.flag.item()) == 0
     route = s.verify()
     torch.cuda.synchronize()
-    assert route.startswith("gdn_verify_k4_d128_kernel grid=[48,16,1]"), route
+    assert route.startswith("gdn_verify_d128_kernel grid=[48,16,1]"), route
     assert int(s.flag.item()) == 1, "verify marks the engaged word"
     assert torch.equal(s.states(), before), "verify writes no state"
     ro, after = oracle_decode(inp)
@@ -131,7 +151,7 @@ def test_d128_shapes_and_stash_bounds(B, Hk, Hv):
     s.clear()
     route = s.verify()
     torch.cuda.synchronize()
-    assert route.startswith(f"gdn_verify_k4_d128_kernel grid=[{Hv},{B},1]"), route
+    assert route.startswith(f"gdn_verify_d128_kernel grid=[{Hv},{B},1]"), route
     stash = s.stash.view(B, s.ssf).cpu()
     assert torch.isnan(stash[:, s.ssf - 16:]).all(), "the stash padding must stay untouched"
     ro, after = oracle_decode(inp)
@@ -156,7 +176,7 @@ def test_generic_shapes(dk, dv):
     before = s.states()
     s.clear()
     route = s.verify()
-    assert route.startswith("gdn_verify_k4_kernel "), route
+    assert route.startswith("gdn_verify_kernel "), route
     s.fold()
     torch.cuda.synchronize()
     ro, after = oracle_decode(inp)
@@ -226,3 +246,116 @@ def test_verify_fold_deterministic():
     for a, b in zip(res[0], res[1]):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+def check_verify_fold(inp, s, route_prefix, out_tol):
+    B = s.B
+    before = s.states()
+    spares_before = [x.cpu() for x in s.spares]
+    s.clear()
+    route = s.verify()
+    torch.cuda.synchronize()
+    assert route.startswith(route_prefix), route
+    assert int(s.flag.item()) == 1
+    assert torch.equal(s.states(), before), "verify writes no state"
+    if s.stash_pad:
+        pad = s.stash.view(B, s.ssf).cpu()[:, s.ssf - s.stash_pad:]
+        assert torch.isnan(pad).all(), "the stash padding must stay untouched"
+    ro, after = oracle_decode(inp)
+    assert rel_err(s.out, ro) <= out_tol
+    s.fold()
+    torch.cuda.synchronize()
+    got = s.states()
+    for b in range(B):
+        na = int(inp["na"][b])
+        if na == 0:
+            assert torch.equal(got[b], before[b]), b
+        else:
+            assert rel_err(got[b], after[b, na]) <= 1e-4, (b, na)
+    for x, y in zip(s.spares, spares_before):
+        assert torch.equal(x.cpu(), y)
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 5, 8])
+def test_verify_fold_any_rows_d128(K):
+    inp = synth.decode_inputs(6, K, 2, 6, 128, 128, io=torch.bfloat16, seed=300 + K)
+    say("verify rows d128", K)
+    s = Setup(inp, torch.bfloat16, torch.float32, qk_pad=8, stash_pad=16)
+    check_verify_fold(inp, s, "gdn_verify_d128_kernel grid=[6,6,1]", 1e-4)
+
+
+@pytest.mark.parametrize("K,io", [(1, torch.float32), (3, torch.bfloat16), (8, torch.float32)])
+def test_verify_fold_any_rows_generic(K, io):
+    inp = synth.decode_inputs(5, K, 1, 3, 64, 96, io=io, seed=320 + K)
+    say("verify rows generic", K, io)
+    s = Setup(inp, io, torch.float32, qk_pad=4, stash_pad=8)
+    check_verify_fold(inp, s, "gdn_verify_kernel grid=[3,5,1]", 1e-4)
+
+
+def test_verify_rows8_d128_bf16_out():
+    inp = synth.decode_inputs(16, 8, 16, 48, 128, 128, io=torch.bfloat16, seed=341)
+    say("verify rows d128 K=8 full heads")
+    s = Setup(inp, torch.bfloat16, torch.bfloat16)
+    check_verify_fold(inp, s, "gdn_verify_d128_kernel grid=[48,16,1]", 4e-3)
+
+
+def check_step(inp, s, route_prefix, out_tol):
+    spares_before = [x.cpu() for x in s.spares]
+    route = s.step()
+    torch.cuda.synchronize()
+    assert route.startswith(route_prefix), route
+    ro, after = oracle_decode(inp)
+    assert rel_err(s.out[:, 0], ro[:, 0]) <= out_tol
+    got = s.states()
+    for b in range(s.B):
+        assert rel_err(got[b], after[b, 1]) <= 1e-4, b
+    for x, y in zip(s.spares, spares_before):
+        assert torch.equal(x.cpu(), y), "a slot outside the table changed"
+
+
+@pytest.mark.parametrize("io,out_dtype,tol", [
+    (torch.bfloat16, torch.float32, 1e-4),
+    (torch.bfloat16, torch.bfloat16, 4e-3),
+    (torch.float32, torch.float32, 1e-4),
+])
+def test_step_d128(io, out_dtype, tol):
+    inp = synth.decode_inputs(16, 1, 16, 48, 128, 128, io=io, seed=360)
+    say("step d128", io, out_dtype)
+    s = Setup(inp, io, out_dtype, qk_pad=8)
+    check_step(inp, s, "gdn_step_d128_kernel grid=[48,16,1]", tol)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 96), (128, 64), (33, 128)])
+def test_step_generic(dk, dv):
+    inp = synth.decode_inputs(5, 1, 2, 4, dk, dv, io=torch.bfloat16, seed=370 + dk + dv)
+    say("step generic", dk, dv)
+    s = Setup(inp, torch.bfloat16, torch.float32, qk_pad=2)
+    check_step(inp, s, "gdn_step_kernel grid=[4,5,1]", 1e-4)
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_two_steps_equal_the_two_row_chunk(dk):
+    """Two K = 1 steps on rows 0 and 1 give the oracle's outputs and state
+    after both rows of the same two-row chunk."""
+    inp2 = synth.decode_inputs(4, 2, 1, 3, dk, dk, io=torch.bfloat16, seed=380 + dk)
+    say("two steps", dk)
+    ro, after = oracle_decode(inp2)
+    rows = []
+    for r in range(2):
+        inp1 = dict(inp2)
+        for name in ("q", "k", "v", "gate", "beta"):
+            inp1[name] = inp2[name][:, r:r + 1]
+        rows.append(inp1)
+    s = Setup(rows[0], torch.bfloat16, torch.float32)
+    s.step()
+    out0 = s.out.clone()
+    s1 = Setup(rows[1], torch.bfloat16, torch.float32)
+    # the second step runs on the states the first one left
+    s1.slots, s1.h_table = s.slots, s.h_table
+    s1.step()
+    torch.cuda.synchronize()
+    assert rel_err(out0[:, 0], ro[:, 0]) <= 1e-4
+    assert rel_err(s1.out[:, 0], ro[:, 1]) <= 1e-4
+    got = torch.stack([x for x in s.slots]).cpu()
+    for b in range(4):
+        assert rel_err(got[b], after[b, 2]) <= 1e-4, b

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in gdn.h but not exported"
     assert set(names) == set(gdn.SIGNATURES), "binding and header disagree"
@@ -105,10 +105,14 @@ def test_workspace_and_stash_sizes(lib):
     # generic route needs none
     assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 128, 128, 64, 0) == 0
     assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 64, 64, 64, 1) == 0
-    # per v-head: delta 4*dv, G 4, keys 4*dk bf16 (2*dk floats) or fp32 (4*dk floats)
+    # per v-head: delta K*dv, G K, keys K*dk bf16 (ceil(K*dk/2) floats) or fp32 (K*dk floats)
     assert gdn.gdn_stash_seq_floats(48, 128, 128, 4, 1) == 48 * (4 * 128 + 4 + 2 * 128)
     assert gdn.gdn_stash_seq_floats(48, 128, 128, 4, 0) == 48 * (4 * 128 + 4 + 4 * 128)
-    assert gdn.gdn_stash_seq_floats(48, 128, 128, 3, 1) == 0
+    assert gdn.gdn_stash_seq_floats(48, 128, 128, 3, 1) == 48 * (3 * 128 + 3 + 192)
+    assert gdn.gdn_stash_seq_floats(2, 33, 64, 1, 1) == 2 * (64 + 1 + 17)
+    assert gdn.gdn_stash_seq_floats(2, 33, 64, 8, 0) == 2 * (8 * 64 + 8 + 8 * 33)
+    assert gdn.gdn_stash_seq_floats(48, 128, 128, 0, 1) == 0
+    assert gdn.gdn_stash_seq_floats(48, 128, 128, 9, 1) == 0
 
 
 def verify_plan(lib, **kw):
@@ -124,9 +128,37 @@ def verify_plan(lib, **kw):
 def test_verify_plan(lib):
     assert verify_plan(lib) == 0
     r = gdn.last_route()
-    assert r.startswith("gdn_verify_k4_d128_kernel grid=[48,16,1] block=256"), r
+    assert r.startswith("gdn_verify_d128_kernel grid=[48,16,1] block=256 lds=32416B"), r
     assert verify_plan(lib, dk=64, dv=64, qks=16 * 64, vs=48 * 64, ssf=48 * (256 + 4 + 128)) == 0
-    assert gdn.last_route().startswith("gdn_verify_k4_kernel grid=[48,16,1]")
+    assert gdn.last_route().startswith("gdn_verify_kernel grid=[48,16,1]")
+
+
+def verify_rows_plan(lib, k_rows, **kw):
+    a = dict(ht=X, q=X, k=X, v=X, gate=X, beta=X, out=X, stash=X, B=16, Hk=16, Hv=48, dk=128,
+             dv=128, qks=16 * 128, vs=48 * 128, gbs=48, flag=X, io=1, od=1)
+    a.update(kw)
+    ssf = a.pop("ssf", gdn.gdn_stash_seq_floats(a["Hv"], a["dk"], a["dv"], max(1, min(k_rows, 8)), a["io"]))
+    return lib.gdn_decode_verify_plan(a["ht"], a["q"], a["k"], a["v"], a["gate"], a["beta"], a["out"],
+                                      a["stash"], a["B"], a["Hk"], a["Hv"], a["dk"], a["dv"], k_rows,
+                                      a["qks"], a["vs"], a["gbs"], ssf, a["flag"], a["io"], a["od"])
+
+
+@pytest.mark.parametrize("k_rows", [1, 2, 3, 5, 8])
+def test_verify_any_rows_plan(lib, k_rows):
+    assert verify_rows_plan(lib, k_rows) == 0
+    assert gdn.last_route().startswith("gdn_verify_d128_kernel grid=[48,16,1] block=256")
+    assert verify_rows_plan(lib, k_rows, dk=64, dv=96, qks=16 * 64, vs=48 * 96) == 0
+    assert gdn.last_route().startswith("gdn_verify_kernel grid=[48,16,1]")
+    # a stash sized for fewer rows is refused
+    if k_rows > 1:
+        small = gdn.gdn_stash_seq_floats(48, 128, 128, k_rows - 1, 1)
+        assert verify_rows_plan(lib, k_rows, ssf=small) == 7
+
+
+@pytest.mark.parametrize("k_rows", [0, 9, -1])
+def test_verify_rows_refused(lib, k_rows):
+    assert verify_rows_plan(lib, k_rows, ssf=1 << 20) == 8
+    assert "k_rows must be 1..8" in gdn.last_route()
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -150,15 +182,46 @@ def fold_plan(lib, **kw):
 
 def test_fold_plan(lib):
     assert fold_plan(lib) == 0
-    assert gdn.last_route().startswith("gdn_fold_k4_d128_kernel grid=[48,16,1] block=256")
+    assert gdn.last_route().startswith("gdn_fold_d128_kernel grid=[48,16,1] block=256")
+    for k_rows in (1, 3, 8):
+        ssf = gdn.gdn_stash_seq_floats(48, 128, 128, k_rows, 1)
+        assert fold_plan(lib, k_rows=k_rows, ssf=ssf) == 0
+    assert fold_plan(lib, dk=64, dv=64, ssf=48 * (256 + 4 + 128)) == 0
+    assert gdn.last_route().startswith("gdn_fold_kernel grid=[48,16,1]")
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(k_rows=3), 8), (dict(hi=X), 10), (dict(na=None), 1), (dict(ht=None), 1),
+    (dict(k_rows=0), 8), (dict(k_rows=9), 8), (dict(k_rows=5), 7), (dict(hi=X), 10), (dict(na=None), 1), (dict(ht=None), 1),
     (dict(ssf=10), 7), (dict(Hv=47), 3), (dict(io=9), 5),
 ])
 def test_fold_refusals(lib, kw, status):
     assert fold_plan(lib, **kw) == status
+    assert "refused" in gdn.last_route()
+
+
+def step_plan(lib, **kw):
+    a = dict(ht=X, q=X, k=X, v=X, gate=X, beta=X, out=X, B=16, Hk=16, Hv=48, dk=128, dv=128,
+             qks=16 * 128, vs=48 * 128, gbs=48, io=1, od=1)
+    a.update(kw)
+    return lib.gdn_decode_step_plan(a["ht"], a["q"], a["k"], a["v"], a["gate"], a["beta"], a["out"],
+                                    a["B"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["qks"], a["vs"],
+                                    a["gbs"], a["io"], a["od"])
+
+
+def test_step_plan(lib):
+    assert step_plan(lib) == 0
+    assert gdn.last_route().startswith("gdn_step_d128_kernel grid=[48,16,1] block=256")
+    assert step_plan(lib, dk=32, dv=96, qks=16 * 32, vs=48 * 96) == 0
+    assert gdn.last_route().startswith("gdn_step_kernel grid=[48,16,1] block=256")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ht=None), 1), (dict(out=None), 1), (dict(gate=None), 1), (dict(B=0), 2),
+    (dict(B=70000), 2), (dict(Hk=7), 3), (dict(dk=129), 4), (dict(dv=126), 4),
+    (dict(qks=100), 9), (dict(gbs=47), 9), (dict(io=2), 5), (dict(od=7), 5),
+])
+def test_step_refusals(lib, kw, status):
+    assert step_plan(lib, **kw) == status
     assert "refused" in gdn.last_route()
 
 
