@@ -265,6 +265,11 @@ def bench_verify(w, args, torch):
     total_ms, kern_ms, eager_ms = time_launches(launch, n_sets, args.warmup, args.steps, torch)
     ms = total_ms / args.steps
     ach = byt / (kern_ms * 1e-3) / 1e9
+    # parity of the timed launches' outputs (the verify writes no state, so every
+    # set's outputs are those of the oracle on the same inputs)
+    import oracle
+    ro, _ = oracle.decode(inp["states"], inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"])
+    err = synth.max_rel_err(sets[(args.steps - 1) % n_sets]["out"].float().cpu(), ro)
     # the fold that follows a verify (word set by the verify above), on the same sets
     na_l = inp["na"].tolist()
     for g in sets:
@@ -288,6 +293,7 @@ def bench_verify(w, args, torch):
                      "algorithmic_bytes": byt, "kernel_ms": kern_ms, "eager_launch_ms": eager_ms},
         "timing": "HIP events around one replay of a graph of the K launches",
         "draft_tokens_per_s": w.B * K / (kern_ms * 1e-3),
+        "parity_max_rel_err_out": err,
         "fold": {"kernel_ms": fold_ms, "eager_launch_ms": fold_eager_ms, "algorithmic_bytes": fbyt, "achieved": fbyt / (fold_ms * 1e-3) / 1e9,
                  "unit": "GB/s", "frac": fbyt / (fold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "na": na_l},
         "route": route[0] if route else None,
@@ -322,6 +328,13 @@ def bench_step(w, args, torch):
         if not route:
             route.append(r)
 
+    # parity of one step on fresh states (before the timed launches move them on)
+    import oracle
+    launch(0)
+    torch.cuda.synchronize()
+    ro, after = oracle.decode(inp["states"], inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"])
+    err_out = synth.max_rel_err(sets[0]["out"].float().cpu(), ro[:, 0])
+    err_state = max(synth.max_rel_err(sets[0]["slots"][b].cpu(), after[b, 1]) for b in range(w.B))
     total_ms, kern_ms, eager_ms = time_launches(launch, n_sets, args.warmup, args.steps, torch)
     ach = byt / (kern_ms * 1e-3) / 1e9
     return {
@@ -335,6 +348,7 @@ def bench_step(w, args, torch):
                      "algorithmic_bytes": byt, "kernel_ms": kern_ms, "eager_launch_ms": eager_ms},
         "timing": "HIP events around one replay of a graph of the K launches",
         "tokens_per_s": w.B / (kern_ms * 1e-3),
+        "parity_max_rel_err_out": err_out, "parity_max_rel_err_state": err_state,
         "route": route[0] if route else None,
         "input_sets_rotated": n_sets,
     }

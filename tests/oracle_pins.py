@@ -24,6 +24,9 @@ What pins what:
   empty              T = 0 leaves h0 unchanged
   decode             the K=4 verify/fold algebra (4x4 UT solve, fold of the first
                      na rows) in numpy equals the oracle's per-prefix states
+  decode_rows        for K = 1, 2, 5, 8 rows, the oracle's outputs and per-prefix
+                     states equal the token recurrence S <- a S (I - b k k^T) + b v k^T,
+                     o = S q, applied row by row (the K = 1 step is its first row)
 """
 from __future__ import annotations
 
@@ -343,6 +346,28 @@ def pin_decode(lib=None):
             assert np.array_equal(after[b, 0, vh], states[b, vh]), "na = 0 is the untouched state"
 
 
+def pin_decode_rows(lib=None):
+    for K in (1, 2, 5, 8):
+        rng = _rng(40 + K)
+        B, Hk, Hv, dk, dv = 2, 1, 3, 7, 4
+        states = rng.standard_normal((B, Hv, dk, dv)) * 0.3
+        q = _unit(rng, (B, K, Hk, dk))
+        k = _unit(rng, (B, K, Hk, dk))
+        v = rng.standard_normal((B, K, Hv, dv))
+        gate = -np.logaddexp(0.0, rng.standard_normal((B, K, Hv))) * 0.3
+        beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, K, Hv))))
+        out, after = oracle.decode(states, q, k, v, gate, beta, lib=lib)
+        for b in range(B):
+            for vh in range(Hv):
+                S = states[b, vh].T.copy()   # S is dv x dk; the state h = S^T
+                for r in range(K):
+                    kt = k[b, r, 0][:, None]
+                    S = np.exp(gate[b, r, vh]) * S @ (np.eye(dk) - beta[b, r, vh] * kt @ kt.T) \
+                        + beta[b, r, vh] * v[b, r, vh][:, None] @ kt.T
+                    _close(out[b, r, vh], S @ q[b, r, 0], 1e-12, f"K={K} row {r} output")
+                    _close(after[b, r + 1, vh], S.T, 1e-12, f"K={K} state after {r + 1} rows")
+
+
 ALL_PINS = [pin_scalar_golden, pin_matrix_form, pin_chunked_form, pin_pure_decay, pin_overwrite,
             pin_state_carry, pin_linearity, pin_contraction, pin_packed, pin_head_grouping,
-            pin_heads_subset, pin_empty, pin_decode]
+            pin_heads_subset, pin_empty, pin_decode, pin_decode_rows]
