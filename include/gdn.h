@@ -97,9 +97,11 @@ const char* gdn_last_route(void);
  * gdn_last_route() names the one that ran.
  * workspace: device scratch of at least gdn_prefill_workspace_bytes() bytes
  * (may be NULL when that is 0), asked with the same B, T, shapes and io_dtype,
- * and packed = (cu_seqlens != NULL).  The MFMA route keeps T = (I + A)^-1 and
- * P = lower_incl(Gamma o Q K^T) of every (chunk, v-head) there as bf16 (16 KiB
- * each) plus a chunk table of packed sequences; the generic route needs none.
+ * and packed = (cu_seqlens != NULL).  The MFMA route keeps a chunk table of
+ * packed sequences, T = (I + A)^-1 of every (chunk, v-head) and
+ * S = lower_incl(Q K^T) of every (chunk, k-head) there, as 64 x 64 bf16
+ * matrices (8 KiB each; the granules above their diagonals are never written
+ * or read); the generic route needs none.
  * The library reads and writes the workspace only inside the call's stream
  * order; its contents need no initialisation.
  */

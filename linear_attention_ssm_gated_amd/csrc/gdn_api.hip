@@ -188,7 +188,7 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv,
     gdn::PrefillArgs a{};
     a.io_dtype = io_dtype; a.dk = dk; a.dv = dv; a.chunk = chunk;
     if (!gdn::prefill_mfma_accepts(a)) return 0;  // the generic kernel keeps everything in LDS
-    return gdn::prefill_mfma_workspace_bytes(B, T, Hv, packed != 0);
+    return gdn::prefill_mfma_workspace_bytes(B, T, Hk, Hv, packed != 0);
 }
 
 int gdn_chunk_prefill_plan(const void* q, const void* k, const void* v, const float* log_g,

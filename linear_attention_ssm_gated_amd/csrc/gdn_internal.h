@@ -76,7 +76,7 @@ struct Geometry {
 
 // Kernel choice and geometry of a prefill call (no launch).
 bool prefill_mfma_accepts(const PrefillArgs& a);
-size_t prefill_mfma_workspace_bytes(int B, int T, int Hv, bool packed);
+size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv, bool packed);
 Geometry prefill_generic_geometry(const PrefillArgs& a);
 Geometry prefill_mfma_geometry(const PrefillArgs& a);
 Geometry verify_geometry(const VerifyArgs& a);

@@ -2,15 +2,19 @@
 //
 // Two kernels on the caller's stream:
 //
-// gdn_wy_prep_kernel, one workgroup per (chunk, v-head), all chunks at once:
+// gdn_wy_prep_kernel, one workgroup per (chunk, k-head), all chunks at once:
 //   the intra-chunk terms that do not depend on the state (the pages' W/U
 //   producer behind the spine, ssm_gdn_tc_route.rs, doc of the pipe spine):
 //     G = cumsum(log_g), Gamma_rs = exp(G_r - G_s) for s <= r
-//     A = strict_lower(diag(beta) (Gamma o K K^T)),  T = (I + A)^-1
-//     P = lower_incl(Gamma o Q K^T)
+//     A = strict_lower(diag(beta) (Gamma o K K^T)),  T = (I + A)^-1   (per v-head)
+//     S = lower_incl(Q K^T)                                            (per k-head)
 //   K K^T and Q K^T run on bf16 MFMA with fp32 accumulation; T is solved in
 //   fp32 (16x16 diagonal blocks by forward substitution on VALU, the blocks
-//   below them on fp32 MFMA); T and P are stored as bf16 in the workspace.
+//   below them on fp32 MFMA); T and S are stored as bf16 in the workspace,
+//   their granules above the diagonal left unwritten (they are zero, and the
+//   spine never reads them from memory).  The output's decay-weighted
+//   P = Gamma o S is never formed: Gamma_rs = gm_r / gm_s with gm = exp(G)
+//   factors out of the product (see the spine).
 //
 // gdn_spine_kernel, one workgroup per (sequence, v-head, 32 dv columns), two
 //   waves of 16 columns each, walking the chunks in order: the state spine
@@ -19,8 +23,9 @@
 //     X = K h, Y = Q h                       (state as the bf16 B operand)
 //     R = diag(beta) (V - diag(gamma) X)
 //     Delta = T R                            (= U - W h of the WY form)
-//     O = diag(gamma) Y + P Delta
-//     h <- gamma_L h + K^T diag(exp(G_L - G)) Delta
+//     O = diag(gamma) Y + (Gamma o S) Delta
+//       = diag(gamma / gamma_L) (gamma_L Y + S (el o Delta)),  el = exp(G_L - G)
+//     h <- gamma_L h + K^T (el o Delta)
 //   Columns of h evolve independently (the dv split of the pages' SPLIT
 //   variants), so the waves never exchange data.
 //
@@ -41,7 +46,7 @@ constexpr int C = 64;        // chunk rows
 constexpr int D = 128;       // dk = dv
 constexpr int TILE_COLS = 32;            // dv columns per spine workgroup
 constexpr int N_TILES = D / TILE_COLS;   // 4
-constexpr int SLOT_ELEMS = 2 * C * C;    // T then P, bf16, per (chunk, v-head)
+constexpr int SLOT_ELEMS = C * C;        // one 64 x 64 bf16 matrix: T per (chunk, v-head), S per (chunk, k-head)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -184,10 +189,11 @@ __device__ __forceinline__ s16x8 lds_read16(const unsigned char* p) {
 // WY prep: one workgroup per (chunk, k-head, group of up to four of its
 // v-heads), one wave per v-head.  The workgroup stages the chunk's K and Q
 // rows in LDS once; each wave then forms, for its v-head,
-//   A = strict_lower(beta_r exp(G_r - G_s) (K K^T)_rs),
-//   P = lower_incl(exp(G_r - G_s) (Q K^T)_rs),   T = (I + A)^-1,
-// and writes T and P as bf16 64 x 64 row-major matrices to the chunk's slot.
-// The waves never wait for each other after the staging.
+//   A = strict_lower(beta_r exp(G_r - G_s) (K K^T)_rs),   T = (I + A)^-1,
+// and writes T as a bf16 64 x 64 row-major matrix to the (chunk, v-head)
+// slot.  The k-head's S = lower_incl(Q K^T) (no decay) is written once, its
+// ten 16 x 16 tiles shared out over the first group's waves.  The waves never
+// wait for each other after the staging.
 //
 // Gram tiles are formed above the diagonal, tile (m, i) = K_m K_i^T and
 // K_m Q_i^T (16-row blocks, m <= i), so that lane (g, n) register s holds
@@ -242,9 +248,9 @@ extern __shared__ __attribute__((aligned(1024))) float prep_lds[];
 __global__ void __launch_bounds__(256, 3)
 gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const float* __restrict__ log_g, const float* __restrict__ beta,
-                   uint16_t* __restrict__ slots, int B, int T, int Hk, int Hv,
-                   const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_base,
-                   int nc_dense)
+                   uint16_t* __restrict__ tslots, uint16_t* __restrict__ sslots, int B, int T,
+                   int Hk, int Hv, const int32_t* __restrict__ cu,
+                   const int32_t* __restrict__ chunk_base, int nc_dense)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), nw = blockDim.x >> 6;
@@ -321,10 +327,13 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         Gc[i] = f32x4{t4.x, t4.y, t4.z, t4.w};
     }
 
-    // Gram tiles by block column i: P leaves at once, A stays in registers
-    uint16_t* dstT = slots + ((size_t)x * Hv + vh) * SLOT_ELEMS;
-    uint16_t* dstP = dstT + C * C;
+    // Gram tiles by block column i: S tiles leave at once, A stays in
+    // registers.  S tile number i (i + 1) / 2 + m belongs to wave (that
+    // number) % nw of the first group.
+    uint16_t* dstT = tslots + ((size_t)x * Hv + vh) * SLOT_ELEMS;
+    uint16_t* dstS = sslots + ((size_t)x * Hk + kh) * SLOT_ELEMS;
     const bool live = h < G;
+    const bool s_group = blockIdx.z == 0;
     s16x8 kf[4][4];
     f32x4 Aoff[6];   // A_im, m < i, index (i - 1) i / 2 + m
     f32x4 Adg[4];    // A_ii: register s = A_ii[n][4g + s]
@@ -339,31 +348,32 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
 #pragma unroll
         for (int m = 0; m <= i; ++m) {
+            const bool mine = s_group && ((i * (i + 1) / 2 + m) % nw) == w;   // wave-uniform
             f32x4 kk_acc = zero4(), kq_acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                kk_acc = mfma_bf16(kf[m][kk], kf[i][kk], kk_acc);
-                kq_acc = mfma_bf16(kf[m][kk], qf[kk], kq_acc);
+            for (int kk = 0; kk < 4; ++kk) kk_acc = mfma_bf16(kf[m][kk], kf[i][kk], kk_acc);
+            if (mine) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) kq_acc = mfma_bf16(kf[m][kk], qf[kk], kq_acc);
             }
-            f32x4 av, pv;
+            f32x4 av, sv;
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
                 const float e = __builtin_amdgcn_exp2f(Gr[i] - Gc[m][s2]);
                 av[s2] = Bt[i] * e * kk_acc[s2];
-                pv[s2] = e * kq_acc[s2];
-                if (m == i) {   // A strictly lower, P lower with the diagonal
+                sv[s2] = kq_acc[s2];
+                if (m == i) {   // A strictly lower, S lower with the diagonal
                     av[s2] = (n > 4 * g + s2) ? av[s2] : 0.f;
-                    pv[s2] = (n >= 4 * g + s2) ? pv[s2] : 0.f;
+                    sv[s2] = (n >= 4 * g + s2) ? sv[s2] : 0.f;
                 }
             }
             if (m == i) Adg[i] = av;
             else Aoff[(i - 1) * i / 2 + m] = av;
-            const s16x4 pb = s16x4{bf16_bits(pv[0]), bf16_bits(pv[1]), bf16_bits(pv[2]), bf16_bits(pv[3])};
-            if (live) *reinterpret_cast<s16x4*>(dstP + (16 * i + n) * C + 16 * m + 4 * g) = pb;
+            if (mine) {
+                const s16x4 sb = s16x4{bf16_bits(sv[0]), bf16_bits(sv[1]), bf16_bits(sv[2]), bf16_bits(sv[3])};
+                *reinterpret_cast<s16x4*>(dstS + (16 * i + n) * C + 16 * m + 4 * g) = sb;
+            }
         }
-#pragma unroll
-        for (int m = i + 1; m < 4; ++m)   // above the diagonal
-            if (live) *reinterpret_cast<s16x4*>(dstP + (16 * i + n) * C + 16 * m + 4 * g) = s16x4{0, 0, 0, 0};
     }
     __syncthreads();      // the staging area becomes the waves' own regions
     if (!live) return;    // a partial last group of v-heads
@@ -443,22 +453,22 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         wave_lds_sync();
     }
 
-    // T rows -> workspace as bf16 (tiles above the diagonal are zero)
+    // T rows -> workspace as bf16: the 8-column granules that reach the
+    // diagonal (8 cg <= r); those wholly above it are zero and not written
     const int cg = lane & 7, jb = cg >> 1;
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         const int r = (lane >> 3) + 8 * p, ib = p >> 1, rr = r & 15;
-        s16x8 v = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        if (jb <= ib) {
+        if (8 * cg <= r) {
             const float* blk = lds + (jb == ib ? 272 * ib : 1088 + 256 * ((ib - 1) * ib / 2 + jb));
             const int c0 = 2 * (cg & 1);   // first 4-column granule
             const float* row = blk + 16 * prow(rr);
             const float4 a = *reinterpret_cast<const float4*>(row + 4 * (c0 ^ (rr >> 2)));
             const float4 e = *reinterpret_cast<const float4*>(row + 4 * ((c0 + 1) ^ (rr >> 2)));
-            v = s16x8{bf16_bits(a.x), bf16_bits(a.y), bf16_bits(a.z), bf16_bits(a.w),
+            *reinterpret_cast<s16x8*>(dstT + r * C + 8 * cg) =
+                s16x8{bf16_bits(a.x), bf16_bits(a.y), bf16_bits(a.z), bf16_bits(a.w),
                       bf16_bits(e.x), bf16_bits(e.y), bf16_bits(e.z), bf16_bits(e.w)};
         }
-        *reinterpret_cast<s16x8*>(dstT + r * C + 8 * cg) = v;
     }
 }
 
@@ -468,16 +478,19 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 //   recurrence waves (2, 3): each owns 16 columns of the state h in MFMA
 //     accumulators and walks the chunks in order: X = K h,
 //     R = beta (V - gm X), Delta = T R, h <- gamma_L h + K^T (el Delta).
-//     It hands the chunk's bf16 state (before the update) and Delta to its
-//     output wave through a double-buffered LDS exchange.
-//   output waves (0, 1): one chunk behind, O = gm (Q h) + P Delta for the
-//     same 16 columns.  The output path does not feed back into the state,
-//     so it leaves the recurrence waves' critical path.
+//     It hands the chunk's bf16 state (before the update) and el Delta to
+//     its output wave through a double-buffered LDS exchange.
+//   output waves (0, 1): one chunk behind, O = (gm / gm_L) (gm_L (Q h) +
+//     S (el Delta)) for the same 16 columns, which is gm (Q h) + (Gamma o S)
+//     Delta because Gamma_rs = gm_r / gm_s and el_s = gm_L / gm_s.  The
+//     output path does not feed back into the state, so it leaves the
+//     recurrence waves' critical path.
 //   loader waves (4, 5): fill the recurrence waves' three-stage LDS ring two
-//     chunks ahead, and the output waves' two-slot ring of Q and P one
+//     chunks ahead, and the output waves' two-slot ring of Q and S one
 //     chunk ahead, by buffer->LDS DMA (a 64-lane DMA writes lane l's 16 bytes
 //     at base + 16 l; lanes beyond the buffer's range write zeros, which pads
-//     a partial chunk), and prepare the chunk's decay factors.
+//     a partial chunk and fills the granules of T and S above the diagonal,
+//     which are not in memory), and prepare the chunk's decay factors.
 // All six waves meet at one barrier per chunk.
 //
 // MFMA k-slots.  Lane group g (lanes 16g .. 16g+15) supplies k-values
@@ -507,19 +520,19 @@ constexpr int ST_EL = 29440;
 constexpr int ST_SO = 29696;
 constexpr int ST_BYTES = 29712;
 constexpr int N_STAGES = 3;
-constexpr int DMA_K_WAVE = 17;    // loader 0: 16 K + 1 log_g (then 8 P for the output ring)
+constexpr int DMA_K_WAVE = 17;    // loader 0: 16 K + 1 log_g (then 8 S for the output ring)
 constexpr int DMA_TV_WAVE = 13;   // loader 1: 8 T + 4 V + 1 beta (then 16 Q for the output ring)
 // The exchange: per output/recurrence pair and parity of the chunk, the
-// bf16 state fragments (4 x 1 KB) and the bf16 Delta fragments (2 x 1 KB),
+// bf16 state fragments (4 x 1 KB) and the bf16 el Delta fragments (2 x 1 KB),
 // each stored lane-major (lane l's 16 bytes at 16 l).  Then 256 bytes of
 // decay factors per output wave.
-// The output ring: per slot Q (64 rows x 256 B, laid out as K) and P (64
+// The output ring: per slot Q (64 rows x 256 B, laid out as K) and S (64
 // rows x 128 B, laid out as T).
 constexpr int EX_BASE = 89344;                 // N_STAGES * ST_BYTES rounded up to 1 KB
 constexpr int EX_SLOT = 6144;
 constexpr int OR_BASE = EX_BASE + 4 * EX_SLOT;
 constexpr int OR_Q = 0;
-constexpr int OR_P = 16384;
+constexpr int OR_S = 16384;
 constexpr int OR_SLOT = 24576;
 constexpr int OUT_SCR = OR_BASE + 2 * OR_SLOT;
 constexpr int SPINE_LDS = OUT_SCR + 2 * 256;
@@ -592,7 +605,7 @@ struct LoadOffsets {
     uint32_t gb;      // log_g / beta
     // per 1 KB piece j: lane offsets and (uniform) SGPR offsets
     uint32_t kv[8], ks[16];   // K and Q pieces 0..15 (lane offsets repeat every 8)
-    uint32_t tv[8], ts[8];    // T and P pieces 0..7
+    uint32_t tv[8], ts[8];    // T and S pieces 0..7 (lanes above the diagonal out of range)
     uint32_t vs[4];           // V pieces 0..3
 };
 
@@ -612,7 +625,12 @@ __device__ __forceinline__ LoadOffsets load_offsets(int lane, int Hk, int Hv) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         o.kv[j] = o.k[(j >> 1) & 1];
-        o.tv[j] = o.t[j & 1];
+        // piece j, lane l: row 8 j + l / 8, memory granule (columns 8 q ..
+        // 8 q + 7) q = (l % 8) ^ fT(row); a granule wholly above the
+        // diagonal (8 q > row) is not in memory and reads as zero
+        const int row = 8 * j + (lane >> 3);
+        const int qg = p8 ^ (hb | ((j & 1) << 1));
+        o.tv[j] = 8 * qg <= row ? o.t[j & 1] : 0x80000000u;
         o.ts[j] = 1024u * j;
     }
 #pragma unroll
@@ -653,16 +671,16 @@ __device__ __forceinline__ void spine_load(unsigned char* stage, const LoadOffse
     }
 }
 
-// Loader wave wl's share of chunk c's output-ring DMA into `slot_lds`: P
+// Loader wave wl's share of chunk c's output-ring DMA into `slot_lds`: S
 // (wl = 0, 8 operations) or Q (wl = 1, 16 operations).
 __device__ __forceinline__ void spine_load_out(unsigned char* slot_lds, const LoadOffsets& o,
-                                               const uint16_t* q, const uint16_t* pslot, long row0,
+                                               const uint16_t* q, const uint16_t* sslot, long row0,
                                                long len, int c, int Hk, int kh, int wl)
 {
     const uint32_t base = lds_u32(slot_lds);
     if (wl == 0) {
-        const Rsrc rp = make_dma_rsrc(pslot, C * C * 2u);
-        dma_x8(rp, base + OR_P, o.tv, o.ts);
+        const Rsrc rs = make_dma_rsrc(sslot, C * C * 2u);
+        dma_x8(rs, base + OR_S, o.tv, o.ts);
     } else {
         const long r = row0 + (long)c * C;
         const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)r);
@@ -810,14 +828,14 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char
     Dl[2] = mfma_bf16(ft[4], rb1, Dl[2]);
     Dl[3] = mfma_bf16(ft[5], rb1, Dl[3]);
     sched_fence();
-    *reinterpret_cast<s16x8*>(E + 4096 + 16 * lane) = frag_b(Dl[0], Dl[1]);
-    *reinterpret_cast<s16x8*>(E + 5120 + 16 * lane) = frag_b(Dl[2], Dl[3]);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         const float4 el4 = *reinterpret_cast<const float4*>(elv + sig_tile(cb) + 8 * g);
         Dl[cb][0] *= el4.x; Dl[cb][1] *= el4.y; Dl[cb][2] *= el4.z; Dl[cb][3] *= el4.w;
     }
     const s16x8 ds0 = frag_b(Dl[0], Dl[1]), ds1 = frag_b(Dl[2], Dl[3]);
+    *reinterpret_cast<s16x8*>(E + 4096 + 16 * lane) = ds0;
+    *reinterpret_cast<s16x8*>(E + 5120 + 16 * lane) = ds1;
 
     // h <- gamma_L h + K^T (el Delta): 8 row blocks, two blocks ahead
 #pragma unroll
@@ -844,15 +862,15 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char
     wait_lgkm0();   // the exchange writes are complete before the barrier
 }
 
-// One output wave, one chunk: O = gm (Q h) + P Delta for its 16 columns,
-// with Q and P from output-ring slot Sq, the bf16 state and Delta from the
-// exchange slot E the recurrence wave filled, and lg this lane's log_g
-// (lane = row).  The products are formed transposed, O^T = gm (h^T Q^T) +
-// Delta^T P^T: a B-operand fragment of h or Delta is the A operand of its
-// transpose and an A-operand fragment of Q or P the B operand of its
-// transpose, so the same fragments serve, and lane (g, n) register r of tile
-// cb ends up holding O[sig(cb, n)][4g + r]: four consecutive columns of one
-// row, stored at once.  `ro` covers exactly the chunk's output rows;
+// One output wave, one chunk: O = (gm / gm_L) (gm_L (Q h) + S (el Delta))
+// for its 16 columns, with Q and S from output-ring slot Sq, the bf16 state
+// and el Delta from the exchange slot E the recurrence wave filled, and lg
+// this lane's log_g (lane = row).  The products are formed transposed: a
+// B-operand fragment of h or el Delta is the A operand of its transpose and
+// an A-operand fragment of Q or S the B operand of its transpose, so the
+// same fragments serve, and lane (g, n) register r of tile cb ends up
+// holding O[sig(cb, n)][4g + r]: four consecutive columns of one row, stored
+// at once.  `ro` covers exactly the chunk's output rows;
 // `lane_off` is the lane's byte offset for row sig(0, n) and column 4g, and
 // soff[cb] the uniform offset of tile cb's rows.
 template <bool kOutF32>
@@ -861,7 +879,10 @@ __device__ __forceinline__ void out_step(const unsigned char* Sq, const unsigned
                                          uint32_t lane_off, const uint32_t (&soff)[4], int n,
                                          int lane)
 {
-    scr[lane] = __expf(wave_scan_dpp(lg));   // gm_r = exp(G_r)
+    const float G = wave_scan_dpp(lg);
+    const float GL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
+    scr[lane] = __expf(G - GL);   // gm_r / gm_L
+    const float gmL = __expf(GL);
     s16x8 hb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) hb[kk] = lds_read16(E + 1024 * kk + 16 * lane);
@@ -877,22 +898,24 @@ __device__ __forceinline__ void out_step(const unsigned char* Sq, const unsigned
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) Y[cb] = mfma_bf16(hb[kk], qf[cb], Y[cb]);
     }
-    s16x8 pf[6];
+    s16x8 sf[6];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) pf[cb] = lds_read16(Sq + fo.t + OR_P + 128 * sig_tile(cb));
-    pf[4] = lds_read16(Sq + fo.t + OR_P + 128 * sig_tile(2) + 64);
-    pf[5] = lds_read16(Sq + fo.t + OR_P + 128 * sig_tile(3) + 64);
+    for (int cb = 0; cb < 4; ++cb) sf[cb] = lds_read16(Sq + fo.t + OR_S + 128 * sig_tile(cb));
+    sf[4] = lds_read16(Sq + fo.t + OR_S + 128 * sig_tile(2) + 64);
+    sf[5] = lds_read16(Sq + fo.t + OR_S + 128 * sig_tile(3) + 64);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) Y[cb] = Y[cb] * gmL;
+    f32x4 O[4];
+    O[0] = mfma_bf16(db0, sf[0], Y[0]);
+    O[1] = mfma_bf16(db0, sf[1], Y[1]);
+    O[2] = mfma_bf16(db0, sf[2], Y[2]);
+    O[3] = mfma_bf16(db0, sf[3], Y[3]);
+    O[2] = mfma_bf16(db1, sf[4], O[2]);
+    O[3] = mfma_bf16(db1, sf[5], O[3]);
     wave_lds_sync();
     const int sig0 = 8 * (n >> 2) + (n & 3);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) Y[cb] = Y[cb] * scr[sig_tile(cb) + sig0];   // row factor of this lane's row
-    f32x4 O[4];
-    O[0] = mfma_bf16(db0, pf[0], Y[0]);
-    O[1] = mfma_bf16(db0, pf[1], Y[1]);
-    O[2] = mfma_bf16(db0, pf[2], Y[2]);
-    O[3] = mfma_bf16(db0, pf[3], Y[3]);
-    O[2] = mfma_bf16(db1, pf[4], O[2]);
-    O[3] = mfma_bf16(db1, pf[5], O[3]);
+    for (int cb = 0; cb < 4; ++cb) O[cb] = O[cb] * scr[sig_tile(cb) + sig0];   // row factor of this lane's row
     // hardware RNE conversion; rows beyond a partial chunk fall outside `ro`
     // and are dropped
 #pragma unroll
@@ -916,7 +939,8 @@ __global__ void __launch_bounds__(384)
 gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const float* __restrict__ log_g,
                  const float* __restrict__ beta, const float* h0, void* __restrict__ out,
-                 float* h_final, const uint16_t* __restrict__ slots, int T, int Hk, int Hv,
+                 float* h_final, const uint16_t* __restrict__ tslots,
+                 const uint16_t* __restrict__ sslots, int T, int Hk, int Hv,
                  const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_base,
                  int nc_dense, long n_slots)
 {
@@ -943,8 +967,10 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // Only a decreasing cu_seqlens (a broken precondition) can make this
     // bind; it keeps every read inside the workspace.
     if (slot0 + nc > n_slots) nc = (int)max(0L, n_slots - slot0);
-    const uint16_t* slot_base = slots + ((size_t)slot0 * Hv + vh) * SLOT_ELEMS;
+    const uint16_t* slot_base = tslots + ((size_t)slot0 * Hv + vh) * SLOT_ELEMS;   // T, by chunk
     const size_t slot_stride = (size_t)Hv * SLOT_ELEMS;
+    const uint16_t* s_base = sslots + ((size_t)slot0 * Hk + kh) * SLOT_ELEMS;      // S, by chunk
+    const size_t s_stride = (size_t)Hk * SLOT_ELEMS;
 
     if (w >= 4) {   // loader waves
         const int wl = w - 4;
@@ -963,8 +989,8 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             // output slot c%2 are free
             ring_barrier();
             if (c < nc)
-                spine_load_out(lds + OR_BASE + (c & 1) * OR_SLOT, o, q,
-                               slot_base + (size_t)c * slot_stride + C * C, row0, len, c, Hk, kh, wl);
+                spine_load_out(lds + OR_BASE + (c & 1) * OR_SLOT, o, q, s_base + (size_t)c * s_stride, row0,
+                               len, c, Hk, kh, wl);
             if (c + 2 < nc)
                 spine_load(ring + ((c + 2) % N_STAGES) * ST_BYTES, o, k, v, log_g, beta,
                            slot_base + (size_t)(c + 2) * slot_stride, row0, len, c + 2, Hk, Hv, kh,
@@ -1057,9 +1083,9 @@ long slot_count(int B, int T, bool packed) {
 
 }  // namespace
 
-size_t prefill_mfma_workspace_bytes(int B, int T, int Hv, bool packed)
+size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv, bool packed)
 {
-    return table_bytes(B) + (size_t)slot_count(B, T, packed) * Hv * SLOT_ELEMS * sizeof(uint16_t);
+    return table_bytes(B) + (size_t)slot_count(B, T, packed) * (Hv + Hk) * SLOT_ELEMS * sizeof(uint16_t);
 }
 
 bool prefill_mfma_accepts(const PrefillArgs& a)
@@ -1078,9 +1104,10 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
 {
     const bool packed = a.cu_seqlens != nullptr;
     int32_t* base = reinterpret_cast<int32_t*>(a.workspace);
-    uint16_t* slots = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(a.workspace) + table_bytes(a.B));
     const int nc_dense = (a.T + C - 1) / C;
     const long n_slots = slot_count(a.B, a.T, packed);
+    uint16_t* tslots = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(a.workspace) + table_bytes(a.B));
+    uint16_t* sslots = tslots + (size_t)n_slots * a.Hv * SLOT_ELEMS;
     if (packed) {
         hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.B, a.T, base);
     }
@@ -1089,18 +1116,18 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
         const size_t shmem = prep_lds_bytes(nw);
         hipLaunchKernelGGL(gdn_wy_prep_kernel, dim3((unsigned)n_slots, a.Hk, (unsigned)((G + nw - 1) / nw)),
                            dim3(64 * nw), shmem, s,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, a.log_g, a.beta, slots, a.B,
-                           a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense);
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, a.log_g, a.beta, tslots, sslots,
+                           a.B, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense);
     }
     dim3 grid(a.Hv * N_TILES, a.B);
     if (a.out_dtype == 0)
         hipLaunchKernelGGL((gdn_spine_kernel<true>), grid, dim3(384), 0, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, a.log_g, a.beta, a.h0, a.out,
-                           a.h_final, slots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense, n_slots);
+                           a.h_final, tslots, sslots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense, n_slots);
     else
         hipLaunchKernelGGL((gdn_spine_kernel<false>), grid, dim3(384), 0, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, a.log_g, a.beta, a.h0, a.out,
-                           a.h_final, slots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense, n_slots);
+                           a.h_final, tslots, sslots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense, n_slots);
     return hipGetLastError();
 }
 

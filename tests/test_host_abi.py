@@ -96,12 +96,13 @@ def test_prefill_empty_needs_no_pointers(lib):
 
 
 def test_workspace_and_stash_sizes(lib):
-    # MFMA route: a 256-byte chunk table, then T and P (2 x 64 x 64 bf16) per (chunk, v-head)
-    assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 128, 128, 64, 1) == 256 + 72 * 48 * 16384
-    assert gdn.gdn_prefill_workspace_bytes(2, 100, 16, 48, 128, 128, 64, 1) == 256 + 2 * 2 * 48 * 16384
+    # MFMA route: a 256-byte chunk table, then T (64 x 64 bf16) per (chunk, v-head) and
+    # S (64 x 64 bf16) per (chunk, k-head)
+    assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 128, 128, 64, 1) == 256 + 72 * (48 + 16) * 8192
+    assert gdn.gdn_prefill_workspace_bytes(2, 100, 16, 48, 128, 128, 64, 1) == 256 + 2 * 2 * (48 + 16) * 8192
     # packed: ceil(T / 64) + B chunks at most
     assert gdn.gdn_prefill_workspace_bytes(8, 39168, 16, 48, 128, 128, 64, 1, packed=True) == \
-        256 + (612 + 8) * 48 * 16384
+        256 + (612 + 8) * (48 + 16) * 8192
     # generic route needs none
     assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 128, 128, 64, 0) == 0
     assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 64, 64, 64, 1) == 0
