@@ -754,16 +754,23 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char
 #define KTF(db, kk) join(lds_read_tr(pz[(db) >> 1] + ST_K + 8192 * (kk) + 8 * ((db) & 1)), \
                          lds_read_tr(pz[(db) >> 1] + ST_K + 8192 * (kk) + 1024 + 8 * ((db) & 1)))
 
-    // every read of the chunk's scalars, V and T comes before the exchange
-    // writes (which the compiler cannot prove disjoint from them), so all are
-    // in flight while X is formed
-    float4 gm4[4], bt4[4];
+    // every read of the chunk's K fragments, scalars, V and T comes before
+    // the exchange writes (which the compiler cannot prove disjoint from
+    // them), so all are in flight while X is formed; the K fragments go
+    // first, all four k-steps at once
+    s16x8 kf[4][4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) kf[kk][cb] = KF(cb, kk);
+    float4 gm4[4], bt4[4], el4[4];
     s16x4 vv[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         const int row = sig_tile(cb) + 8 * g;
         gm4[cb] = *reinterpret_cast<const float4*>(gmv + row);
         bt4[cb] = *reinterpret_cast<const float4*>(btv + row);
+        el4[cb] = *reinterpret_cast<const float4*>(elv + row);
         vv[cb] = lds_read_tr(pv + ST_V + 64 * sig_tile(cb));
     }
     s16x8 ft[6];
@@ -773,9 +780,6 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char
     ft[5] = TF(3, 1);
     const float gamL = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
         __builtin_bit_cast(int, *reinterpret_cast<const float*>(S + ST_SO))));
-    s16x8 fcur[4], fnext[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) fcur[cb] = KF(cb, 0);
 
     s16x8 hb[4];
 #pragma unroll
@@ -784,25 +788,14 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char
         *reinterpret_cast<s16x8*>(E + 1024 * kk + 16 * lane) = hb[kk];
     }
 
-    // X = K h: per k-step 4 K fragments, loaded one k-step ahead
+    // X = K h, k-step by k-step as the fragments land
     f32x4 X[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) X[cb] = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        if (kk + 1 < 4) {
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) fnext[cb] = KF(cb, kk + 1);
-        }
-        sched_fence();
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) X[cb] = mfma_bf16(fcur[cb], hb[kk], X[cb]);
-        sched_fence();
-        if (kk + 1 < 4) {
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) fcur[cb] = fnext[cb];
-        }
-    }
+        for (int cb = 0; cb < 4; ++cb) X[cb] = mfma_bf16(kf[kk][cb], hb[kk], X[cb]);
 
     // R = beta (V - gm X) for this lane's rows
 #pragma unroll
@@ -830,8 +823,7 @@ __device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char
     sched_fence();
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-        const float4 el4 = *reinterpret_cast<const float4*>(elv + sig_tile(cb) + 8 * g);
-        Dl[cb][0] *= el4.x; Dl[cb][1] *= el4.y; Dl[cb][2] *= el4.z; Dl[cb][3] *= el4.w;
+        Dl[cb][0] *= el4[cb].x; Dl[cb][1] *= el4[cb].y; Dl[cb][2] *= el4[cb].z; Dl[cb][3] *= el4[cb].w;
     }
     const s16x8 ds0 = frag_b(Dl[0], Dl[1]), ds1 = frag_b(Dl[2], Dl[3]);
     *reinterpret_cast<s16x8*>(E + 4096 + 16 * lane) = ds0;
