@@ -48,6 +48,9 @@ def open_library(path: str):
     lib.gdn_oracle_prefill.restype = I
     lib.gdn_oracle_decode.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I]
     lib.gdn_oracle_decode.restype = I
+    L = ctypes.c_long
+    lib.gdn_oracle_ba_gates.argtypes = [P, P, P, P, P, I, I, I, L, L, I, I]
+    lib.gdn_oracle_ba_gates.restype = I
     return lib
 
 
@@ -134,3 +137,19 @@ def decode(states, q, k, v, gate, beta, lib=None):
     if rc != 0:
         raise ValueError("oracle decode: bad shape")
     return out, after
+
+
+def ba_gates(x, w, a_log, dt_bias, nv, vheads_per_group, lib=None):
+    """The gate/beta producer: x [m, k] (or [m, x_stride] with the first k
+    columns used, k = w.shape[1]), w [2 nv, k], a_log and dt_bias [nv].
+    Returns out [m, 2 nv]: columns 0..nv-1 the log-decay gate, nv..2nv-1 beta.
+    """
+    x, w, a_log, dt_bias = (_f64(a) for a in (x, w, a_log, dt_bias))
+    m, x_stride = x.shape
+    n, k = w.shape
+    out = np.full((m, 2 * nv), np.nan)
+    rc = (lib or _load()).gdn_oracle_ba_gates(_ptr(x), _ptr(w), _ptr(a_log), _ptr(dt_bias), _ptr(out),
+                                              m, n, k, x_stride, 2 * nv, nv, vheads_per_group)
+    if rc != 0:
+        raise ValueError("oracle ba_gates: bad shape")
+    return out

@@ -219,3 +219,55 @@ int gdn_oracle_decode(const double* states, const double* q, const double* k,
     free(st);
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* The gate/beta producer (the BA projection) ahead of the recurrence.
+ *
+ * The pages give its launcher and index model (ssm_ba_gates_hopper.rs, the
+ * launcher of dense_gemm_ba_gates_prefill_hopper and "the index model"): every
+ * token's activation row (k values) is multiplied by n = 2*nv weight rows,
+ * and output n lands, by ba_gates_slot, in the token's output row
+ * [gate(nv) | beta(nv)]: with G = vheads_per_group, group = n / (2G) and
+ * w = n % (2G), the first G outputs of a group are beta of v-heads
+ * group*G + w and the next G the gates of v-heads group*G + (w - G).
+ *
+ * The activation of the two halves is not printed on the pages; the reading
+ * taken (from the names a_log and dt_bias the launcher passes) is the usual
+ * Gated DeltaNet gating:
+ *     gate = -exp(a_log[vh]) * softplus(y + dt_bias[vh])   (log of alpha)
+ *     beta = 1 / (1 + exp(-y))
+ * with softplus(z) = log(1 + exp(z)), evaluated as max(z, 0) + log1p(exp(-|z|)),
+ * the same number without overflow.
+ *
+ * x   : [m][x_stride] (the first k values of a row are used)
+ * w   : [n][k]
+ * out : [m][out_stride]; columns 0..nv-1 gate, nv..2nv-1 beta
+ * Returns 0, or -1 on a shape error.
+ */
+static double softplus(double z) { return (z > 0.0 ? z : 0.0) + log1p(exp(-fabs(z))); }
+
+int gdn_oracle_ba_gates(const double* x, const double* w, const double* a_log,
+                        const double* dt_bias, double* out, int m, int n, int k,
+                        long x_stride, long out_stride, int nv, int G)
+{
+    if (m < 0 || k <= 0 || nv <= 0 || G <= 0 || n != 2 * nv || nv % G != 0 ||
+        x_stride < k || out_stride < 2L * nv)
+        return -1;
+    for (int t = 0; t < m; ++t) {
+        const double* xt = x + (long)t * x_stride;
+        double* ot = out + (long)t * out_stride;
+        for (int o = 0; o < n; ++o) {
+            double y = 0.0;
+            for (int i = 0; i < k; ++i) y += xt[i] * w[(long)o * k + i];
+            const int group = o / (2 * G), within = o % (2 * G);
+            if (within < G) {
+                const int vh = group * G + within;
+                ot[nv + vh] = 1.0 / (1.0 + exp(-y));
+            } else {
+                const int vh = group * G + (within - G);
+                ot[vh] = -exp(a_log[vh]) * softplus(y + dt_bias[vh]);
+            }
+        }
+    }
+    return 0;
+}

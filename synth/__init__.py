@@ -13,6 +13,13 @@ Recipe (per workload below):
   * h0: zeros (passed as "no initial state") or N(0, 0.02^2) (0.02 is the
     standard deviation) in fp32, one dk x dv state per (sequence, v-head);
   * packed sequences: lengths uniform on the integers of [lo, hi].
+The gate/beta producer (BA projection) takes, in place of a model's trained
+weights and activations:
+  * activations x ~ N(0, 1), rounded to bf16;
+  * the weight [2 nv][k] ~ N(0, 1/k) (unit-variance pre-activations), bf16;
+  * a_log = ln(A) with A ~ U(1, 16), and dt_bias = ln(e^dt - 1) with
+    ln(dt) ~ U(ln 0.001, ln 0.1), both fp32 (the usual initialisation of
+    these two parameters in Mamba-style gating).
 The generator is numpy's PCG64 (``numpy.random.default_rng(seed)``).
 """
 from __future__ import annotations
@@ -85,6 +92,26 @@ WORKLOADS = {
                  note="single-token decode step of 16 sequences, states updated in place"),
     ]
 }
+
+
+# The gate/beta producer at the pages' geometry: one 4576-token prefill's
+# activations (hidden size 5120) against 2 x 48 BA outputs, 3 v-heads per
+# k-head group.
+BA_WORKLOAD = dict(name="ba_gates_t4576", m=4576, k=5120, nv=48, vheads_per_group=3, seed=1006)
+
+
+def ba_inputs(m, k, nv, seed=0, x_stride=None):
+    """Inputs of one gate/beta producer call as CPU tensors: x bf16
+    [m, x_stride] (columns k.. are filled too, and must be ignored), w bf16
+    [2 nv, k], a_log and dt_bias fp32 [nv]."""
+    rng = np.random.default_rng(seed)
+    xs = k if x_stride is None else x_stride
+    x = _round(rng.standard_normal((m, xs)), torch.bfloat16)
+    w = _round(rng.standard_normal((2 * nv, k)) / np.sqrt(k), torch.bfloat16)
+    a_log = _round(np.log(rng.uniform(1.0, 16.0, nv)), torch.float32)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), nv))
+    dt_bias = _round(np.log(np.expm1(dt)), torch.float32)
+    return dict(x=x, w=w, a_log=a_log, dt_bias=dt_bias)
 
 
 def packed_lengths(B: int, lo: int, hi: int, seed: int) -> np.ndarray:

@@ -27,6 +27,17 @@ What pins what:
   decode_rows        for K = 1, 2, 5, 8 rows, the oracle's outputs and per-prefix
                      states equal the token recurrence S <- a S (I - b k k^T) + b v k^T,
                      o = S q, applied row by row (the K = 1 step is its first row)
+
+The gate/beta producer (the BA projection):
+  ba_slots           where each output lands, against a table worked by hand from
+                     the pages' index model (tests/golden/ba_slot_g3.json)
+  ba_zero_input      x = 0: beta = 1/2 exactly, gate = -e^{a_log} ln(1 + e^{dt_bias})
+  ba_special_values  softplus(0) = ln 2, softplus(z) -> z and e^{-|z|} for large |z|,
+                     sigmoid(+-40) = 1 - e^{-40} and e^{-40}; e^{a_log} with a_log = ln 2
+  ba_one_hot         a one-hot activation row picks one column of the weight
+  ba_linearity       the pre-activations recovered from beta (logit) and from the
+                     gate (inverse softplus) are linear in x and agree with each
+                     other's group structure; extra row-stride columns are ignored
 """
 from __future__ import annotations
 
@@ -368,6 +379,110 @@ def pin_decode_rows(lib=None):
                     _close(after[b, r + 1, vh], S.T, 1e-12, f"K={K} state after {r + 1} rows")
 
 
+# --------------------------------------------------------------------------
+# The gate/beta producer.  Inputs are chosen so that each pre-activation
+# y = x . w_n is known without the oracle (zero, one-hot, or a linear
+# combination of runs), and the gating is checked at values whose results are
+# closed forms.
+
+def _ba(x, w, a_log, dt_bias, nv, G, lib):
+    return oracle.ba_gates(x, w, a_log, dt_bias, nv, G, lib=lib)
+
+
+def pin_ba_slots(lib=None):
+    g = json.load(open(os.path.join(GOLDEN, "ba_slot_g3.json")))
+    nv, G = g["nv"], g["vheads_per_group"]
+    n, k = 2 * nv, 4
+    y = 0.25 * np.arange(1, n + 1)          # distinct pre-activation per output
+    w = np.zeros((n, k))
+    w[:, 2] = y                              # x = e_2 selects column 2
+    x = np.zeros((1, k))
+    x[0, 2] = 1.0
+    out = _ba(x, w, np.zeros(nv), np.zeros(nv), nv, G, lib)[0]
+    for o, (kind, vh) in enumerate(g["slots"]):
+        if kind == "beta":
+            _close(out[nv + vh], 1.0 / (1.0 + np.exp(-y[o])), 1e-15, f"beta slot of output {o}")
+        else:
+            _close(out[vh], -np.logaddexp(0.0, y[o]), 1e-15, f"gate slot of output {o}")
+
+
+def pin_ba_zero_input(lib=None):
+    rng = _rng(71)
+    nv, G, k = 8, 4, 32
+    a_log = rng.standard_normal(nv)
+    dt_bias = rng.standard_normal(nv) * 3.0
+    out = _ba(np.zeros((3, k)), rng.standard_normal((2 * nv, k)), a_log, dt_bias, nv, G, lib)
+    assert np.all(out[:, nv:] == 0.5), "beta of a zero pre-activation is exactly 1/2"
+    gate = -np.exp(a_log) * np.log1p(np.exp(dt_bias))   # ln(1 + e^z) for moderate z
+    for t in range(3):
+        _close(out[t, :nv], gate, 1e-14, "gate of a zero input")
+    assert np.all(out[:, :nv] < 0.0), "the log-decay is negative"
+
+
+def pin_ba_special_values(lib=None):
+    # one v-head per group, G = 1: output 2j is beta, 2j + 1 the gate of v-head j
+    zs = np.array([0.0, 60.0, -60.0, 40.0])
+    nv = zs.size
+    w = np.zeros((2 * nv, 1))
+    w[0::2, 0] = zs                          # beta pre-activations
+    w[1::2, 0] = zs                          # gate pre-activations (dt_bias = 0)
+    a_log = np.full(nv, np.log(2.0))         # e^{a_log} = 2
+    out = _ba(np.ones((1, 1)), w, a_log, np.zeros(nv), nv, 1, lib)[0]
+    gate, beta = out[:nv], out[nv:]
+    _close(gate[0], -2.0 * np.log(2.0), 1e-15, "softplus(0) = ln 2")
+    _close(gate[1], -2.0 * 60.0, 1e-15, "softplus(60) = 60 to fp64")
+    assert abs(gate[2] - (-2.0 * np.exp(-60.0))) <= 1e-15 * 2.0 * np.exp(-60.0) * 10, "softplus(-60) = e^-60"
+    assert beta[0] == 0.5
+    assert abs(beta[3] - (1.0 - np.exp(-40.0))) <= 1e-16, "sigmoid(40) = 1 - e^-40"
+    assert abs(beta[2] - np.exp(-60.0)) <= 1e-15 * np.exp(-60.0) * 10, "sigmoid(-60) = e^-60"
+
+
+def pin_ba_one_hot(lib=None):
+    rng = _rng(72)
+    nv, G, k = 6, 2, 9
+    w = rng.standard_normal((2 * nv, k))
+    for j in (0, 4, k - 1):
+        x = np.zeros((1, k))
+        x[0, j] = 1.0
+        out = _ba(x, w, np.zeros(nv), np.zeros(nv), nv, G, lib)[0]
+        for o in range(2 * nv):
+            grp, wi = divmod(o, 2 * G)
+            if wi < G:
+                _close(out[nv + grp * G + wi], 1.0 / (1.0 + np.exp(-w[o, j])), 1e-15, "one-hot beta")
+            else:
+                _close(out[grp * G + wi - G], -np.logaddexp(0.0, w[o, j]), 1e-15, "one-hot gate")
+
+
+def _pre_activations(out, a_log, dt_bias, nv):
+    """Invert the gating: y from beta (logit) and from the gate (inverse softplus)."""
+    b = out[:, nv:]
+    s = -out[:, :nv] / np.exp(a_log)                 # softplus(y + dt_bias) > 0
+    with np.errstate(invalid="ignore", divide="ignore"):   # NaN where that fails: the pin then fails
+        yb = np.log(b) - np.log1p(-b)
+        yg = np.log(np.expm1(s)) - dt_bias
+    return yg, yb
+
+
+def pin_ba_linearity(lib=None):
+    rng = _rng(73)
+    nv, G, k, m = 6, 3, 40, 5
+    w = rng.standard_normal((2 * nv, k)) * 0.2
+    a_log = rng.standard_normal(nv) * 0.5
+    dt_bias = rng.standard_normal(nv) * 0.5
+    x1 = rng.standard_normal((m, k))
+    x2 = rng.standard_normal((m, k))
+    g1, b1 = _pre_activations(_ba(x1, w, a_log, dt_bias, nv, G, lib), a_log, dt_bias, nv)
+    g2, b2 = _pre_activations(_ba(x2, w, a_log, dt_bias, nv, G, lib), a_log, dt_bias, nv)
+    g3, b3 = _pre_activations(_ba(2.0 * x1 - x2, w, a_log, dt_bias, nv, G, lib), a_log, dt_bias, nv)
+    _close(g3, 2.0 * g1 - g2, 1e-9, "gate pre-activation is linear in x")
+    _close(b3, 2.0 * b1 - b2, 1e-9, "beta pre-activation is linear in x")
+    # a wider row (row stride > k): the extra columns are not read
+    wide = np.concatenate([x1, 1e6 * np.ones((m, 7))], axis=1)
+    _close(_ba(wide, w, a_log, dt_bias, nv, G, lib), _ba(x1, w, a_log, dt_bias, nv, G, lib), 0.0,
+           "columns beyond k")
+
+
 ALL_PINS = [pin_scalar_golden, pin_matrix_form, pin_chunked_form, pin_pure_decay, pin_overwrite,
             pin_state_carry, pin_linearity, pin_contraction, pin_packed, pin_head_grouping,
-            pin_heads_subset, pin_empty, pin_decode, pin_decode_rows]
+            pin_heads_subset, pin_empty, pin_decode, pin_decode_rows, pin_ba_slots,
+            pin_ba_zero_input, pin_ba_special_values, pin_ba_one_hot, pin_ba_linearity]

@@ -72,6 +72,15 @@ MUTANTS = {
                       "r0 = c->cu[b] + (b > 0); L = c->cu[b + 1] - c->cu[b] - (b > 0);"),
     "decode_head_map": ("const int kh = vh / (Hv / Hk);", "const int kh = vh % Hk;"),
     "decode_prefix_off_by_one": ("st + (long)(r - 1) * dkdv", "st + (long)(r > 1 ? r - 2 : 0) * dkdv"),
+    "ba_gate_sign": ("ot[vh] = -exp(a_log[vh]) *", "ot[vh] = exp(a_log[vh]) *"),
+    "ba_no_dt_bias": ("softplus(y + dt_bias[vh]);", "softplus(y);"),
+    "ba_a_log_not_exponentiated": ("ot[vh] = -exp(a_log[vh]) *", "ot[vh] = -a_log[vh] *"),
+    "ba_halves_swapped": ("ot[nv + vh] = 1.0 / (1.0 + exp(-y));", "ot[vh] = 1.0 / (1.0 + exp(-y));"),
+    "ba_transposed_weight": ("y += xt[i] * w[(long)o * k + i];", "y += xt[i] * w[(long)i * n + o];"),
+    "ba_sigmoid_sign": ("1.0 / (1.0 + exp(-y))", "1.0 / (1.0 + exp(y))"),
+    "ba_softplus_no_log": ("log1p(exp(-fabs(z)))", "exp(-fabs(z))"),
+    "ba_row_stride": ("x + (long)t * x_stride", "x + (long)t * k"),
+    "ba_slot_within": ("const int vh = group * G + (within - G);", "const int vh = (group * G + (within - G) + 1) % nv;"),
 }
 
 
