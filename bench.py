@@ -73,6 +73,12 @@ def step_bytes(B, Hk, Hv, dk, dv, s_io=2, s_out=2):
             + B * Hv * dv * s_out)
 
 
+def ba_bytes(m, k, nv):
+    """Read the activations, the weight and the two parameter vectors once;
+    write the [gate | beta] rows once."""
+    return m * k * 2 + 2 * nv * k * 2 + 2 * nv * 4 + m * 2 * nv * 4
+
+
 def kernel_source_sha():
     import glob
     h = hashlib.sha256()
@@ -354,6 +360,54 @@ def bench_step(w, args, torch):
     }
 
 
+def bench_ba(args, torch):
+    import linear_attention_ssm_gated_amd as gdn
+    import synth
+    wl = synth.BA_WORKLOAD
+    m, k, nv, G = wl["m"], wl["k"], wl["nv"], wl["vheads_per_group"]
+    d = torch.device("cuda:0")
+    inp = synth.ba_inputs(m, k, nv, seed=wl["seed"])
+    byt = ba_bytes(m, k, nv)
+    n_sets = max(3, int(ROTATE_BYTES // byt) + 1)
+    ws = torch.empty(gdn.gdn_ba_gates_workspace_bytes(m, 2 * nv, k), dtype=torch.uint8, device=d)
+    sets = [dict(x=inp["x"].to(d), w=inp["w"].to(d), a_log=inp["a_log"].to(d), dt_bias=inp["dt_bias"].to(d),
+                 out=torch.empty((m, 2 * nv), dtype=torch.float32, device=d)) for _ in range(n_sets)]
+    route = []
+
+    def launch(i):   # on the current stream (the capture stream while a graph is recorded)
+        g = sets[i]
+        r = gdn.gdn_ba_gates(g["x"], g["w"], g["a_log"], g["dt_bias"], g["out"], m, 2 * nv, k, k, 2 * nv,
+                             nv, G, workspace=ws, stream=None)
+        if not route:
+            route.append(r)
+
+    # parity of the first launch on a sample of tokens (fp64 oracle)
+    import oracle
+    launch(0)
+    torch.cuda.synchronize()
+    rows = list(range(0, m, 97))
+    ref = oracle.ba_gates(inp["x"][rows], inp["w"], inp["a_log"], inp["dt_bias"], nv, G)
+    err = synth.max_rel_err(sets[0]["out"][rows].double().cpu().numpy(), ref)
+    total_ms, kern_ms, eager_ms = time_launches(launch, n_sets, args.warmup, args.steps, torch)
+    ach = byt / (kern_ms * 1e-3) / 1e9
+    return {
+        "metric": "GDN gate/beta producer (BA projection), achieved HBM GB/s (m=4576, k=5120, n=96)",
+        "value": ach, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 x and weight, fp32 accumulation and gates", "data": "synthetic",
+        "config": {"workload": wl["name"], "m": m, "k": k, "n": 2 * nv, "nv": nv, "vheads_per_group": G},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(wl["name"]),
+                     "algorithmic_bytes": byt, "algorithmic_flops": 2.0 * m * k * 2 * nv,
+                     "kernel_ms": kern_ms, "eager_launch_ms": eager_ms},
+        "timing": "HIP events around one replay of a graph of the K launches",
+        "tokens_per_s": m / (kern_ms * 1e-3),
+        "parity_max_rel_err_sampled_tokens": err,
+        "route": route[0] if route else None,
+        "input_sets_rotated": n_sets,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -382,6 +436,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
+        return
+    if args.workload == synth.BA_WORKLOAD["name"]:
+        print(json.dumps(bench_ba(args, torch)), flush=True)
         return
     w = synth.WORKLOADS[args.workload]
     if w.kind == "prefill":

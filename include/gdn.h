@@ -220,6 +220,46 @@ int gdn_decode_step_plan(float* const* h_table, const void* q, const void* k, co
                          int qk_stride, int v_stride, int gb_stride,
                          int io_dtype, int out_dtype);
 
+/* ------------------------------------------------------------------------ */
+/* Gate/beta producer (the BA projection ahead of the recurrence).
+ *
+ * Follows the launcher of the BA-gates kernels and their index model in
+ * ssm_ba_gates_hopper.rs (dense_gemm_ba_gates_prefill_hopper, ba_gates_slot):
+ * token t's activation row (input + t*k_stride, k bf16 values) is multiplied
+ * by the n = 2*nv weight rows (ba_weight, bf16 [n][k] row-major) in fp32, and
+ * output o is placed in the token's fp32 row gate_out + t*gate_stride, laid
+ * out [gate(nv) | beta(nv)]: with G = vheads_per_group, group = o / (2G) and
+ * w = o % (2G), w < G is beta of v-head group*G + w and w >= G the gate of
+ * v-head group*G + (w - G).  The gating, a reading of the a_log and dt_bias
+ * arguments (the pages do not print it):
+ *     gate = -exp(a_log[vh]) * softplus(y + dt_bias[vh])   (natural log of alpha,
+ *                                                            the log_g of the prefill)
+ *     beta = 1 / (1 + exp(-y)),   softplus(z) = log(1 + exp(z)).
+ * a_log, dt_bias: fp32 [nv].  All pointers are device pointers owned by the
+ * caller; gate_out must not overlap the inputs.
+ * Shapes: m >= 0 tokens; nv >= 1 with nv % vheads_per_group == 0; n == 2*nv
+ * <= 128; k a positive multiple of 64; k_stride >= k and a multiple of 8;
+ * gate_stride >= 2*nv; m*k_stride and n*k below 2^30 elements.
+ * workspace: device scratch of at least gdn_ba_gates_workspace_bytes(m, n, k)
+ * bytes (fp32 partial sums of the k splits; no initialisation needed), used
+ * only in the stream's order.
+ * Returns GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_HEAD_GROUPS (nv not a
+ * multiple of vheads_per_group), GDN_ERR_DIM_LIMIT (n > 128 or k not a multiple
+ * of 64), GDN_ERR_STRIDE, GDN_ERR_WORKSPACE or GDN_ERR_HIP; nothing is
+ * launched on error.  m = 0 launches nothing and returns GDN_OK.
+ */
+size_t gdn_ba_gates_workspace_bytes(int m, int n, int k);
+
+int gdn_ba_gates(const void* input, const void* ba_weight, const float* a_log,
+                 const float* dt_bias, float* gate_out, int m, int n, int k, int k_stride,
+                 int gate_stride, int nv, int vheads_per_group, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+int gdn_ba_gates_plan(const void* input, const void* ba_weight, const float* a_log,
+                      const float* dt_bias, float* gate_out, int m, int n, int k, int k_stride,
+                      int gate_stride, int nv, int vheads_per_group, void* workspace,
+                      size_t workspace_bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,9 @@ SIGNATURES = {
     "gdn_fold_plan": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, I]),
     "gdn_decode_step": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P]),
     "gdn_decode_step_plan": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I]),
+    "gdn_ba_gates_workspace_bytes": (Z, [I, I, I]),
+    "gdn_ba_gates": (I, [P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]),
+    "gdn_ba_gates_plan": (I, [P, P, P, P, P, I, I, I, I, I, I, I, P, Z]),
 }
 
 _lib = None
@@ -172,6 +175,39 @@ def gdn_fold(h_table, stash, na_tab, hi_tables, slab_entries, engaged_flag, k_ro
 
 
 # ---- allocation conveniences (torch allocates, the library computes) ------
+
+def gdn_ba_gates_workspace_bytes(m, n, k) -> int:
+    return library().gdn_ba_gates_workspace_bytes(m, n, k)
+
+
+def gdn_ba_gates(input, ba_weight, a_log, dt_bias, gate_out, m, n, k, k_stride, gate_stride, nv,
+                 vheads_per_group, workspace=None, stream=None):
+    """Enqueue one gate/beta producer call (layouts in include/gdn.h).  Returns the route line."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().gdn_ba_gates(
+        _ptr(input), _ptr(ba_weight), _ptr(a_log), _ptr(dt_bias), _ptr(gate_out), m, n, k, k_stride,
+        gate_stride, nv, vheads_per_group, _ptr(workspace), ws_bytes, _stream(stream)))
+    return last_route()
+
+
+def ba_gates(x, w, a_log, dt_bias, nv, vheads_per_group, gate_stride=None, stream=None):
+    """Allocate the output and workspace with torch and run gdn_ba_gates.
+
+    x: bf16 [m, k_stride] (the first k = w.shape[1] columns used); w: bf16
+    [2 nv, k]; a_log, dt_bias: fp32 [nv].  Returns (gate_out fp32 [m,
+    gate_stride] with the gates in columns 0..nv-1 and beta in nv..2nv-1,
+    route line).
+    """
+    m, k_stride = x.shape
+    n, k = w.shape
+    gs = 2 * nv if gate_stride is None else gate_stride
+    out = torch.empty((m, gs), dtype=torch.float32, device=x.device)
+    ws_n = gdn_ba_gates_workspace_bytes(m, n, k)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=x.device) if ws_n else None
+    route = gdn_ba_gates(x, w, a_log, dt_bias, out, m, n, k, k_stride, gs, nv, vheads_per_group,
+                         workspace=ws, stream=stream)
+    return out, route
+
 
 def chunk_prefill(q, k, v, log_g, beta, h0=None, cu_seqlens=None, chunk=64, out_dtype=None,
                   want_state=True, stream=None):

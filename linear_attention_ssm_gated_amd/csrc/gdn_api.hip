@@ -345,6 +345,28 @@ int gdn_fold(float* const* h_table, const float* stash, const int32_t* na_tab,
     return launched(gdn::launch_fold(a, stream));
 }
 
+// Validation of a gate/beta producer call (shared by the call and its plan).
+static int check_ba(const gdn::BaArgs& a)
+{
+    const char* who = "gdn_ba_gates";
+    if (a.m < 0 || a.nv < 1 || a.vheads_per_group < 1 || a.k < 1)
+        return refuse(GDN_ERR_SHAPE, who, "need m >= 0, nv, vheads_per_group and k >= 1");
+    if (a.n != 2 * a.nv) return refuse(GDN_ERR_SHAPE, who, "n must be 2 * nv");
+    if (a.nv % a.vheads_per_group != 0)
+        return refuse(GDN_ERR_HEAD_GROUPS, who, "nv must be a multiple of vheads_per_group");
+    if (a.n > 128 || a.k % 64 != 0)
+        return refuse(GDN_ERR_DIM_LIMIT, who, "n <= 128 and k a multiple of 64");
+    if (a.k_stride < a.k || a.k_stride % 8 != 0 || a.gate_stride < 2 * a.nv)
+        return refuse(GDN_ERR_STRIDE, who, "k_stride >= k (a multiple of 8) and gate_stride >= 2 * nv");
+    if ((long)a.m * a.k_stride >= (1L << 30) || (long)a.n * a.k >= (1L << 30))
+        return refuse(GDN_ERR_SHAPE, who, "m * k_stride and n * k must stay below 2^30");
+    if (a.m > 0 && (!a.input || !a.ba_weight || !a.a_log || !a.dt_bias || !a.gate_out))
+        return refuse(GDN_ERR_NULL, who, "input, ba_weight, a_log, dt_bias and gate_out are required when m > 0");
+    if (a.m > 0 && (!a.workspace || a.workspace_bytes < gdn::ba_gates_workspace_bytes(a.m, a.n, a.k)))
+        return refuse(GDN_ERR_WORKSPACE, who, "workspace smaller than gdn_ba_gates_workspace_bytes()");
+    return GDN_OK;
+}
+
 static gdn::StepArgs make_step(float* const* h_table, const void* q, const void* k, const void* v,
                                const float* gate, const float* beta, void* out, int B, int Hk, int Hv,
                                int dk, int dv, int qk_stride, int v_stride, int gb_stride,
@@ -381,6 +403,38 @@ int gdn_decode_step(float* const* h_table, const void* q, const void* k, const v
     if (st != GDN_OK) return st;
     route_geometry(gdn::step_geometry(a), "");
     return launched(gdn::launch_step(a, stream));
+}
+
+size_t gdn_ba_gates_workspace_bytes(int m, int n, int k)
+{
+    if (m < 0 || n < 1 || k < 1) return 0;
+    return gdn::ba_gates_workspace_bytes(m, n, k);
+}
+
+int gdn_ba_gates_plan(const void* input, const void* ba_weight, const float* a_log,
+                      const float* dt_bias, float* gate_out, int m, int n, int k, int k_stride,
+                      int gate_stride, int nv, int vheads_per_group, void* workspace,
+                      size_t workspace_bytes)
+{
+    gdn::BaArgs a{input, ba_weight, a_log, dt_bias, gate_out, m, n, k, k_stride, gate_stride, nv,
+                  vheads_per_group, workspace, workspace_bytes};
+    int st = check_ba(a);
+    if (st != GDN_OK) return st;
+    route_geometry(gdn::ba_gates_geometry(a), "");
+    return GDN_OK;
+}
+
+int gdn_ba_gates(const void* input, const void* ba_weight, const float* a_log,
+                 const float* dt_bias, float* gate_out, int m, int n, int k, int k_stride,
+                 int gate_stride, int nv, int vheads_per_group, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream)
+{
+    gdn::BaArgs a{input, ba_weight, a_log, dt_bias, gate_out, m, n, k, k_stride, gate_stride, nv,
+                  vheads_per_group, workspace, workspace_bytes};
+    int st = check_ba(a);
+    if (st != GDN_OK) return st;
+    route_geometry(gdn::ba_gates_geometry(a), "");
+    return launched(gdn::launch_ba_gates(a, stream));
 }
 
 }  // extern "C"

@@ -64,6 +64,18 @@ struct StepArgs {
     int io_dtype, out_dtype;
 };
 
+// Arguments of one gate/beta producer call after host validation.
+struct BaArgs {
+    const void* input;       // bf16 [m][k_stride]
+    const void* ba_weight;   // bf16 [n][k]
+    const float* a_log;
+    const float* dt_bias;
+    float* gate_out;         // fp32 [m][gate_stride]: gate [0, nv), beta [nv, 2 nv)
+    int m, n, k, k_stride, gate_stride, nv, vheads_per_group;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
 constexpr int kMaxVerifyRows = 8;   // draft rows a verify takes
 
 // Launch geometry a launcher reports for the route line.
@@ -83,6 +95,8 @@ Geometry verify_geometry(const VerifyArgs& a);
 Geometry fold_geometry(const FoldArgs& a);
 Geometry step_geometry(const StepArgs& a);
 Geometry flag_clear_geometry();
+size_t ba_gates_workspace_bytes(int m, int n, int k);
+Geometry ba_gates_geometry(const BaArgs& a);
 
 hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);
@@ -90,6 +104,7 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, hipStream_t s);
 hipError_t launch_flag_clear(uint32_t* flag, hipStream_t s);
+hipError_t launch_ba_gates(const BaArgs& a, hipStream_t s);
 
 // Per-v-head stash floats of a k_rows-row verify: delta [k_rows][dv] fp32,
 // G [k_rows] fp32, then the keys [k_rows][dk] as fp32 or as packed bf16 bits

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in gdn.h but not exported"
     assert set(names) == set(gdn.SIGNATURES), "binding and header disagree"
@@ -228,3 +228,38 @@ def test_step_refusals(lib, kw, status):
 
 def test_flag_clear_refuses_null(lib):
     assert lib.gdn_flag_clear(None, None) == 1
+
+
+def ba_plan(lib, **kw):
+    a = dict(x=X, w=X, a_log=X, dt_bias=X, out=X, m=4576, n=96, k=5120, k_stride=5120,
+             gate_stride=96, nv=48, G=3, ws=X, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.gdn_ba_gates_plan(a["x"], a["w"], a["a_log"], a["dt_bias"], a["out"], a["m"], a["n"],
+                                 a["k"], a["k_stride"], a["gate_stride"], a["nv"], a["G"], a["ws"],
+                                 a["ws_bytes"])
+
+
+def test_ba_gates_validation(lib):
+    assert ba_plan(lib) == 0
+    assert gdn.last_route().startswith("gdn_ba_partial_kernel+gdn_ba_gate_kernel grid=[72,4,1] block=448")
+    assert ba_plan(lib, m=0, x=None, w=None, a_log=None, dt_bias=None, out=None, ws=None, ws_bytes=0) == 0
+    assert ba_plan(lib, m=-1) == 2
+    assert ba_plan(lib, n=95) == 2                      # n must be 2 nv
+    assert ba_plan(lib, nv=47, n=94) == 3               # nv not a multiple of G
+    assert ba_plan(lib, nv=66, n=132, G=3) == 4         # n > 128
+    assert ba_plan(lib, k=5000, k_stride=5000) == 4     # k not a multiple of 64
+    assert ba_plan(lib, k_stride=5100) == 9             # k_stride < k
+    assert ba_plan(lib, k_stride=5124) == 9             # not a multiple of 8
+    assert ba_plan(lib, gate_stride=95) == 9
+    assert ba_plan(lib, m=300000) == 2                  # m * k_stride beyond 2^30
+    assert ba_plan(lib, dt_bias=None) == 1
+    assert ba_plan(lib, ws=None) == 6
+    assert ba_plan(lib, ws_bytes=gdn.gdn_ba_gates_workspace_bytes(4576, 96, 5120) - 1) == 6
+    assert "refused" in gdn.last_route()
+
+
+def test_ba_gates_workspace_size(lib):
+    # fp32 partial sums of up to four k splits of 64-wide blocks
+    assert gdn.gdn_ba_gates_workspace_bytes(4576, 96, 5120) == 4 * 4576 * 96 * 4
+    assert gdn.gdn_ba_gates_workspace_bytes(10, 8, 128) == 2 * 10 * 8 * 4
+    assert gdn.gdn_ba_gates_workspace_bytes(10, 8, 64) == 1 * 10 * 8 * 4
