@@ -241,7 +241,8 @@ def ba_plan(lib, **kw):
 
 def test_ba_gates_validation(lib):
     assert ba_plan(lib) == 0
-    assert gdn.last_route().startswith("gdn_ba_partial_kernel+gdn_ba_gate_kernel grid=[72,4,1] block=448")
+    # 36 tiles of 128 tokens x 7 k splits fill 252 of 256 compute units; 3 compute waves + 1 loader
+    assert gdn.last_route().startswith("gdn_ba_partial_kernel+gdn_ba_gate_kernel grid=[36,7,1] block=256")
     assert ba_plan(lib, m=0, x=None, w=None, a_log=None, dt_bias=None, out=None, ws=None, ws_bytes=0) == 0
     assert ba_plan(lib, m=-1) == 2
     assert ba_plan(lib, n=95) == 2                      # n must be 2 nv
@@ -259,7 +260,10 @@ def test_ba_gates_validation(lib):
 
 
 def test_ba_gates_workspace_size(lib):
-    # fp32 partial sums of up to four k splits of 64-wide blocks
-    assert gdn.gdn_ba_gates_workspace_bytes(4576, 96, 5120) == 4 * 4576 * 96 * 4
+    # fp32 partial sums of the k splits (of 64-wide blocks): as many as fill 256 compute
+    # units with the 128-token tiles, evened out so that none is empty
+    assert gdn.gdn_ba_gates_workspace_bytes(4576, 96, 5120) == 7 * 4576 * 96 * 4
+    # one tile: 32 splits of 80 blocks -> 3 blocks each -> 27 splits, none empty
+    assert gdn.gdn_ba_gates_workspace_bytes(100, 96, 5120) == 27 * 100 * 96 * 4
     assert gdn.gdn_ba_gates_workspace_bytes(10, 8, 128) == 2 * 10 * 8 * 4
     assert gdn.gdn_ba_gates_workspace_bytes(10, 8, 64) == 1 * 10 * 8 * 4
