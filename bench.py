@@ -101,15 +101,18 @@ def measured_traffic(name):
 
 # ---- timing ----------------------------------------------------------------
 
-def time_launches(launch, n_sets, warmup, steps, torch):
+def time_launches(launch, n_sets, warmup, steps, torch, extra_replays=10):
     """Warm up, then time `steps` launches (rotating input sets) with HIP events.
 
     The timed launches are captured into one HIP graph and the graph is replayed
     between two events on the replay stream, so the kernels run back to back as
     under a serving loop; eagerly, the Python launch path (tens of microseconds
     per call) would leave the GPU idle between short kernels.  Returns
-    (total_ms, average ms per launch, eager ms per launch), the last from an
-    event pair around each of `steps` eager launches, for reference."""
+    (total_ms, average ms per launch, eager ms per launch, spread), the third
+    from an event pair around each of `steps` eager launches, for reference.
+    The first replay alone is the measurement; `extra_replays` more, each timed
+    on its own afterwards, give the spread of the per-launch average (median,
+    p10, p90 over the replays)."""
     for i in range(warmup):
         launch(i % n_sets)
     torch.cuda.synchronize()
@@ -138,7 +141,43 @@ def time_launches(launch, n_sets, warmup, steps, torch):
     t1.record(stream)
     torch.cuda.synchronize()
     total = t0.elapsed_time(t1)
-    return total, total / steps, eager
+    per = []
+    for _ in range(extra_replays):
+        t0.record(stream)
+        graph.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        per.append(t0.elapsed_time(t1) / steps * 1e3)
+    spread = None
+    if per:
+        q = sorted(per)
+        pick = lambda f: q[min(len(q) - 1, int(round(f * (len(q) - 1))))]
+        spread = {"median_us": pick(0.5), "p10_us": pick(0.1), "p90_us": pick(0.9),
+                  "replays": len(q), "launches_per_replay": steps}
+    return total, total / steps, eager, spread
+
+
+def achievable_copy_gbs(torch, mib=1024, reps=10):
+    """Bytes moved (read + write) per second by the runtime's own device-to-device
+    copy of `mib` MiB, median of `reps`: the achievable-HBM yardstick beside the
+    published peak."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        t0.record()
+        dst.copy_(src)
+        t1.record()
+        torch.cuda.synchronize()
+        ts.append(t0.elapsed_time(t1))
+    ts.sort()
+    del src, dst
+    return 2 * n / (ts[len(ts) // 2] * 1e-3) / 1e9
 
 
 def cpu_baseline_prefill(inp, w, T, budget_s=10.0, max_reps=30):
@@ -196,7 +235,7 @@ def bench_prefill(w, args, torch):
         if not route:
             route.append(r)
 
-    total_ms, kern_ms, eager_ms = time_launches(launch, n_sets, args.warmup, args.steps, torch)
+    total_ms, kern_ms, eager_ms, spread = time_launches(launch, n_sets, args.warmup, args.steps, torch)
     ms = total_ms / args.steps
     # parity of the timed launch's output on a few v-heads (fp64 oracle)
     import oracle
@@ -225,7 +264,7 @@ def bench_prefill(w, args, torch):
                      "algorithmic_bytes": byt, "algorithmic_flops": flops,
                      "mfma_tflops": flops / (kern_ms * 1e-3) / 1e12,
                      "mfma_frac": flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                     "kernel_ms": kern_ms, "eager_launch_ms": eager_ms,
+                     "kernel_ms": kern_ms, "eager_launch_ms": eager_ms, "spread": spread,
                      "kernel": route[0].split(" ")[0] if route else None},
         "timing": "HIP events around one replay of a graph of the K launches",
         "route": route[0] if route else None,
@@ -268,7 +307,7 @@ def bench_verify(w, args, torch):
         if not route:
             route.append(r)
 
-    total_ms, kern_ms, eager_ms = time_launches(launch, n_sets, args.warmup, args.steps, torch)
+    total_ms, kern_ms, eager_ms, spread = time_launches(launch, n_sets, args.warmup, args.steps, torch)
     ms = total_ms / args.steps
     ach = byt / (kern_ms * 1e-3) / 1e9
     # parity of the timed launches' outputs (the verify writes no state, so every
@@ -286,7 +325,7 @@ def bench_verify(w, args, torch):
         gdn.gdn_fold(g["table"], g["stash"], g["na"], None, 0, g["flag"], K, w.B, w.Hk, w.Hv, w.dk,
                      w.dv, ssf, gdn.GDN_BF16, stream=None)
 
-    _, fold_ms, fold_eager_ms = time_launches(launch_fold, n_sets, args.warmup, args.steps, torch)
+    _, fold_ms, fold_eager_ms, fold_spread = time_launches(launch_fold, n_sets, args.warmup, args.steps, torch)
     fbyt = fold_bytes(na_l, w.Hv, w.dk, w.dv, K)
     return {
         "metric": "GDN K=4 write-on-accept verify, achieved HBM GB/s (B=16, Hv=48, d=128)",
@@ -296,11 +335,11 @@ def bench_verify(w, args, torch):
         "config": {"workload": w.name, "B": w.B, "K": K, "Hk": w.Hk, "Hv": w.Hv, "dk": w.dk, "dv": w.dv},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
-                     "algorithmic_bytes": byt, "kernel_ms": kern_ms, "eager_launch_ms": eager_ms},
+                     "algorithmic_bytes": byt, "kernel_ms": kern_ms, "eager_launch_ms": eager_ms, "spread": spread},
         "timing": "HIP events around one replay of a graph of the K launches",
         "draft_tokens_per_s": w.B * K / (kern_ms * 1e-3),
         "parity_max_rel_err_out": err,
-        "fold": {"kernel_ms": fold_ms, "eager_launch_ms": fold_eager_ms, "algorithmic_bytes": fbyt, "achieved": fbyt / (fold_ms * 1e-3) / 1e9,
+        "fold": {"kernel_ms": fold_ms, "eager_launch_ms": fold_eager_ms, "spread": fold_spread, "algorithmic_bytes": fbyt, "achieved": fbyt / (fold_ms * 1e-3) / 1e9,
                  "unit": "GB/s", "frac": fbyt / (fold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "na": na_l},
         "route": route[0] if route else None,
         "input_sets_rotated": n_sets,
@@ -341,7 +380,7 @@ def bench_step(w, args, torch):
     ro, after = oracle.decode(inp["states"], inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"])
     err_out = synth.max_rel_err(sets[0]["out"].float().cpu(), ro[:, 0])
     err_state = max(synth.max_rel_err(sets[0]["slots"][b].cpu(), after[b, 1]) for b in range(w.B))
-    total_ms, kern_ms, eager_ms = time_launches(launch, n_sets, args.warmup, args.steps, torch)
+    total_ms, kern_ms, eager_ms, spread = time_launches(launch, n_sets, args.warmup, args.steps, torch)
     ach = byt / (kern_ms * 1e-3) / 1e9
     return {
         "metric": "GDN K=1 decode step, achieved HBM GB/s (B=16, Hv=48, d=128)",
@@ -351,7 +390,7 @@ def bench_step(w, args, torch):
         "config": {"workload": w.name, "B": w.B, "K": 1, "Hk": w.Hk, "Hv": w.Hv, "dk": w.dk, "dv": w.dv},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
-                     "algorithmic_bytes": byt, "kernel_ms": kern_ms, "eager_launch_ms": eager_ms},
+                     "algorithmic_bytes": byt, "kernel_ms": kern_ms, "eager_launch_ms": eager_ms, "spread": spread},
         "timing": "HIP events around one replay of a graph of the K launches",
         "tokens_per_s": w.B / (kern_ms * 1e-3),
         "parity_max_rel_err_out": err_out, "parity_max_rel_err_state": err_state,
@@ -388,7 +427,7 @@ def bench_ba(args, torch):
     rows = list(range(0, m, 97))
     ref = oracle.ba_gates(inp["x"][rows], inp["w"], inp["a_log"], inp["dt_bias"], nv, G)
     err = synth.max_rel_err(sets[0]["out"][rows].double().cpu().numpy(), ref)
-    total_ms, kern_ms, eager_ms = time_launches(launch, n_sets, args.warmup, args.steps, torch)
+    total_ms, kern_ms, eager_ms, spread = time_launches(launch, n_sets, args.warmup, args.steps, torch)
     ach = byt / (kern_ms * 1e-3) / 1e9
     return {
         "metric": "GDN gate/beta producer (BA projection), achieved HBM GB/s (m=4576, k=5120, n=96)",
@@ -399,13 +438,22 @@ def bench_ba(args, torch):
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(wl["name"]),
                      "algorithmic_bytes": byt, "algorithmic_flops": 2.0 * m * k * 2 * nv,
-                     "kernel_ms": kern_ms, "eager_launch_ms": eager_ms},
+                     "kernel_ms": kern_ms, "eager_launch_ms": eager_ms, "spread": spread},
         "timing": "HIP events around one replay of a graph of the K launches",
         "tokens_per_s": m / (kern_ms * 1e-3),
         "parity_max_rel_err_sampled_tokens": err,
         "route": route[0] if route else None,
         "input_sets_rotated": n_sets,
     }
+
+
+def with_copy_yardstick(rec, torch):
+    """Add the measured copy rate and the fraction of it that the path reaches."""
+    copy = achievable_copy_gbs(torch)
+    r = rec["roofline"]
+    r["copy_GBs"] = copy
+    r["frac_of_copy"] = r["achieved"] / copy
+    return rec
 
 
 def main():
@@ -438,7 +486,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
         return
     if args.workload == synth.BA_WORKLOAD["name"]:
-        print(json.dumps(bench_ba(args, torch)), flush=True)
+        print(json.dumps(with_copy_yardstick(bench_ba(args, torch), torch)), flush=True)
         return
     w = synth.WORKLOADS[args.workload]
     if w.kind == "prefill":
@@ -447,7 +495,7 @@ def main():
         rec = bench_step(w, args, torch)
     else:
         rec = bench_verify(w, args, torch)
-    print(json.dumps(rec), flush=True)
+    print(json.dumps(with_copy_yardstick(rec, torch)), flush=True)
 
 
 if __name__ == "__main__":
