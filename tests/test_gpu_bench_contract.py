@@ -1,0 +1,78 @@
+"""bench.py's JSON line for every workload it times, run in this process with
+a few steps: the fields a reader of the line relies on are present and
+consistent (value from the timed steps, the roofline fraction from its own
+figures, the parity figure within the path's bound).
+"""
+import argparse
+import json
+
+import pytest
+import torch
+
+import bench
+import synth
+from gpu_common import dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _args(workload):
+    return argparse.Namespace(gpus=1, steps=3, warmup=1, workload=workload, no_cpu_baseline=True,
+                              copy_calibration=0)
+
+
+def _common(rec, workload):
+    json.dumps(rec)   # serialisable as one line
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline"):
+        assert key in rec, key
+    assert rec["n_gpus"] == 1 and rec["steps"] == 3 and rec["warmup"] == 1
+    assert rec["vs_baseline"] is None and rec["data"] == "synthetic"
+    assert rec["config"]["workload"] == workload
+    r = rec["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic", "copy_GBs", "frac_of_copy", "spread"):
+        assert key in r, key
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == bench.HBM_PEAK_GBS
+    assert r["achieved"] > 0 and r["frac"] == pytest.approx(r["achieved"] / r["peak"])
+    assert r["frac_of_copy"] == pytest.approx(r["achieved"] / r["copy_GBs"])
+    assert 0 < r["frac"] < 1 and 0 < r["copy_GBs"] < r["peak"]
+    s = r["spread"]
+    assert s["replays"] == 10 and s["p10_us"] <= s["median_us"] <= s["p90_us"]
+    assert "cpu_baseline" not in rec
+
+
+def test_prefill_line():
+    say("bench contract: prefill_t4576_h0")
+    w = synth.WORKLOADS["prefill_t4576_h0"]
+    dev()
+    rec = bench.with_copy_yardstick(bench.bench_prefill(w, _args(w.name), torch), torch)
+    _common(rec, w.name)
+    assert rec["value"] == pytest.approx(w.B * w.T / (rec["ms_per_step"] * 1e-3))
+    assert rec["route"].startswith("gdn_wy_prep_kernel+gdn_spine_kernel")
+    assert rec["parity_max_rel_err_sampled_heads"] <= 2e-2
+
+
+def test_verify_line():
+    say("bench contract: verify_k4_b16")
+    w = synth.WORKLOADS["verify_k4_b16"]
+    rec = bench.with_copy_yardstick(bench.bench_verify(w, _args(w.name), torch), torch)
+    _common(rec, w.name)
+    assert rec["value"] == pytest.approx(rec["roofline"]["achieved"])
+    assert rec["parity_max_rel_err_out"] <= 2e-2
+    assert rec["fold"]["kernel_ms"] > 0 and rec["fold"]["spread"]["replays"] == 10
+
+
+def test_step_line():
+    say("bench contract: step_b16")
+    w = synth.WORKLOADS["step_b16"]
+    rec = bench.with_copy_yardstick(bench.bench_step(w, _args(w.name), torch), torch)
+    _common(rec, w.name)
+    assert rec["parity_max_rel_err_out"] <= 2e-2 and rec["parity_max_rel_err_state"] <= 1e-4
+
+
+def test_ba_line():
+    say("bench contract: ba_gates_t4576")
+    name = synth.BA_WORKLOAD["name"]
+    rec = bench.with_copy_yardstick(bench.bench_ba(_args(name), torch), torch)
+    _common(rec, name)
+    assert rec["parity_max_rel_err_sampled_tokens"] <= 1e-4
