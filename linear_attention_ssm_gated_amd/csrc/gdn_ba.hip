@@ -229,8 +229,19 @@ gdn_ba_gate_kernel(const float* __restrict__ partial, const float* __restrict__ 
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (long)m * n) return;
     const int t = (int)(idx / n), o = (int)(idx % n);
+    // up to eight splits' loads in flight before the first add (a plain loop
+    // over a run-time count waits out each load in turn); the sum still runs
+    // over s = 0, 1, ... in order
     float y = 0.f;
-    for (int s = 0; s < splits; ++s) y += partial[(size_t)s * m * n + idx];
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+        float p[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            p[u] = s0 + u < splits ? partial[(size_t)(s0 + u) * m * n + idx] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < splits) y += p[u];
+    }
     const int group = o / (2 * G), within = o % (2 * G);
     float* row = out + (size_t)t * gate_stride;
     if (within < G) {
