@@ -576,14 +576,21 @@ gdn_fold_d128_kernel(float* const* __restrict__ h_table, const float* stash,
     constexpr int NKU = (KR * D + kThreads - 1) / kThreads;   // key elements per thread
     __shared__ __attribute__((aligned(16))) float sk2[KR][kSlices * SP];
 
-    if (engaged_flag[0] == 0u) return;   // the write-on-accept verify did not run
     const int vh = blockIdx.x, b = blockIdx.y;
-    const int na = min(max(na_tab[b], 0), KR);
-    if (na == 0) return;                 // nothing accepted: the state keeps its bytes
+    // the word, the accept count and the state pointer are independent loads:
+    // issue all three before the first branch, so that their latencies overlap
+    const uint32_t engaged = engaged_flag[0];
+    const int na_in = na_tab[b];
+    float* const hb = h_table[b];
+    asm volatile("" ::"s"(engaged), "s"(na_in), "s"(hb));   // all three loaded here, one wait
+    const int na = min(max(na_in, 0), KR);
+    // the write-on-accept verify did not run, or nothing was accepted: the
+    // state keeps its bytes
+    if (engaged == 0u || na == 0) return;
     const int tid = threadIdx.x;
     const int sl = tid >> 5, cg = tid & 31;
     const float* st = stash + (size_t)b * stash_seq_floats + (size_t)vh * stash_head_floats(D, D, kBf16Keys, KR);
-    const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(h_table[b] + (size_t)vh * D * D, (short)0,
+    const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(hb + (size_t)vh * D * D, (short)0,
                                                         D * D * (int)sizeof(float), 0x00020000);
 
     // stash: this thread's 4 delta columns of every row, the KR decays, and
