@@ -98,7 +98,9 @@ const char* gdn_last_route(void);
  * workspace: device scratch of at least gdn_prefill_workspace_bytes() bytes
  * (may be NULL when that is 0), asked with the same B, T, shapes and io_dtype,
  * and packed = (cu_seqlens != NULL).  The MFMA route keeps a chunk table of
- * packed sequences, T = (I + A)^-1 of every (chunk, v-head) and
+ * packed sequences (their first chunks, and for up to 256 sequences their
+ * order by length, longest first, in which the state walks are dispatched),
+ * T = (I + A)^-1 of every (chunk, v-head) and
  * S = lower_incl(Q K^T) of every (chunk, k-head) there, as 64 x 64 bf16
  * matrices (8 KiB each; the granules above their diagonals are never written
  * or read); the generic route needs none.

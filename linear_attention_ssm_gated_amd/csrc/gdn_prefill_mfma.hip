@@ -99,6 +99,11 @@ __device__ __forceinline__ void seq_rows(const int32_t* cu, int b, int T, long* 
 
 // ---------------------------------------------------------------------------
 // Chunk table for packed sequences: base[b] = sum_{b' < b} ceil(len_b' / C).
+// With at most MAX_ORDERED sequences, order[] (after base[B]) lists them by
+// chunk count, longest first (ties by index): the spine walks sequence
+// order[y] in workgroup row y, so the longest walks are dispatched first and
+// the short ones fill in behind them.
+constexpr int MAX_ORDERED = 256;
 __global__ void __launch_bounds__(256)
 gdn_chunk_table_kernel(const int32_t* __restrict__ cu, int B, int T, int32_t* __restrict__ base)
 {
@@ -126,6 +131,25 @@ gdn_chunk_table_kernel(const int32_t* __restrict__ cu, int B, int T, int32_t* __
         long r0, len;
         seq_rows(cu, b, T, &r0, &len);
         s += (int32_t)((len + C - 1) / C);
+    }
+    if (B <= MAX_ORDERED) {   // one sequence per thread (per == 1)
+        int32_t mine = 0;        // this sequence's chunk count
+        if (tid < B) {
+            long r0, len;
+            seq_rows(cu, tid, T, &r0, &len);
+            mine = (int32_t)((len + C - 1) / C);
+        }
+        __syncthreads();         // every read of the prefix sums is done
+        part[tid] = mine;
+        __syncthreads();
+        if (tid < B) {
+            int rank = 0;
+            for (int j = 0; j < B; ++j) {
+                const int32_t o = part[j];
+                rank += (o > mine || (o == mine && j < tid)) ? 1 : 0;
+            }
+            base[B + 1 + rank] = tid;
+        }
     }
 }
 
@@ -934,7 +958,7 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  float* h_final, const uint16_t* __restrict__ tslots,
                  const uint16_t* __restrict__ sslots, int T, int Hk, int Hv,
                  const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_base,
-                 int nc_dense, long n_slots)
+                 const int32_t* __restrict__ order, int nc_dense, long n_slots)
 {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[SPINE_LDS];
     unsigned char* ring = lds;
@@ -949,7 +973,7 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int lin = (W % 8 == 0) ? (blockIdx.x % 8) * (W / 8) + blockIdx.x / 8 : blockIdx.x;
     const int vh = lin / N_TILES;
     const int tile = lin % N_TILES;
-    const int b = blockIdx.y;
+    const int b = order ? order[blockIdx.y] : (int)blockIdx.y;
     const int kh = vh / (Hv / Hk);
 
     long row0, len;
@@ -1067,7 +1091,8 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
 }
 
-size_t table_bytes(int B) { return ((size_t)(B + 1) * sizeof(int32_t) + 255) & ~(size_t)255; }
+// base[B + 1] then order[B]
+size_t table_bytes(int B) { return ((size_t)(2 * B + 1) * sizeof(int32_t) + 255) & ~(size_t)255; }
 
 long slot_count(int B, int T, bool packed) {
     return packed ? (long)(T + C - 1) / C + B : (long)B * ((T + C - 1) / C);
@@ -1100,6 +1125,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
     const long n_slots = slot_count(a.B, a.T, packed);
     uint16_t* tslots = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(a.workspace) + table_bytes(a.B));
     uint16_t* sslots = tslots + (size_t)n_slots * a.Hv * SLOT_ELEMS;
+    const int32_t* order = packed && a.B <= MAX_ORDERED ? base + a.B + 1 : nullptr;
     if (packed) {
         hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.B, a.T, base);
     }
@@ -1115,11 +1141,13 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
     if (a.out_dtype == 0)
         hipLaunchKernelGGL((gdn_spine_kernel<true>), grid, dim3(384), 0, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, a.log_g, a.beta, a.h0, a.out,
-                           a.h_final, tslots, sslots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense, n_slots);
+                           a.h_final, tslots, sslots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, order, nc_dense,
+                           n_slots);
     else
         hipLaunchKernelGGL((gdn_spine_kernel<false>), grid, dim3(384), 0, s, (const uint16_t*)a.q,
                            (const uint16_t*)a.k, (const uint16_t*)a.v, a.log_g, a.beta, a.h0, a.out,
-                           a.h_final, tslots, sslots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense, n_slots);
+                           a.h_final, tslots, sslots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, order, nc_dense,
+                           n_slots);
     return hipGetLastError();
 }
 

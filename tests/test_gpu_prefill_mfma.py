@@ -81,6 +81,36 @@ def test_packed_with_empty_and_short_sequences():
         assert torch.equal(hf[b].cpu(), inp["h0"][b]), "an empty sequence keeps its state"
 
 
+def test_packed_dispatch_order_up_to_and_past_256_sequences():
+    # the spine walks packed sequences longest first when there are at most
+    # 256 of them, in index order past that; either way every sequence's
+    # result is its own: equal to the oracle, and equal bit for bit to the
+    # same sequences packed in reverse
+    for B in (40, 300):
+        rng = np.random.default_rng(900 + B)
+        lens = [int(x) for x in rng.integers(0, 150, size=B)]
+        lens[B // 2] = 700                     # one long walk in the middle
+        inp = synth.prefill_inputs(B, 0, 1, 2, 128, 128, h0=True, seed=901 + B, lengths=lens)
+        say("packed dispatch order", B, sum(lens))
+        out, hf, _ = gpu_prefill(inp, 64)
+        check(inp, out, hf, heads=[0, 1])
+        # the same sequences packed in reverse order
+        cu = inp["cu_seqlens"].tolist()
+        rev = {}
+        for key in ("q", "k", "v", "log_g", "beta"):
+            t = inp[key]
+            rev[key] = torch.cat([t[cu[b]:cu[b + 1]] for b in reversed(range(B))], dim=0)
+        rev["h0"] = torch.flip(inp["h0"], dims=[0]).contiguous()
+        rl = list(reversed(lens))
+        rev["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(rl)]), dtype=torch.int32)
+        out_r, hf_r, _ = gpu_prefill(rev, 64)
+        cr = rev["cu_seqlens"].tolist()
+        for b in range(B):
+            rb = B - 1 - b
+            assert torch.equal(_bits(out[cu[b]:cu[b + 1]]), _bits(out_r[cr[rb]:cr[rb + 1]])), (B, b)
+            assert torch.equal(_bits(hf[b]), _bits(hf_r[rb])), (B, b)
+
+
 def test_fp32_output_and_no_initial_state():
     inp = synth.prefill_inputs(1, 300, 2, 6, 128, 128, h0=False, seed=32)
     say("fp32 out")
