@@ -249,7 +249,9 @@ def bench_prefill(w, args, torch):
     ach = byt / (kern_ms * 1e-3) / 1e9
     traffic = measured_traffic(w.name)
     rec = {
-        "metric": "GDN chunked-prefill tokens/s (Hv=48, d=128, T=4576); % of MFMA/HBM peak",
+        "metric": (f"GDN chunked-prefill tokens/s (Hv={w.Hv}, d={w.dk}, "
+                   + (f"T={w.T}" if inp["cu_seqlens"] is None else f"{w.B} packed sequences, N={N}")
+                   + "); % of MFMA/HBM peak"),
         "value": N / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
