@@ -348,8 +348,6 @@ gdn_verify_d128_kernel(float* const* __restrict__ h_table, const TIn* q, const T
     const int sl = tid >> 5, cg = tid & 31;
     const int vh = blockIdx.x, b = blockIdx.y;
     const int kh = vh / (Hv / Hk);
-    const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(h_table[b] + (size_t)vh * D * D, (short)0,
-                                                        D * D * (int)sizeof(float), 0x00020000);
 
     // small rows, as raw elements (widened later): element tid + 256 u of
     // [k | q | v] (KR rows of 128 each; a thread past the end re-reads the
@@ -369,6 +367,12 @@ gdn_verify_d128_kernel(float* const* __restrict__ h_table, const TIn* q, const T
     const size_t goff = ((size_t)b * KR + (tid % KR)) * gb_stride + vh;
     const float g_in = gate[goff], b_in = beta[goff];
     mem_fence_here();
+    // the state pointer is read after the small rows are on their way, so
+    // that their loads do not wait for it
+    float* const hb = h_table[b];
+    asm volatile("" ::"s"(hb));
+    const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(hb + (size_t)vh * D * D, (short)0,
+                                                        D * D * (int)sizeof(float), 0x00020000);
 
     float4 hv[16];
 #pragma unroll
