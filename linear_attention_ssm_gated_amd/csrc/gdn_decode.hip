@@ -287,7 +287,8 @@ gdn_step_kernel(float* const* __restrict__ h_table, const TIn* __restrict__ q,
 // scalars are formed while the first rows are in flight.  The two row slices
 // of a wave are added with a cross-half lane swap, the four wave partials
 // through LDS.  The state is read with nontemporal loads (it is read once).
-constexpr int kLookahead = 8;   // state rows in flight per thread
+constexpr int kLookahead = 4;       // state rows in flight per thread: verify, fold
+constexpr int kLookaheadStep = 8;   // and in the K = 1 step (measured best for each)
 constexpr int kD = 128;
 constexpr int kKP = kD + 16;    // key rows padded: rows read together fall in different banks
 constexpr int kSP = 20;         // keys of slice s at [s][m] = row s + 8 m, padded
@@ -710,7 +711,7 @@ gdn_step_d128_kernel(float* const* __restrict__ h_table, const TIn* q, const TIn
 
     float4 hv[16];
 #pragma unroll
-    for (int m = 0; m < kLookahead; ++m) hv[m] = state_row(rs, sl + 8 * m, cg);
+    for (int m = 0; m < kLookaheadStep; ++m) hv[m] = state_row(rs, sl + 8 * m, cg);
     mem_fence_here();
 
 #pragma unroll
@@ -740,7 +741,7 @@ gdn_step_d128_kernel(float* const* __restrict__ h_table, const TIn* q, const TIn
     for (int m4 = 0; m4 < 4; ++m4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int m = 4 * m4 + e + kLookahead;
+            const int m = 4 * m4 + e + kLookaheadStep;
             if (m < 16) hv[m] = state_row(rs, sl + 8 * m, cg);
         }
         mem_fence_here();
