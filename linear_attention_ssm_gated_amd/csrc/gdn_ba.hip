@@ -14,11 +14,11 @@
 //
 // gdn_ba_partial_kernel, grid (token tiles of 128, k splits), one loader wave
 //   plus one compute wave per 32 outputs.  The loader streams the tile's x
-//   through a five-stage LDS ring by buffer->LDS DMA, 64 k per stage (16 KiB,
+//   through a three-stage LDS ring by buffer->LDS DMA, 64 k per stage (16 KiB,
 //   rows beyond m read as zero); each compute wave reads the eight 16-token A
 //   fragments of a k-step from LDS and the fragments of its own 32 weight
 //   rows straight from memory (the weight is small and stays in L2; those
-//   loads run four stages ahead in registers to cover its latency), on
+//   loads run five blocks ahead in registers to cover its latency), on
 //   v_mfma_f32_16x16x32_bf16, and writes its fp32 partial sums.  The number
 //   of k splits is chosen so that the grid fills the 256 compute units once
 //   (36 token tiles x 7 splits at the pages' 4576 tokens): a second round of a
@@ -34,10 +34,11 @@ namespace {
 constexpr int TM = 128;           // tokens per workgroup
 constexpr int RT = TM / 16;       // 16-token MFMA tiles per workgroup
 constexpr int KB = 64;            // k values per ring stage
-constexpr int NSTAGE = 5;         // ring stages
+constexpr int NSTAGE = 3;         // ring stages: deeper rings measured slower (each workgroup
+                                  // asks for NSTAGE - 1 stages at once at its start)
 constexpr int STAGE_BYTES = TM * KB * 2;   // 16 KiB
 constexpr int PIECES = STAGE_BYTES / 1024; // 1 KiB DMAs per stage (8 token rows each)
-constexpr int WAHEAD = 4;         // stages the weight loads run ahead
+constexpr int WAHEAD = 5;         // blocks the weight loads run ahead
 constexpr int OTW = 2;            // 16-output tiles per compute wave
 constexpr int CU_COUNT = 256;     // compute units the split count is sized for
 constexpr int MAX_SPLITS = 32;
