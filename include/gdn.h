@@ -50,19 +50,28 @@ typedef enum gdn_status {
     GDN_ERR_DTYPE = 5,         /* unknown dtype code */
     GDN_ERR_WORKSPACE = 6,     /* workspace smaller than gdn_prefill_workspace_bytes() */
     GDN_ERR_STASH = 7,         /* stash_seq_floats smaller than gdn_stash_seq_floats() */
-    GDN_ERR_K_ROWS = 8,        /* k_rows is not 4 */
+    GDN_ERR_K_ROWS = 8,        /* k_rows outside 1..8 */
     GDN_ERR_STRIDE = 9,        /* a row stride shorter than the heads it must hold */
     GDN_ERR_UNSUPPORTED = 10,  /* a documented branch that this library does not build */
     GDN_ERR_HIP = 11           /* the HIP runtime refused a launch (text: gdn_last_route()) */
 } gdn_status;
 
-/* Static text naming a status.  Never NULL. */
+/* Static text naming a status.  Never NULL.  Every refusal names its reason
+ * rather than failing silently, as the pages' launchers do with their checked
+ * errors on null pointers and bad shapes (ssm_gdn_woa.rs, the argument checks
+ * of the verify, fold and flag-clear launchers; ssm_ba_gates_hopper.rs, doc of
+ * the reject function: a refused fast path names the guard that refused it). */
 const char* gdn_status_string(int status);
 
-/* Thread-local text of the last call on this thread: the kernel entry that
- * was launched (or would be, for the *_plan functions), its grid, block and
- * LDS bytes, or the reason for a refusal.  Never NULL; valid until the next
- * call on the same thread. */
+/* Thread-local route line of the last call on this thread: the kernel entry
+ * that was launched (or would be, for the *_plan functions), its grid, block
+ * and LDS bytes, or the reason for a refusal.  Never NULL; valid until the
+ * next call on the same thread.  The rule that a log line names the entry that
+ * actually ran, with its launch geometry, is the pages' (ssm_gdn_tc_route.rs,
+ * the route-line functions and their tests).  With the environment variable
+ * GDN_LOG_ROUTE=1 (read once per process), each distinct route line is also
+ * written once to stderr, the first time a call produces it (the pages log
+ * each branch once, ssm_ba_gates_hopper.rs, its once-per-branch logging). */
 const char* gdn_last_route(void);
 
 /* ------------------------------------------------------------------------ */
@@ -126,6 +135,7 @@ int gdn_chunk_prefill_plan(const void* q, const void* k, const void* v,
                            int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                            const int32_t* cu_seqlens, int io_dtype, int out_dtype,
                            void* workspace, size_t workspace_bytes);
+
 
 /* ------------------------------------------------------------------------ */
 /* Write-on-accept decode verify of K draft rows (the pages' K = 4, and any K

@@ -10,11 +10,34 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <mutex>
+#include <set>
+#include <string>
 
 namespace {
 
 thread_local char t_route[512] = "no call yet";
+
+// GDN_LOG_ROUTE=1: each distinct route line goes to stderr once per process.
+bool log_routes()
+{
+    static const bool on = [] {
+        const char* e = getenv("GDN_LOG_ROUTE");
+        return e && e[0] == '1' && e[1] == 0;
+    }();
+    return on;
+}
+
+void log_route_once(const char* line)
+{
+    static std::mutex mu;
+    static std::set<std::string> seen;
+    std::lock_guard<std::mutex> lock(mu);
+    if (seen.insert(line).second) fprintf(stderr, "[gdn route] %s\n", line);
+}
 
 void set_route(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
 void set_route(const char* fmt, ...)
@@ -23,6 +46,7 @@ void set_route(const char* fmt, ...)
     va_start(ap, fmt);
     vsnprintf(t_route, sizeof(t_route), fmt, ap);
     va_end(ap);
+    if (log_routes()) log_route_once(t_route);
 }
 
 int refuse(int status, const char* who, const char* why)
@@ -139,6 +163,7 @@ int launched(hipError_t e)
     if (e == hipSuccess) return GDN_OK;
     size_t n = strlen(t_route);
     snprintf(t_route + n, sizeof(t_route) - n, " -- launch failed: %s", hipGetErrorString(e));
+    if (log_routes()) log_route_once(t_route);
     return GDN_ERR_HIP;
 }
 

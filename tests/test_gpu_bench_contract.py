@@ -76,3 +76,25 @@ def test_ba_line():
     rec = bench.with_copy_yardstick(bench.bench_ba(_args(name), torch), torch)
     _common(rec, name)
     assert rec["parity_max_rel_err_sampled_tokens"] <= 1e-4
+
+
+def test_default_line_carries_verify_and_fold():
+    """The default run (what the driver times) prints one JSON line whose extra
+    keys hold the K = 4 verify's and the fold's HBM rooflines."""
+    import os
+    import subprocess
+    import sys
+    say("bench contract: default line (subprocess)")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "bench.py", "--steps", "3", "--warmup", "1", "--no-cpu-baseline"],
+                       cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1
+    rec = json.loads(lines[0])
+    assert rec["config"]["workload"] == "prefill_t4576_h0"
+    for key in ("decode_verify_k4", "fold_k4"):
+        rf = rec[key]["roofline"]
+        assert rf["bound"] == "hbm" and rf["unit"] == "GB/s"
+        assert 0 < rf["frac"] < 1 and rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
+    assert rec["decode_verify_k4"]["parity_max_rel_err_out"] <= 2e-2

@@ -267,3 +267,27 @@ def test_ba_gates_workspace_size(lib):
     assert gdn.gdn_ba_gates_workspace_bytes(100, 96, 5120) == 27 * 100 * 96 * 4
     assert gdn.gdn_ba_gates_workspace_bytes(10, 8, 128) == 2 * 10 * 8 * 4
     assert gdn.gdn_ba_gates_workspace_bytes(10, 8, 64) == 1 * 10 * 8 * 4
+
+
+def test_route_log_once_per_line():
+    """GDN_LOG_ROUTE=1 writes each distinct route line to stderr once."""
+    import subprocess
+    import sys
+    code = (
+        "import linear_attention_ssm_gated_amd as gdn\n"
+        "lib = gdn.library()\n"
+        "for T in (128, 128, 256):\n"
+        "    lib.gdn_chunk_prefill_plan(1, 1, 1, 1, 1, None, 1, 1, 1, T, 16, 48, 128, 128, 64, None, 1, 1, 1, 1 << 40)\n"
+        "lib.gdn_chunk_prefill_plan(1, 1, 1, 1, 1, None, 1, 1, 1, 128, 16, 47, 128, 128, 64, None, 1, 1, 1, 1 << 40)\n"
+    )
+    env = dict(os.environ, GDN_LOG_ROUTE="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[gdn route]")]
+    assert len(lines) == 2, lines          # one launch route (same geometry for both T) + one refusal
+    assert any("refused" in l for l in lines)
+    env["GDN_LOG_ROUTE"] = "0"
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert "[gdn route]" not in r.stderr
