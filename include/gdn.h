@@ -136,6 +136,29 @@ int gdn_chunk_prefill_plan(const void* q, const void* k, const void* v,
                            const int32_t* cu_seqlens, int io_dtype, int out_dtype,
                            void* workspace, size_t workspace_bytes);
 
+/* gdn_chunk_prefill for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops and harnesses that forbid hipMalloc.
+ * Same arguments, kernels, results and route line as gdn_chunk_prefill, minus
+ * the workspace: the device scratch lives in a static array inside the library
+ * (GDN_NOALLOC_SCRATCH_BYTES per GPU, held from the library's first use on that
+ * GPU until the process ends).  The call allocates and frees nothing; the first
+ * call on a device looks the array's device address up once (the caller's
+ * current device must be the device of `stream`).  A call whose scratch,
+ * gdn_prefill_workspace_bytes(...), exceeds GDN_NOALLOC_SCRATCH_BYTES returns
+ * GDN_ERR_WORKSPACE and launches nothing (e.g. a 4576-token call at Hv = 48
+ * fits; a 29k-token packed call does not).  Every call on one GPU shares that
+ * GPU's scratch, so two calls that overlap on one GPU (different streams or
+ * threads without ordering between them) race; calls in one stream's order do
+ * not.  The scratch needs no clearing between calls.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v,
+                              const float* log_g, const float* beta,
+                              const float* h0, void* out, float* h_final,
+                              int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                              const int32_t* cu_seqlens, int io_dtype, int out_dtype,
+                              hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Write-on-accept decode verify of K draft rows (the pages' K = 4, and any K

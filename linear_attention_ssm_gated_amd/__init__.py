@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libgdn.so")
 GDN_F32 = 0
 GDN_BF16 = 1
 K_ROWS = 4
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
 
 _STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_HEAD_GROUPS",
@@ -34,6 +35,7 @@ SIGNATURES = {
     "gdn_prefill_workspace_bytes": (Z, [I, I, I, I, I, I, I, I, I]),
     "gdn_chunk_prefill": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, I, I, P, Z, P]),
     "gdn_chunk_prefill_plan": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, I, I, P, Z]),
+    "gdn_chunk_prefill_noalloc": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, I, I, P]),
     "gdn_stash_seq_floats": (Z, [I, I, I, I, I]),
     "gdn_flag_clear": (I, [P, P]),
     "gdn_decode_verify": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, I, I, P]),
@@ -127,6 +129,17 @@ def gdn_chunk_prefill(q, k, v, log_g, beta, h0, out, h_final, B, T, Hk, Hv, dk, 
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta), _ptr(h0), _ptr(out), _ptr(h_final),
         B, T, Hk, Hv, dk, dv, chunk, _ptr(cu_seqlens), _dtype_code(q), _dtype_code(out),
         _ptr(workspace), ws_bytes, _stream(stream)))
+    return last_route()
+
+
+def gdn_chunk_prefill_noalloc(q, k, v, log_g, beta, h0, out, h_final, B, T, Hk, Hv, dk, dv, chunk,
+                              cu_seqlens=None, stream=None):
+    """gdn_chunk_prefill with the library's static device scratch (no workspace,
+    no allocation).  Returns the route line."""
+    _check(library().gdn_chunk_prefill_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta), _ptr(h0), _ptr(out), _ptr(h_final),
+        B, T, Hk, Hv, dk, dv, chunk, _ptr(cu_seqlens), _dtype_code(q), _dtype_code(out),
+        _stream(stream)))
     return last_route()
 
 

@@ -183,6 +183,21 @@ gdn::PrefillArgs make_prefill(const void* q, const void* k, const void* v, const
 
 }  // namespace
 
+namespace gdn {
+int refuse_noalloc(size_t need)
+{
+    char why[160];
+    snprintf(why, sizeof(why), "the call needs %zu bytes of device scratch, more than the %zu-byte static scratch",
+             need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+    return refuse(GDN_ERR_WORKSPACE, "gdn_chunk_prefill_noalloc", why);
+}
+int hip_failure(const char* what, hipError_t e)
+{
+    set_route("%s failed: %s", what, hipGetErrorString(e));
+    return GDN_ERR_HIP;
+}
+}  // namespace gdn
+
 extern "C" {
 
 const char* gdn_status_string(int status)

@@ -114,6 +114,12 @@ __host__ __device__ inline size_t stash_head_floats(int dk, int dv, int io_dtype
     return (size_t)k_rows * dv + k_rows + (io_dtype == 1 ? (kd + 1) / 2 : kd);
 }
 
+// Route-line helpers of the C ABI layer (gdn_api.hip) for the other entry
+// files: a refusal of a call whose scratch exceeds the static scratch, and a
+// failed runtime call.  Both return the status to hand back.
+int refuse_noalloc(size_t need);
+int hip_failure(const char* what, hipError_t e);
+
 // ---- element helpers ------------------------------------------------------
 // bf16 is carried as its 16 raw bits; widening is exact.
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in gdn.h but not exported"
     assert set(names) == set(gdn.SIGNATURES), "binding and header disagree"
@@ -267,6 +267,27 @@ def test_ba_gates_workspace_size(lib):
     assert gdn.gdn_ba_gates_workspace_bytes(100, 96, 5120) == 27 * 100 * 96 * 4
     assert gdn.gdn_ba_gates_workspace_bytes(10, 8, 128) == 2 * 10 * 8 * 4
     assert gdn.gdn_ba_gates_workspace_bytes(10, 8, 64) == 1 * 10 * 8 * 4
+
+
+def test_noalloc_refuses_before_touching_a_device(lib):
+    """gdn_chunk_prefill_noalloc validates shapes and its scratch limit on the
+    host first: these refusals come back on a machine without a GPU."""
+    text = open(HEADER).read()
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == gdn.NOALLOC_SCRATCH_BYTES
+    big = dict(B=1, T=40000, Hk=16, Hv=48)
+    need = gdn.gdn_prefill_workspace_bytes(big["B"], big["T"], big["Hk"], big["Hv"], 128, 128, 64, 1)
+    assert need > gdn.NOALLOC_SCRATCH_BYTES
+    st = lib.gdn_chunk_prefill_noalloc(X, X, X, X, X, None, X, X, 1, 40000, 16, 48, 128, 128, 64,
+                                       None, 1, 1, None)
+    assert st == 6, gdn.last_route()
+    assert "static scratch" in gdn.last_route()
+    st = lib.gdn_chunk_prefill_noalloc(X, X, X, X, X, None, X, X, 1, 128, 16, 47, 128, 128, 64,
+                                       None, 1, 1, None)
+    assert st == 3   # Hv not a multiple of Hk, refused by the shared validation
+    st = lib.gdn_chunk_prefill_noalloc(None, X, X, X, X, None, X, X, 1, 128, 16, 48, 128, 128, 64,
+                                       None, 1, 1, None)
+    assert st == 1
 
 
 def test_route_log_once_per_line():
