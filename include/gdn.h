@@ -97,8 +97,9 @@ const char* gdn_last_route(void);
  *   h0, h_final: [B][Hv][dk][dv] fp32.  h0 == NULL means zero states;
  *   h_final == NULL means the final states are not written; h0 == h_final is
  *   allowed (updated in place).  q, k, v: io_dtype; out: out_dtype; log_g
- *   (natural log of the decay, <= 0) and beta: fp32.
- *   Precondition: within any chunk the sum of log_g stays above -80.
+ *   (natural log of the decay, <= 0, finite) and beta: fp32.  Any finite
+ *   gates are taken: every decay factor either kernel forms is exp of a
+ *   non-positive difference of cumulative log decays.
  *
  * Kernels: io_dtype == GDN_BF16 with dk == dv == 128 and chunk == 64 runs the
  * bf16-MFMA spine (fp32 state and accumulators).  Every other accepted shape
@@ -109,10 +110,11 @@ const char* gdn_last_route(void);
  * and packed = (cu_seqlens != NULL).  The MFMA route keeps a chunk table of
  * packed sequences (their first chunks, and for up to 256 sequences their
  * order by length, longest first, in which the state walks are dispatched),
- * T = (I + A)^-1 of every (chunk, v-head) and
- * S = lower_incl(Q K^T) of every (chunk, k-head) there, as 64 x 64 bf16
- * matrices (8 KiB each; the granules above their diagonals are never written
- * or read); the generic route needs none.
+ * and for every (chunk, v-head) T diag(beta) with T = (I + A)^-1 and
+ * P = Gamma o lower_incl(Q K^T), each as 64 x 64 bf16 in MFMA fragment order
+ * (6 KiB; the granules above their diagonals are never written or read)
+ * followed by the chunk's per-row decay factors exp(G_r), exp(G_L - G_r) and
+ * exp(G_L) (1 KiB), 7 KiB per matrix; the generic route needs none.
  * The library reads and writes the workspace only inside the call's stream
  * order; its contents need no initialisation.
  */

@@ -7,36 +7,31 @@
 //   producer behind the spine, ssm_gdn_tc_route.rs, doc of the pipe spine):
 //     G = cumsum(log_g), Gamma_rs = exp(G_r - G_s) for s <= r
 //     A = strict_lower(diag(beta) (Gamma o K K^T)),  T = (I + A)^-1   (per v-head)
-//     S = lower_incl(Q K^T)                                            (per k-head)
+//     T_b = T diag(beta),  P = Gamma o lower_incl(Q K^T)              (per v-head)
 //   K K^T and Q K^T run on bf16 MFMA with fp32 accumulation; T is solved in
 //   fp32 (16x16 diagonal blocks by forward substitution on VALU, the blocks
-//   below them on fp32 MFMA); T and S are stored as bf16 in the workspace,
-//   their granules above the diagonal left unwritten (they are zero, and the
-//   spine never reads them from memory).  The output's decay-weighted
-//   P = Gamma o S is never formed: Gamma_rs = gm_r / gm_s with gm = exp(G)
-//   factors out of the product (see the spine).
+//   below them on fp32 MFMA); T_b and P are stored as bf16 MFMA fragments in
+//   the workspace, their granules above the diagonal left unwritten (they are
+//   zero, and the spine never reads them from memory).  P carries the decay
+//   exactly (every factor exp(G_r - G_s) with s <= r is at most 1), so no
+//   rescaling in the spine can overflow, whatever the gates.
 //
-// gdn_spine_kernel, one workgroup per (sequence, v-head, 32 dv columns), two
-//   waves of 16 columns each, walking the chunks in order: the state spine
-//   (same page, the tensor-core spine: bf16 MFMA operands, the fp32
-//   accumulators are the recurrent state, h stays f32).  Per chunk:
-//     X = K h, Y = Q h                       (state as the bf16 B operand)
-//     R = diag(beta) (V - diag(gamma) X)
-//     Delta = T R                            (= U - W h of the WY form)
-//     O = diag(gamma) Y + (Gamma o S) Delta
-//       = diag(gamma / gamma_L) (gamma_L Y + S (el o Delta)),  el = exp(G_L - G)
-//     h <- gamma_L h + K^T (el o Delta)
+// gdn_spine_kernel, one workgroup per (sequence, v-head, 32 dv columns),
+//   walking the chunks in order: the state spine (same page, the tensor-core
+//   spine: bf16 MFMA operands, the fp32 accumulators are the recurrent state,
+//   h stays f32).  Per chunk:
+//     X = K h,  R = V - gm X,  Delta = T_b R      (= U - W h of the WY form)
+//     O = gm (Q h) + P Delta
+//     h <- gamma_L h + K^T (el o Delta),  el = exp(G_L - G), gm = exp(G)
 //   Columns of h evolve independently (the dv split of the pages' SPLIT
-//   variants), so the waves never exchange data.
+//   variants), so the workgroups never exchange data.
 //
 // MFMA operand convention (v_mfma_f32_16x16x32_bf16, 64 lanes, lane = 16 g + i):
-// the hardware pairs element e of A in lane 16g+m with element e of B in lane
-// 16g+n and sums over (g, e).  We assign the 32 k indices of one k-step as
-//     k(g, e) = 4g + e        for e < 4
-//     k(g, e) = 16 + 4g + e-4 for e >= 4
-// so that a 16x16 fp32 accumulator tile (lane 16g+n holds rows 4g..4g+3 of
-// column n) of two consecutive k-blocks IS a B operand after rounding to bf16,
-// and an A operand is two 8-byte LDS reads of its row.
+// lane group g supplies k-values 8g .. 8g+7 of each 32-wide k-step.  A 16x16
+// fp32 accumulator tile holds rows 4g .. 4g+3 of column n in lane 16g + n;
+// when row m of tile t stands for index sig(t, m) = 32 (t/2) + 8 (m/4) +
+// 4 (t%2) + m%4, tiles 2j and 2j+1 ARE the B operand of k-step j after
+// rounding to bf16, and every A fragment is one 16-byte read of its row.
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -46,7 +41,26 @@ constexpr int C = 64;        // chunk rows
 constexpr int D = 128;       // dk = dv
 constexpr int TILE_COLS = 32;            // dv columns per spine workgroup
 constexpr int N_TILES = D / TILE_COLS;   // 4
-constexpr int SLOT_ELEMS = C * C;        // one 64 x 64 bf16 matrix: T per (chunk, v-head), S per (chunk, k-head)
+
+// Workspace slots: T_b and P per (chunk, v-head), each the six 1 KiB MFMA
+// fragments of a 64 x 64 bf16 lower-triangular matrix M; fragment f covers
+// output tile cb(f) and k-step kk(f) (f = 0..3: (f, 0); f = 4: (2, 1); f = 5:
+// (3, 1)), and its lane l = 16 g + n holds M[sig(cb, n)][32 kk + 8 g .. + 7] at
+// byte 16 l.  Granules wholly above the diagonal are neither written nor read.
+constexpr int NFRAG = 6;
+constexpr int FRAG_BYTES = 1024;
+constexpr int SLOT_BYTES = NFRAG * FRAG_BYTES;
+// each slot also carries the chunk's per-row decay factors after the fragments
+// (1 KiB for T_b's, 256 B for P's)
+constexpr int SLOT_STRIDE = SLOT_BYTES + 1024;
+__host__ __device__ constexpr int frag_cb(int f) { return f < 4 ? f : f - 2; }
+__host__ __device__ constexpr int frag_kk(int f) { return f < 4 ? 0 : 1; }
+// first index of tile t under sig(t, .), and the index of row m of tile t
+__host__ __device__ constexpr int sig_tile(int t) { return 32 * (t >> 1) + 4 * (t & 1); }
+__host__ __device__ constexpr int sig_row(int t, int m) { return sig_tile(t) + 8 * (m >> 2) + (m & 3); }
+__host__ __device__ constexpr bool frag_live(int f, int l) {
+    return 32 * frag_kk(f) + 8 * (l >> 4) <= sig_row(frag_cb(f), l & 15);
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -72,16 +86,6 @@ __device__ __forceinline__ short bf16_bits(float x) {
 __device__ __forceinline__ s16x8 frag_b(f32x4 lo, f32x4 hi) {
     return s16x8{bf16_bits(lo[0]), bf16_bits(lo[1]), bf16_bits(lo[2]), bf16_bits(lo[3]),
                  bf16_bits(hi[0]), bf16_bits(hi[1]), bf16_bits(hi[2]), bf16_bits(hi[3])};
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
 }
 
 // Rows of sequence b: [row0, row0 + len).
@@ -214,10 +218,11 @@ __device__ __forceinline__ s16x8 lds_read16(const unsigned char* p) {
 // v-heads), one wave per v-head.  The workgroup stages the chunk's K and Q
 // rows in LDS once; each wave then forms, for its v-head,
 //   A = strict_lower(beta_r exp(G_r - G_s) (K K^T)_rs),   T = (I + A)^-1,
-// and writes T as a bf16 64 x 64 row-major matrix to the (chunk, v-head)
-// slot.  The k-head's S = lower_incl(Q K^T) (no decay) is written once, its
-// ten 16 x 16 tiles shared out over the first group's waves.  The waves never
-// wait for each other after the staging.
+// and writes T_b = T diag(beta) to the (chunk, v-head) slot as bf16 MFMA
+// fragments.  The ten 16 x 16 tiles of Q K^T are shared out over the group's
+// waves; the wave that forms a tile writes P = exp(G_r - G_s) (Q K^T)_rs
+// (lower, with the diagonal) of every v-head of the group for it.  The waves
+// never wait for each other after the staging.
 //
 // Gram tiles are formed above the diagonal, tile (m, i) = K_m K_i^T and
 // K_m Q_i^T (16-row blocks, m <= i), so that lane (g, n) register s holds
@@ -272,7 +277,7 @@ extern __shared__ __attribute__((aligned(1024))) float prep_lds[];
 __global__ void __launch_bounds__(256, 3)
 gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const float* __restrict__ log_g, const float* __restrict__ beta,
-                   uint16_t* __restrict__ tslots, uint16_t* __restrict__ sslots, int B, int T,
+                   unsigned char* __restrict__ tbs, unsigned char* __restrict__ pps, int B, int T,
                    int Hk, int Hv, const int32_t* __restrict__ cu,
                    const int32_t* __restrict__ chunk_base, int nc_dense)
 {
@@ -332,8 +337,23 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         const rsrc_t rb_ = make_rsrc(beta + ru * Hv + vh, gb_bytes);
         const float gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)lane * Hv * 4u, 0, 0));
         const float bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb_, (uint32_t)lane * Hv * 4u, 0, 0));
-        sG[lane] = wave_scan_dpp(gv) * 1.4426950408889634f;
+        const float Gl2 = wave_scan_dpp(gv) * 1.4426950408889634f;
+        sG[lane] = Gl2;
         sBt[lane] = bv;
+        if (h < G) {
+            // the spine's per-row decay factors of this (chunk, v-head), rows
+            // past a partial chunk keeping the last row's G: (gm, el, gamma_L)
+            // in recurrence-lane order after T_b, gm in output-lane order
+            // after P (row = sig(t, m))
+            const float GLl2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gl2), 63));
+            const float gm = __builtin_amdgcn_exp2f(Gl2), el = __builtin_amdgcn_exp2f(GLl2 - Gl2);
+            const int t = 2 * (lane >> 5) + ((lane >> 2) & 1), m = 4 * ((lane >> 3) & 3) + (lane & 3);
+            unsigned char* tb_slot = tbs + ((size_t)x * Hv + vh) * SLOT_STRIDE;
+            unsigned char* pp_slot = pps + ((size_t)x * Hv + vh) * SLOT_STRIDE;
+            *reinterpret_cast<float4*>(tb_slot + SLOT_BYTES + 16 * (16 * (m >> 2) + 4 * t + (m & 3))) =
+                make_float4(gm, el, __builtin_amdgcn_exp2f(GLl2), 0.f);
+            reinterpret_cast<float*>(pp_slot + SLOT_BYTES)[4 * m + t] = gm;
+        }
     }
     // the DMA is inline assembly the compiler does not track: wait for it
     // explicitly, then let every wave see every wave's rows
@@ -351,13 +371,12 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         Gc[i] = f32x4{t4.x, t4.y, t4.z, t4.w};
     }
 
-    // Gram tiles by block column i: S tiles leave at once, A stays in
-    // registers.  S tile number i (i + 1) / 2 + m belongs to wave (that
-    // number) % nw of the first group.
-    uint16_t* dstT = tslots + ((size_t)x * Hv + vh) * SLOT_ELEMS;
-    uint16_t* dstS = sslots + ((size_t)x * Hk + kh) * SLOT_ELEMS;
+    // Gram tiles by block column i: P tiles leave at once, A stays in
+    // registers.  Q K^T tile number i (i + 1) / 2 + m belongs to wave (that
+    // number) % nw of the group.
+    unsigned char* dstT = tbs + ((size_t)x * Hv + vh) * SLOT_STRIDE;
     const bool live = h < G;
-    const bool s_group = blockIdx.z == 0;
+    const int nlive = min(nw, G - (int)blockIdx.z * nw);   // live v-heads of the group
     s16x8 kf[4][4];
     f32x4 Aoff[6];   // A_im, m < i, index (i - 1) i / 2 + m
     f32x4 Adg[4];    // A_ii: register s = A_ii[n][4g + s]
@@ -372,7 +391,7 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
 #pragma unroll
         for (int m = 0; m <= i; ++m) {
-            const bool mine = s_group && ((i * (i + 1) / 2 + m) % nw) == w;   // wave-uniform
+            const bool mine = ((i * (i + 1) / 2 + m) % nw) == w;   // wave-uniform
             f32x4 kk_acc = zero4(), kq_acc = zero4();
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) kk_acc = mfma_bf16(kf[m][kk], kf[i][kk], kk_acc);
@@ -380,22 +399,38 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) kq_acc = mfma_bf16(kf[m][kk], qf[kk], kq_acc);
             }
-            f32x4 av, sv;
+            f32x4 av;
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
                 const float e = __builtin_amdgcn_exp2f(Gr[i] - Gc[m][s2]);
                 av[s2] = Bt[i] * e * kk_acc[s2];
-                sv[s2] = kq_acc[s2];
-                if (m == i) {   // A strictly lower, S lower with the diagonal
-                    av[s2] = (n > 4 * g + s2) ? av[s2] : 0.f;
-                    sv[s2] = (n >= 4 * g + s2) ? sv[s2] : 0.f;
-                }
+                if (m == i) av[s2] = (n > 4 * g + s2) ? av[s2] : 0.f;   // A strictly lower
             }
             if (m == i) Adg[i] = av;
             else Aoff[(i - 1) * i / 2 + m] = av;
             if (mine) {
-                const s16x4 sb = s16x4{bf16_bits(sv[0]), bf16_bits(sv[1]), bf16_bits(sv[2]), bf16_bits(sv[3])};
-                *reinterpret_cast<s16x4*>(dstS + (16 * i + n) * C + 16 * m + 4 * g) = sb;
+                // this lane's four entries: row rho = 16 i + n, columns c0 .. c0 + 3;
+                // rho = sig(cb, np), and the columns are half `hf` of lane
+                // (gp, np)'s granule in fragment (cb, kk)
+                const int rho = 16 * i + n, c0 = 16 * m + 4 * g;
+                const int cb = 2 * (rho >> 5) + ((rho >> 2) & 1), np = 4 * ((rho >> 3) & 3) + (rho & 3);
+                const int kk2 = c0 >> 5, gp = (c0 & 31) >> 3, hf = (c0 >> 2) & 1;
+                const uint32_t off = FRAG_BYTES * (kk2 == 0 ? cb : cb + 2) + 16u * (16 * gp + np) + 8u * hf;
+                for (int hh = 0; hh < nlive; ++hh) {   // every v-head of the group
+                    const float* sGh = prep_lds + prep_gb_base(nw) + hh * 2 * C;
+                    const float gr = sGh[16 * i + n];
+                    const float4 gc = *reinterpret_cast<const float4*>(sGh + 16 * m + 4 * g);
+                    const float gcv[4] = {gc.x, gc.y, gc.z, gc.w};
+                    f32x4 pv;
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        pv[s2] = __builtin_amdgcn_exp2f(gr - gcv[s2]) * kq_acc[s2];
+                        if (m == i) pv[s2] = (n >= 4 * g + s2) ? pv[s2] : 0.f;   // P lower with the diagonal
+                    }
+                    const int vh2 = kh * G + (int)blockIdx.z * nw + hh;
+                    *reinterpret_cast<s16x4*>(pps + ((size_t)x * Hv + vh2) * SLOT_STRIDE + off) =
+                        s16x4{bf16_bits(pv[0]), bf16_bits(pv[1]), bf16_bits(pv[2]), bf16_bits(pv[3])};
+                }
             }
         }
     }
@@ -477,95 +512,83 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         wave_lds_sync();
     }
 
-    // T rows -> workspace as bf16: the 8-column granules that reach the
-    // diagonal (8 cg <= r); those wholly above it are zero and not written
-    const int cg = lane & 7, jb = cg >> 1;
+    // T_b = T diag(beta) -> workspace as bf16 fragments: lane l of fragment f
+    // holds row sig(cb, l % 16), columns c0 .. c0 + 7 (c0 = 32 kk + 8 (l / 16)),
+    // when that granule reaches the diagonal
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int r = (lane >> 3) + 8 * p, ib = p >> 1, rr = r & 15;
-        if (8 * cg <= r) {
+    for (int f = 0; f < NFRAG; ++f) {
+        if (frag_live(f, lane)) {
+            const int r = sig_row(frag_cb(f), n), c0 = 32 * frag_kk(f) + 8 * g;
+            const int ib = r >> 4, jb = c0 >> 4, rr = r & 15;
             const float* blk = lds + (jb == ib ? 272 * ib : 1088 + 256 * ((ib - 1) * ib / 2 + jb));
-            const int c0 = 2 * (cg & 1);   // first 4-column granule
+            const int q4 = (c0 & 15) >> 2;   // first 4-column granule within the block
             const float* row = blk + 16 * prow(rr);
-            const float4 a = *reinterpret_cast<const float4*>(row + 4 * (c0 ^ (rr >> 2)));
-            const float4 e = *reinterpret_cast<const float4*>(row + 4 * ((c0 + 1) ^ (rr >> 2)));
-            *reinterpret_cast<s16x8*>(dstT + r * C + 8 * cg) =
-                s16x8{bf16_bits(a.x), bf16_bits(a.y), bf16_bits(a.z), bf16_bits(a.w),
-                      bf16_bits(e.x), bf16_bits(e.y), bf16_bits(e.z), bf16_bits(e.w)};
+            const float4 a = *reinterpret_cast<const float4*>(row + 4 * (q4 ^ (rr >> 2)));
+            const float4 e = *reinterpret_cast<const float4*>(row + 4 * ((q4 + 1) ^ (rr >> 2)));
+            const float4 b0 = *reinterpret_cast<const float4*>(sBt + c0);
+            const float4 b1 = *reinterpret_cast<const float4*>(sBt + c0 + 4);
+            *reinterpret_cast<s16x8*>(dstT + FRAG_BYTES * f + 16 * lane) =
+                s16x8{bf16_bits(a.x * b0.x), bf16_bits(a.y * b0.y), bf16_bits(a.z * b0.z), bf16_bits(a.w * b0.w),
+                      bf16_bits(e.x * b1.x), bf16_bits(e.y * b1.y), bf16_bits(e.z * b1.z), bf16_bits(e.w * b1.w)};
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// The state spine.  One workgroup per (sequence, v-head, 32 dv columns), six
-// waves in three roles:
-//   recurrence waves (2, 3): each owns 16 columns of the state h in MFMA
-//     accumulators and walks the chunks in order: X = K h,
-//     R = beta (V - gm X), Delta = T R, h <- gamma_L h + K^T (el Delta).
-//     It hands the chunk's bf16 state (before the update) and el Delta to
-//     its output wave through a double-buffered LDS exchange.
-//   output waves (0, 1): one chunk behind, O = (gm / gm_L) (gm_L (Q h) +
-//     S (el Delta)) for the same 16 columns, which is gm (Q h) + (Gamma o S)
-//     Delta because Gamma_rs = gm_r / gm_s and el_s = gm_L / gm_s.  The
-//     output path does not feed back into the state, so it leaves the
-//     recurrence waves' critical path.
-//   loader waves (4, 5): fill the recurrence waves' three-stage LDS ring two
-//     chunks ahead, and the output waves' two-slot ring of Q and S one
-//     chunk ahead, by buffer->LDS DMA (a 64-lane DMA writes lane l's 16 bytes
-//     at base + 16 l; lanes beyond the buffer's range write zeros, which pads
-//     a partial chunk and fills the granules of T and S above the diagonal,
-//     which are not in memory), and prepare the chunk's decay factors.
-// All six waves meet at one barrier per chunk.
+// The state spine.  One workgroup per (sequence, v-head, 32 dv columns), four
+// waves, one per SIMD (wave w runs on SIMD w):
+//   recurrence waves (2, 3): 16 columns each; the fp32 state h lives in MFMA
+//     accumulators and walks the chunks in order:
+//       X = K h,  R = V - gm X,  Delta = T_b R,  h <- gamma_L h + K^T (el Delta)
+//     where T_b = T diag(beta), so Delta = T_b V - T_b diag(gm) K h is the WY
+//     form's U - W h.  The chunk's bf16 state and Delta go to the output wave
+//     of the same columns through a double-buffered LDS exchange.
+//   output waves (0, 1): one chunk behind, O = gm (Q h) + P Delta for the
+//     same 16 columns (P = Gamma o lower_incl(Q K^T) from the workspace), and
+//     the loaders of the workgroup's LDS rings, wave 0 the K rows and P,
+//     wave 1 the V rows and Q.
+// An LDS read costs ~450 cycles, so a recurrence wave reads every operand of
+// chunk c + 1 while it computes chunk c: the K fragments of X and the
+// transposed K fragments of the update from the ring, V from the ring, and
+// T_b with the per-row decay factors straight from the workspace (seven
+// contiguous 1 KiB loads; the compute unit's vector-memory path is shared
+// with the ring DMA, so the recurrence waves keep their own memory loads few).
+// The per-row factors reach the lanes that need them by a DPP row broadcast:
+// recurrence lane (g, 4 cb + r) holds (gm, el) of row sig(cb, 4g + r), which
+// every lane of its row of 16 needs for accumulator register r of tile cb.
 //
-// MFMA k-slots.  Lane group g (lanes 16g .. 16g+15) supplies k-values
-// 8g .. 8g+7 of each 32-wide k-step, so every A fragment is one 16-byte read.
-// An accumulator tile holds rows 4g .. 4g+3 in lane group g; tiles 2j and
-// 2j+1 form the B operand of k-step j without any exchange when row m of
-// tile t stands for index
-//     sig(t, m) = 32 (t/2) + 8 (m/4) + 4 (t%2) + m%4.
-// The state tiles h[db] (state rows) and the chunk-row tiles X, Y, Delta and
-// O all use this map.
-//
-// Stage layout.  Rows are dense; the 16-byte granules of a row are permuted
-// so that every fragment read is free of bank conflicts (64 banks of 4
-// bytes; a 16-byte read serves 8 lanes per pass, an 8-byte read 16):
-//   K (64 rows x 256 B): granule q of row r at q ^ fK(r), fK(r) = 4 (r%4) + (r/8)%2
-//   T (64 rows x 128 B): granule q of row r at q ^ fT(r), fT(r) = (r/2)%2 + 2 ((r/8)%2)
-//   V (64 rows x  64 B: the workgroup's 32 columns)
-//   log_g, beta as loaded (64 fp32 each), then the prepared decay factors
-//   gm_r = exp(G_r) and el_r = exp(G_L - G_r), and gamma_L = exp(G_L).
-constexpr int ST_K = 0;
-constexpr int ST_T = 16384;
-constexpr int ST_V = 24576;
-constexpr int ST_G = 28672;
-constexpr int ST_B = 28928;
-constexpr int ST_GM = 29184;
-constexpr int ST_EL = 29440;
-constexpr int ST_SO = 29696;
-constexpr int ST_BYTES = 29712;
-constexpr int N_STAGES = 3;
-constexpr int DMA_K_WAVE = 17;    // loader 0: 16 K + 1 log_g (then 8 S for the output ring)
-constexpr int DMA_TV_WAVE = 13;   // loader 1: 8 T + 4 V + 1 beta (then 16 Q for the output ring)
-// The exchange: per output/recurrence pair and parity of the chunk, the
-// bf16 state fragments (4 x 1 KB) and the bf16 el Delta fragments (2 x 1 KB),
-// each stored lane-major (lane l's 16 bytes at 16 l).  Then 256 bytes of
-// decay factors per output wave.
-// The output ring: per slot Q (64 rows x 256 B, laid out as K) and S (64
-// rows x 128 B, laid out as T).
-constexpr int EX_BASE = 89344;                 // N_STAGES * ST_BYTES rounded up to 1 KB
-constexpr int EX_SLOT = 6144;
-constexpr int OR_BASE = EX_BASE + 4 * EX_SLOT;
-constexpr int OR_Q = 0;
-constexpr int OR_S = 16384;
-constexpr int OR_SLOT = 24576;
-constexpr int OUT_SCR = OR_BASE + 2 * OR_SLOT;
-constexpr int SPINE_LDS = OUT_SCR + 2 * 256;
+// LDS (bytes).  Recurrence ring stage (four stages, three chunks ahead):
+//   K rows (64 x 256 B), granule q of row r at q ^ fK(r), fK(r) = 4 (r%4) + (r/8)%2
+//   V rows of the workgroup's 32 columns (64 x 64 B)
+// Output ring slot (two slots, each filled one step before it is read): Q
+// rows laid out as K, the six P fragments, gm in output-lane order [n][cb].
+// Exchange, per recurrence wave and chunk parity: the bf16 state fragments
+// (4 x 1 KiB) and the bf16 Delta fragments (2 x 1 KiB), lane-major.
+constexpr int RS_K = 0;
+constexpr int RS_V = 16384;
+constexpr int RS_BYTES = 20480;
+constexpr int N_RS = 4;
+constexpr int OS_BASE = N_RS * RS_BYTES;
+constexpr int OS_Q = 0;
+constexpr int OS_P = 16384;
+constexpr int OS_GM = OS_P + SLOT_BYTES;
+constexpr int OS_BYTES = 23552;
+constexpr int EX_BASE = OS_BASE + 2 * OS_BYTES;
+constexpr int EX_BYTES = 6144;
+constexpr int SPINE_LDS = EX_BASE + 4 * EX_BYTES;
 static_assert(SPINE_LDS <= 160 * 1024, "the spine's LDS");
-static_assert(EX_BASE >= N_STAGES * ST_BYTES, "exchange after the ring");
+static_assert(OS_GM + 256 <= OS_BYTES, "output slot layout");
+// DMA operations per chunk: output wave 0 loads K (16 pieces) into the ring
+// and P (6 pieces) with gm (1) into an output slot; output wave 1 loads V (4
+// pieces) into the ring and Q (16 pieces) into the output slot.  Each also
+// stores its 16 columns of a chunk's outputs (4 stores).
+constexpr int DMA_REC0 = 16, DMA_OUT0 = 7;
+constexpr int DMA_REC1 = 4, DMA_OUT1 = 16;
+constexpr int OUT_STORES = 4;
 
-// Batches of buffer->LDS DMAs into consecutive 1 KB pieces of LDS starting
-// at the LDS byte address `lds`: M0 is set once and advanced by one scalar
-// add per piece, and every lane and SGPR offset is precomputed.
+// Batches of buffer->LDS DMAs into consecutive 1 KiB pieces of LDS starting at
+// the LDS byte address `lds`: M0 is set once and advanced by one scalar add per
+// piece; lane and SGPR offsets are precomputed.
 __device__ __forceinline__ void dma_x4(const Rsrc& r, uint32_t lds, uint32_t v0, uint32_t v1,
                                        uint32_t v2, uint32_t v3, uint32_t s0, uint32_t s1,
                                        uint32_t s2, uint32_t s3) {
@@ -577,7 +600,19 @@ __device__ __forceinline__ void dma_x4(const Rsrc& r, uint32_t lds, uint32_t v0,
                  :: "s"(lds), "s"(r.d), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(s0), "s"(s1), "s"(s2), "s"(s3)
                  : "memory", "m0", "scc");
 }
-__device__ __forceinline__ void dma_x8(const Rsrc& r, uint32_t lds, const uint32_t (&v)[8], const uint32_t (&so)[8]) {
+__device__ __forceinline__ void dma_x6(const Rsrc& r, uint32_t lds, const uint32_t (&v)[6], const uint32_t (&so)[6]) {
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "buffer_load_dwordx4 %2, %1, %8 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %3, %1, %9 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %4, %1, %10 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %5, %1, %11 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %6, %1, %12 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
+                 "buffer_load_dwordx4 %7, %1, %13 offen lds"
+                 :: "s"(lds), "s"(r.d), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]),
+                    "s"(so[0]), "s"(so[1]), "s"(so[2]), "s"(so[3]), "s"(so[4]), "s"(so[5])
+                 : "memory", "m0", "scc");
+}
+__device__ __forceinline__ void dma_x8(const Rsrc& r, uint32_t lds, const uint32_t (&v)[8], const uint32_t* so) {
     asm volatile("s_mov_b32 m0, %0\n\t"
                  "buffer_load_dwordx4 %2, %1, %10 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
                  "buffer_load_dwordx4 %3, %1, %11 offen lds\n\ts_add_u32 m0, m0, 0x400\n\t"
@@ -597,19 +632,15 @@ __device__ __forceinline__ uint32_t lds_u32(const unsigned char* p) {
 }
 
 // A workgroup barrier without the fences of __syncthreads, whose vmcnt(0)
-// would wait for the DMA of later chunks too.  Producers wait for their own
-// writes (wait_vmcnt, wait_lgkm0) before they arrive.
+// would wait for the DMA of later chunks too.  Each wave waits for its own
+// LDS writes and DMA before it arrives.
 __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
-// s_waitcnt vmcnt(n) for the DMA counts used here, other counters free (gfx9
-// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+// s_waitcnt vmcnt(N), other counters free (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt 6:4, lgkmcnt 11:8)
 #define GDN_VMCNT(N) (((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    if (n == DMA_K_WAVE) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_K_WAVE));
-    else if (n == DMA_TV_WAVE) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_TV_WAVE));
-    else __builtin_amdgcn_s_waitcnt(GDN_VMCNT(0));
-}
-#undef GDN_VMCNT
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+// s_waitcnt lgkmcnt(N), other counters free
+#define GDN_LGKMCNT(N) (15 | (3 << 14) | (7 << 4) | ((N) << 8))
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(GDN_LGKMCNT(0)); }
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ s16x4 lds_read_tr(const unsigned char* p) {
@@ -618,291 +649,316 @@ __device__ __forceinline__ s16x4 lds_read_tr(const unsigned char* p) {
 __device__ __forceinline__ s16x8 join(s16x4 a, s16x4 b) {
     return s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
-// first index of tile t under sig(t, .), and of lane group g within it
-__device__ __forceinline__ constexpr int sig_tile(int t) { return 32 * (t >> 1) + 4 * (t & 1); }
 
-// Per-lane DMA byte offsets of a loader wave (chunk-independent).
+// Lane j of each row of 16 lanes, to every lane of that row.
+template <int J>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xf, 0xf, false));
+}
+
+// Per-lane DMA byte offsets of the output waves, chunk-independent.
 struct LoadOffsets {
-    uint32_t k[2];    // K rows, by (j/2)%2 of the 4-row block j
-    uint32_t t[2];    // T rows, by j%2 of the 8-row block j
-    uint32_t v;       // V
-    uint32_t gb;      // log_g / beta
-    // per 1 KB piece j: lane offsets and (uniform) SGPR offsets
     uint32_t kv[8], ks[16];   // K and Q pieces 0..15 (lane offsets repeat every 8)
-    uint32_t tv[8], ts[8];    // T and S pieces 0..7 (lanes above the diagonal out of range)
-    uint32_t vs[4];           // V pieces 0..3
+    uint32_t v, vs[4];        // V pieces 0..3
+    uint32_t pv[NFRAG], ps[NFRAG];   // P fragments (granules above the diagonal out of range)
+    uint32_t gmv;             // gm, 64 lanes x 4 bytes
 };
 
 __device__ __forceinline__ LoadOffsets load_offsets(int lane, int Hk, int Hv) {
     LoadOffsets o;
     const uint32_t k_row = (uint32_t)Hk * D * 2u, v_row = (uint32_t)Hv * D * 2u;
-    const int rr = lane >> 4, p = lane & 15, p8 = lane & 7, hb = (lane >> 4) & 1;
+    const int rr = lane >> 4, p = lane & 15;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        o.k[s] = rr * k_row + (uint32_t)((p ^ (4 * rr + s)) * 16);
-        o.t[s] = (uint32_t)((lane >> 3) * 128 + ((p8 ^ (hb | (s << 1))) * 16));
-    }
-    o.v = (uint32_t)(lane >> 2) * v_row + (uint32_t)((lane & 3) * 16);
-    o.gb = (uint32_t)lane * Hv * 4u;
+    for (int j = 0; j < 8; ++j)   // piece j: rows 4 j + rr, fK = 4 rr + (j/2)%2
+        o.kv[j] = rr * k_row + (uint32_t)((p ^ (4 * rr + ((j >> 1) & 1))) * 16);
 #pragma unroll
     for (int j = 0; j < 16; ++j) o.ks[j] = __builtin_amdgcn_readfirstlane((uint32_t)(4 * j) * k_row);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        o.kv[j] = o.k[(j >> 1) & 1];
-        // piece j, lane l: row 8 j + l / 8, memory granule (columns 8 q ..
-        // 8 q + 7) q = (l % 8) ^ fT(row); a granule wholly above the
-        // diagonal (8 q > row) is not in memory and reads as zero
-        const int row = 8 * j + (lane >> 3);
-        const int qg = p8 ^ (hb | ((j & 1) << 1));
-        o.tv[j] = 8 * qg <= row ? o.t[j & 1] : 0x80000000u;
-        o.ts[j] = 1024u * j;
-    }
+    o.v = (uint32_t)(lane >> 2) * v_row + (uint32_t)((lane & 3) * 16);
 #pragma unroll
     for (int j = 0; j < 4; ++j) o.vs[j] = __builtin_amdgcn_readfirstlane((uint32_t)(16 * j) * v_row);
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f) {
+        o.pv[f] = frag_live(f, lane) ? 16u * lane : 0x80000000u;
+        o.ps[f] = 1024u * f;
+    }
+    o.gmv = (uint32_t)SLOT_BYTES + 4u * lane;
     return o;
 }
 
-// Loader wave wl's share of chunk c's DMA into `stage`: K and log_g
-// (wl = 0, DMA_K_WAVE operations) or T, V and beta (wl = 1, DMA_TV_WAVE).
-// Rows beyond the chunk read as zero.
-__device__ __forceinline__ void spine_load(unsigned char* stage, const LoadOffsets& o,
-                                           const uint16_t* k, const uint16_t* v,
-                                           const float* log_g, const float* beta,
-                                           const uint16_t* slot, long row0, long len, int c, int Hk,
-                                           int Hv, int kh, int vh, int tile, int wl)
-{
-    const long r = row0 + (long)c * C;
+// Where chunk cc of this workgroup's sequence starts, and its length.
+struct ChunkRows {
+    size_t r0;      // first token row (wave-uniform)
+    uint32_t L;     // rows in the chunk, 0 past the last chunk
+};
+__device__ __forceinline__ ChunkRows chunk_rows(long row0, long len, int cc) {
+    const long r = row0 + (long)cc * C;
     const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)r);
     const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)r >> 32));
-    const size_t ru = ((size_t)rhi << 32) | rlo;
-    const uint32_t L = __builtin_amdgcn_readfirstlane((uint32_t)min((long)C, len - (long)c * C));
-    const uint32_t base = lds_u32(stage);
-    if (wl == 0) {
-        const uint32_t k_row = (uint32_t)Hk * D * 2u;
-        const Rsrc rk = make_dma_rsrc(k + (ru * Hk + kh) * D, L * k_row);
-        dma_x8(rk, base + ST_K, o.kv, *reinterpret_cast<const uint32_t(*)[8]>(&o.ks[0]));
-        dma_x8(rk, base + ST_K + 8192, o.kv, *reinterpret_cast<const uint32_t(*)[8]>(&o.ks[8]));
-        const Rsrc rg = make_dma_rsrc(log_g + ru * Hv + vh, L * Hv * 4u);
-        dma4(rg, stage + ST_G, o.gb);
-    } else {
-        const uint32_t v_row = (uint32_t)Hv * D * 2u;
-        const Rsrc rt = make_dma_rsrc(slot, C * C * 2u);
-        dma_x8(rt, base + ST_T, o.tv, o.ts);
-        const Rsrc rv = make_dma_rsrc(v + (ru * Hv + vh) * D + tile * TILE_COLS, L * v_row);
-        dma_x4(rv, base + ST_V, o.v, o.v, o.v, o.v, o.vs[0], o.vs[1], o.vs[2], o.vs[3]);
-        const Rsrc rb = make_dma_rsrc(beta + ru * Hv + vh, L * Hv * 4u);
-        dma4(rb, stage + ST_B, o.gb);
-    }
+    const long rem = len - (long)cc * C;
+    ChunkRows cr;
+    cr.r0 = ((size_t)rhi << 32) | rlo;
+    cr.L = __builtin_amdgcn_readfirstlane((uint32_t)(rem <= 0 ? 0 : (rem < C ? rem : C)));
+    return cr;
 }
 
-// Loader wave wl's share of chunk c's output-ring DMA into `slot_lds`: S
-// (wl = 0, 8 operations) or Q (wl = 1, 16 operations).
-__device__ __forceinline__ void spine_load_out(unsigned char* slot_lds, const LoadOffsets& o,
-                                               const uint16_t* q, const uint16_t* sslot, long row0,
-                                               long len, int c, int Hk, int kh, int wl)
-{
-    const uint32_t base = lds_u32(slot_lds);
-    if (wl == 0) {
-        const Rsrc rs = make_dma_rsrc(sslot, C * C * 2u);
-        dma_x8(rs, base + OR_S, o.tv, o.ts);
-    } else {
-        const long r = row0 + (long)c * C;
-        const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)r);
-        const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)r >> 32));
-        const size_t ru = ((size_t)rhi << 32) | rlo;
-        const uint32_t L = __builtin_amdgcn_readfirstlane((uint32_t)min((long)C, len - (long)c * C));
-        const uint32_t q_row = (uint32_t)Hk * D * 2u;
-        const Rsrc rq = make_dma_rsrc(q + (ru * Hk + kh) * D, L * q_row);
-        (void)q_row;   // the Q rows share K's precomputed offsets (same k-head layout)
-        dma_x8(rq, base + OR_Q, o.kv, *reinterpret_cast<const uint32_t(*)[8]>(&o.ks[0]));
-        dma_x8(rq, base + OR_Q + 8192, o.kv, *reinterpret_cast<const uint32_t(*)[8]>(&o.ks[8]));
-    }
-}
-
-// Decay factors of the chunk in `stage` (its log_g has landed): G = cumsum
-// of log_g within the chunk.  One wave, lane = row.
-__device__ __forceinline__ void spine_scan(unsigned char* stage, int lane) {
-    const float gv = reinterpret_cast<const float*>(stage + ST_G)[lane];
-    const float G = wave_scan_dpp(gv);
-    const float GL = __shfl(G, 63, 64);
-    reinterpret_cast<float*>(stage + ST_GM)[lane] = __expf(G);
-    reinterpret_cast<float*>(stage + ST_EL)[lane] = __expf(GL - G);
-    if (lane == 0) *reinterpret_cast<float*>(stage + ST_SO) = __expf(GL);
-}
-
-// Per-lane byte offsets of a recurrence wave's operand reads inside a stage
-// (chunk- and stage-independent).  Each chunk then needs a few base
-// additions; the tile and k-step parts of every address are immediates.
-struct FragOffsets {
-    uint32_t k[4];    // K fragments, by k-step
-    uint32_t t;       // T fragments
-    uint32_t kt[4];   // K^T (transposing) fragments, by db / 2
-    uint32_t v;       // V (transposing)
+struct SpineArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const unsigned char* tbs;   // T_b slots (fragments, then (gm, el, gamma_L) per recurrence lane)
+    const unsigned char* pps;   // P slots (fragments, then gm per output lane)
+    long row0, len;
+    long slot0;
+    int nc, Hk, Hv, kh, vh, tile;
 };
 
-__device__ __forceinline__ FragOffsets frag_offsets(int g, int n, int w) {
+// Output wave j's share of chunk cc's recurrence stage: K (j = 0) or V (j = 1);
+// rows past the chunk read as zero.
+__device__ __forceinline__ void issue_rec(unsigned char* ring, const LoadOffsets& o, const SpineArgs& a,
+                                          int cc, int j) {
+    const ChunkRows cr = chunk_rows(a.row0, a.len, cc);
+    const uint32_t base = lds_u32(ring + (cc % N_RS) * RS_BYTES);
+    if (j == 0) {
+        const uint32_t k_row = (uint32_t)a.Hk * D * 2u;
+        const Rsrc rk = make_dma_rsrc(a.k + (cr.r0 * a.Hk + a.kh) * D, cr.L * k_row);
+        dma_x8(rk, base + RS_K, o.kv, &o.ks[0]);
+        dma_x8(rk, base + RS_K + 8192, o.kv, &o.ks[8]);
+    } else {
+        const uint32_t v_row = (uint32_t)a.Hv * D * 2u;
+        const Rsrc rv = make_dma_rsrc(a.v + (cr.r0 * a.Hv + a.vh) * D + a.tile * TILE_COLS, cr.L * v_row);
+        dma_x4(rv, base + RS_V, o.v, o.v, o.v, o.v, o.vs[0], o.vs[1], o.vs[2], o.vs[3]);
+    }
+}
+
+// Output wave j's share of chunk cc's output slot: P and gm (j = 0) or Q (j = 1).
+__device__ __forceinline__ void issue_out(unsigned char* slot, const LoadOffsets& o, const SpineArgs& a,
+                                          int cc, int j) {
+    const uint32_t base = lds_u32(slot);
+    if (j == 0) {
+        const Rsrc rp = make_dma_rsrc(a.pps + ((size_t)(a.slot0 + cc) * a.Hv + a.vh) * SLOT_STRIDE,
+                                      SLOT_BYTES + 256);
+        dma_x6(rp, base + OS_P, o.pv, o.ps);
+        dma4(rp, slot + OS_GM, o.gmv);
+    } else {
+        const ChunkRows cr = chunk_rows(a.row0, a.len, cc);
+        const uint32_t q_row = (uint32_t)a.Hk * D * 2u;
+        const Rsrc rq = make_dma_rsrc(a.q + (cr.r0 * a.Hk + a.kh) * D, cr.L * q_row);
+        dma_x8(rq, base + OS_Q, o.kv, &o.ks[0]);
+        dma_x8(rq, base + OS_Q + 8192, o.kv, &o.ks[8]);
+    }
+}
+
+// Per-lane byte offsets of the operand reads (chunk-independent).
+struct FragOffsets {
+    uint32_t k[4];    // K / Q fragments in the ring layout, by k-step
+    uint32_t kt[4];   // K^T (transposing) fragments, by db / 2
+    uint32_t v;       // V (transposing), this wave's 16 columns
+};
+
+__device__ __forceinline__ FragOffsets frag_offsets(int g, int n, int half) {
     FragOffsets o;
     const int sig0 = 8 * (n >> 2) + (n & 3);                 // sig(0, n)
     const int fKn = 4 * (n & 3) + ((n >> 2) & 1);            // fK(sig(t, n)), any t
-    const int fTn = ((n >> 1) & 1) | (((n >> 2) & 1) << 1);  // fT(sig(t, n)), any t
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) o.k[kk] = (uint32_t)(sig0 * 256 + 16 * ((4 * kk + g) ^ fKn));
-    o.t = (uint32_t)(sig0 * 128 + 16 * (g ^ fTn));
     // transposing reads: this lane sources row 8g + kr (+ 32 kk + 4 half) and
     // the 4 columns of quarter qq of the 8-column group
     const int kr = n >> 2, qq = n & 3;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
         o.kt[d] = (uint32_t)((8 * g + kr) * 256 + 16 * (4 * (d ^ kr) + (qq ^ (g & 1))));
-    o.v = (uint32_t)((8 * g + kr) * 64 + 32 * w + 8 * qq);
+    o.v = (uint32_t)((8 * g + kr) * 64 + 32 * half + 8 * qq);
     return o;
 }
 
-// One recurrence wave, one chunk, 16 columns (column half w of the
-// workgroup) from stage S; hands its bf16 state and Delta fragments to the
-// output wave through exchange slot E.
-__device__ __forceinline__ void spine_step(const unsigned char* S, unsigned char* E, f32x4 (&h)[8],
-                                           int g, int lane, const FragOffsets& fo)
-{
-    const float* gmv = reinterpret_cast<const float*>(S + ST_GM);
-    const float* elv = reinterpret_cast<const float*>(S + ST_EL);
-    const float* btv = reinterpret_cast<const float*>(S + ST_B);
-    const unsigned char* pk[4];
-    const unsigned char* pz[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { pk[i] = S + fo.k[i]; pz[i] = S + fo.kt[i]; }
-    const unsigned char* pt = S + fo.t;
-    const unsigned char* pv = S + fo.v;
-#define KF(cb, kk) lds_read16(pk[kk] + ST_K + 256 * sig_tile(cb))
-#define TF(cb, kk) lds_read16(pt + ST_T + 128 * sig_tile(cb) + 64 * (kk))
-#define KTF(db, kk) join(lds_read_tr(pz[(db) >> 1] + ST_K + 8192 * (kk) + 8 * ((db) & 1)), \
-                         lds_read_tr(pz[(db) >> 1] + ST_K + 8192 * (kk) + 1024 + 8 * ((db) & 1)))
+// A recurrence wave's operands of one chunk: from the workspace, the T_b
+// fragments and (gm, el, gamma_L); from the ring, the K fragments of X (by
+// k-step and tile), the transposed K fragments of the update (by state block
+// and k-step) and V in accumulator layout.
+struct RecOps {
+    s16x8 tb[NFRAG];
+    float4 sc;
+    s16x8 kx[4][4];
+    s16x8 kt[8][2];
+    s16x4 vv[4];
+};
 
-    // every read of the chunk's K fragments, scalars, V and T comes before
-    // the exchange writes (which the compiler cannot prove disjoint from
-    // them), so all are in flight while X is formed; the K fragments go
-    // first, all four k-steps at once
-    s16x8 kf[4][4];
+// Memory loads of chunk cc's T_b and decay factors (zeros past the last chunk).
+__device__ __forceinline__ void rec_load_mem(RecOps& m, const uint32_t (&tbv)[NFRAG], const SpineArgs& a,
+                                             int cc, int lane) {
+    const bool live = cc < a.nc;
+    const rsrc_t rt = make_rsrc(a.tbs + ((size_t)(a.slot0 + (live ? cc : 0)) * a.Hv + a.vh) * SLOT_STRIDE,
+                                live ? (uint32_t)SLOT_STRIDE : 0u);
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f) m.tb[f] = buffer_load16(rt, tbv[f], 0);
+    const u32x4v s = __builtin_amdgcn_raw_buffer_load_b128(rt, (uint32_t)SLOT_BYTES + 16u * lane, 0, 0);
+    m.sc = make_float4(__uint_as_float(s[0]), __uint_as_float(s[1]), __uint_as_float(s[2]), __uint_as_float(s[3]));
+}
+
+#define GDN_KX(S, kk, cb) lds_read16((S) + RS_K + fo.k[kk] + 256 * sig_tile(cb))
+#define GDN_KT(S, db, kk) join(lds_read_tr((S) + RS_K + fo.kt[(db) >> 1] + 8192 * (kk) + 8 * ((db) & 1)), \
+                               lds_read_tr((S) + RS_K + fo.kt[(db) >> 1] + 8192 * (kk) + 1024 + 8 * ((db) & 1)))
+#define GDN_VV(S, cb) lds_read_tr((S) + RS_V + fo.v + 64 * sig_tile(cb))
+
+// Every ring read of one chunk at once (the first chunk, before the walk).
+__device__ __forceinline__ void rec_read_lds(RecOps& l, const unsigned char* S, const FragOffsets& fo) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) kf[kk][cb] = KF(cb, kk);
-    float4 gm4[4], bt4[4], el4[4];
-    s16x4 vv[4];
+        for (int cb = 0; cb < 4; ++cb) l.kx[kk][cb] = GDN_KX(S, kk, cb);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        const int row = sig_tile(cb) + 8 * g;
-        gm4[cb] = *reinterpret_cast<const float4*>(gmv + row);
-        bt4[cb] = *reinterpret_cast<const float4*>(btv + row);
-        el4[cb] = *reinterpret_cast<const float4*>(elv + row);
-        vv[cb] = lds_read_tr(pv + ST_V + 64 * sig_tile(cb));
-    }
-    s16x8 ft[6];
+    for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) ft[cb] = TF(cb, 0);
-    ft[4] = TF(2, 1);
-    ft[5] = TF(3, 1);
-    const float gamL = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-        __builtin_bit_cast(int, *reinterpret_cast<const float*>(S + ST_SO))));
+        for (int kk = 0; kk < 2; ++kk) l.kt[db][kk] = GDN_KT(S, db, kk);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) l.vv[cb] = GDN_VV(S, cb);
+}
 
+// R = V - gm X on accumulator register r of tile cb (row sig(cb, 4g + r))
+template <int CB>
+__device__ __forceinline__ void resid(f32x4& x, const s16x4 vv, float gm) {
+    x[0] = bf16_bits_to_f32((uint16_t)vv[0]) - row_bcast<4 * CB + 0>(gm) * x[0];
+    x[1] = bf16_bits_to_f32((uint16_t)vv[1]) - row_bcast<4 * CB + 1>(gm) * x[1];
+    x[2] = bf16_bits_to_f32((uint16_t)vv[2]) - row_bcast<4 * CB + 2>(gm) * x[2];
+    x[3] = bf16_bits_to_f32((uint16_t)vv[3]) - row_bcast<4 * CB + 3>(gm) * x[3];
+}
+template <int CB>
+__device__ __forceinline__ f32x4 scale_rows(const f32x4 x, float el) {
+    return f32x4{row_bcast<4 * CB + 0>(el) * x[0], row_bcast<4 * CB + 1>(el) * x[1],
+                 row_bcast<4 * CB + 2>(el) * x[2], row_bcast<4 * CB + 3>(el) * x[3]};
+}
+
+// One recurrence step on chunk c (operands o), 16 columns; the next chunk's
+// operands go into on: its ring reads (stage Sn) spread between this step's
+// products, its memory loads issued right away.  The bf16 state and Delta go
+// to exchange slot E.
+__device__ __forceinline__ void rec_step(f32x4 (&h)[8], const RecOps& o, RecOps& on, const unsigned char* Sn,
+                                         unsigned char* E, const FragOffsets& fo, const uint32_t (&tbv)[NFRAG],
+                                         const SpineArgs& a, int cn, int lane)
+{
+    // state -> bf16 B operand, and to the output partner
     s16x8 hb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         hb[kk] = frag_b(h[2 * kk], h[2 * kk + 1]);
         *reinterpret_cast<s16x8*>(E + 1024 * kk + 16 * lane) = hb[kk];
     }
-
-    // X = K h, k-step by k-step as the fragments land
+    // the next chunk's T_b and decay factors from the workspace
+    rec_load_mem(on, tbv, a, cn, lane);
+    sched_fence();
+    // X = K h, with the next chunk's update fragments of state blocks 0..3 read
+    // in between; h scaled by gamma_L meanwhile (hb holds the state before it)
     f32x4 X[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) X[cb] = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) X[cb] = mfma_bf16(kf[kk][cb], hb[kk], X[cb]);
-
-    // R = beta (V - gm X) for this lane's rows
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        const float gmr[4] = {gm4[cb].x, gm4[cb].y, gm4[cb].z, gm4[cb].w};
-        const float btr[4] = {bt4[cb].x, bt4[cb].y, bt4[cb].z, bt4[cb].w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            X[cb][r] = btr[r] * (bf16_bits_to_f32((uint16_t)vv[cb][r]) - gmr[r] * X[cb][r]);
+        for (int cb = 0; cb < 4; ++cb) {
+            X[cb] = mfma_bf16(o.kx[kk][cb], hb[kk], X[cb]);
+            if (cb & 1) {
+                const int db = 2 * kk + (cb >> 1);   // 0..7 in order
+                if (db < 4) {
+                    on.kt[db][0] = GDN_KT(Sn, db, 0);
+                    on.kt[db][1] = GDN_KT(Sn, db, 1);
+                } else {
+                    h[2 * (db - 4)] = h[2 * (db - 4)] * o.sc.z;
+                    h[2 * (db - 4) + 1] = h[2 * (db - 4) + 1] * o.sc.z;
+                }
+            }
+            sched_fence();
+        }
     }
-    const s16x8 rb0 = frag_b(X[0], X[1]), rb1 = frag_b(X[2], X[3]);
-
-    // Delta = T R (T lower triangular: its first 32 rows need only k < 32)
-    s16x8 fk1[4];
+    // the next chunk's K fragments of X into the registers X just read
 #pragma unroll
-    for (int db = 0; db < 2; ++db) { fk1[2 * db] = KTF(db, 0); fk1[2 * db + 1] = KTF(db, 1); }
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) on.kx[kk][cb] = GDN_KX(Sn, kk, cb);
+    sched_fence();
+    // R = V - gm X, rounded to the B operand of Delta = T_b R
+    resid<0>(X[0], o.vv[0], o.sc.x);
+    resid<1>(X[1], o.vv[1], o.sc.x);
+    resid<2>(X[2], o.vv[2], o.sc.x);
+    resid<3>(X[3], o.vv[3], o.sc.x);
+    const s16x8 rb0 = frag_b(X[0], X[1]), rb1 = frag_b(X[2], X[3]);
     sched_fence();
     f32x4 Dl[4];
-    Dl[0] = mfma_bf16(ft[0], rb0, zero4());
-    Dl[1] = mfma_bf16(ft[1], rb0, zero4());
-    Dl[2] = mfma_bf16(ft[2], rb0, zero4());
-    Dl[3] = mfma_bf16(ft[3], rb0, zero4());
-    Dl[2] = mfma_bf16(ft[4], rb1, Dl[2]);
-    Dl[3] = mfma_bf16(ft[5], rb1, Dl[3]);
+    Dl[0] = mfma_bf16(o.tb[0], rb0, zero4());
+    on.kx[2][0] = GDN_KX(Sn, 2, 0);
     sched_fence();
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        Dl[cb][0] *= el4[cb].x; Dl[cb][1] *= el4[cb].y; Dl[cb][2] *= el4[cb].z; Dl[cb][3] *= el4[cb].w;
-    }
+    Dl[1] = mfma_bf16(o.tb[1], rb0, zero4());
+    on.kx[2][1] = GDN_KX(Sn, 2, 1);
+    sched_fence();
+    Dl[2] = mfma_bf16(o.tb[2], rb0, zero4());
+    on.kx[2][2] = GDN_KX(Sn, 2, 2);
+    sched_fence();
+    Dl[3] = mfma_bf16(o.tb[3], rb0, zero4());
+    on.kx[2][3] = GDN_KX(Sn, 2, 3);
+    sched_fence();
+    Dl[2] = mfma_bf16(o.tb[4], rb1, Dl[2]);
+    Dl[3] = mfma_bf16(o.tb[5], rb1, Dl[3]);
+    sched_fence();
+    // Delta to the output partner; el Delta as the update's B operand
+    const s16x8 db0 = frag_b(Dl[0], Dl[1]), db1 = frag_b(Dl[2], Dl[3]);
+    *reinterpret_cast<s16x8*>(E + 4096 + 16 * lane) = db0;
+    *reinterpret_cast<s16x8*>(E + 5120 + 16 * lane) = db1;
+    sched_fence();
+    Dl[0] = scale_rows<0>(Dl[0], o.sc.y);
+    Dl[1] = scale_rows<1>(Dl[1], o.sc.y);
+    Dl[2] = scale_rows<2>(Dl[2], o.sc.y);
+    Dl[3] = scale_rows<3>(Dl[3], o.sc.y);
     const s16x8 ds0 = frag_b(Dl[0], Dl[1]), ds1 = frag_b(Dl[2], Dl[3]);
-    *reinterpret_cast<s16x8*>(E + 4096 + 16 * lane) = ds0;
-    *reinterpret_cast<s16x8*>(E + 5120 + 16 * lane) = ds1;
-
-    // h <- gamma_L h + K^T (el Delta): 8 row blocks, two blocks ahead
+    sched_fence();
+    // h <- gamma_L h + K^T (el Delta), with the rest of the next chunk's ring reads
 #pragma unroll
-    for (int db = 0; db < 8; ++db) h[db] = h[db] * gamL;
-#pragma unroll
-    for (int db = 0; db < 8; db += 2) {
-        s16x8 fk2[4];
-        if (db + 2 < 8) {
-            fk2[0] = KTF(db + 2, 0); fk2[1] = KTF(db + 2, 1);
-            fk2[2] = KTF(db + 3, 0); fk2[3] = KTF(db + 3, 1);
-        }
+    for (int db = 0; db < 8; ++db) {
+        h[db] = mfma_bf16(o.kt[db][0], ds0, h[db]);
+        if (db < 4) on.kx[3][db] = GDN_KX(Sn, 3, db);
+        if (db == 4) on.kt[4][0] = GDN_KT(Sn, 4, 0);
+        if (db == 5) on.kt[4][1] = GDN_KT(Sn, 4, 1);
+        if (db == 6) on.kt[5][0] = GDN_KT(Sn, 5, 0);
+        if (db == 7) on.kt[5][1] = GDN_KT(Sn, 5, 1);
         sched_fence();
-        h[db] = mfma_bf16(fk1[1], ds1, mfma_bf16(fk1[0], ds0, h[db]));
-        h[db + 1] = mfma_bf16(fk1[3], ds1, mfma_bf16(fk1[2], ds0, h[db + 1]));
-        sched_fence();
-        if (db + 2 < 8) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) fk1[i] = fk2[i];
-        }
     }
-#undef KF
-#undef TF
-#undef KTF
-    wait_lgkm0();   // the exchange writes are complete before the barrier
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+        h[db] = mfma_bf16(o.kt[db][1], ds1, h[db]);
+        if (db == 0) on.kt[6][0] = GDN_KT(Sn, 6, 0);
+        if (db == 1) on.kt[6][1] = GDN_KT(Sn, 6, 1);
+        if (db == 2) on.kt[7][0] = GDN_KT(Sn, 7, 0);
+        if (db == 3) on.kt[7][1] = GDN_KT(Sn, 7, 1);
+        if (db == 4) on.vv[0] = GDN_VV(Sn, 0);
+        if (db == 5) on.vv[1] = GDN_VV(Sn, 1);
+        if (db == 6) on.vv[2] = GDN_VV(Sn, 2);
+        if (db == 7) on.vv[3] = GDN_VV(Sn, 3);
+        sched_fence();
+    }
 }
+#undef GDN_KX
+#undef GDN_KT
+#undef GDN_VV
+// ring reads a recurrence step issues after its last exchange write: K
+// fragments 4 (k-step 3), transposed fragments of state blocks 4..7 (16
+// transposing reads) and V (4)
+constexpr int REC_READS_AFTER_EX = 24;
+static_assert(REC_READS_AFTER_EX >= 15, "the wait below then allows at most 15 outstanding");
 
-// One output wave, one chunk: O = (gm / gm_L) (gm_L (Q h) + S (el Delta))
-// for its 16 columns, with Q and S from output-ring slot Sq, the bf16 state
-// and el Delta from the exchange slot E the recurrence wave filled, and lg
-// this lane's log_g (lane = row).  The products are formed transposed: a
-// B-operand fragment of h or el Delta is the A operand of its transpose and
-// an A-operand fragment of Q or S the B operand of its transpose, so the
-// same fragments serve, and lane (g, n) register r of tile cb ends up
-// holding O[sig(cb, n)][4g + r]: four consecutive columns of one row, stored
-// at once.  `ro` covers exactly the chunk's output rows;
-// `lane_off` is the lane's byte offset for row sig(0, n) and column 4g, and
-// soff[cb] the uniform offset of tile cb's rows.
+// One output wave, chunk c: O = gm (Q h) + P Delta for its 16 columns, with Q,
+// P and gm from output slot Os and the bf16 state and Delta from exchange
+// slot E.  The products are formed transposed: a B-operand fragment of h or
+// Delta is the A operand of its transpose and an A-operand fragment of Q or P
+// the B operand of its transpose, so lane (g, n) register r of tile cb ends up
+// holding O[sig(cb, n)][4g + r], four consecutive columns of one row.  `ro`
+// covers exactly the chunk's rows.
 template <bool kOutF32>
-__device__ __forceinline__ void out_step(const unsigned char* Sq, const unsigned char* E, float* scr,
-                                         float lg, const FragOffsets& fo, rsrc_t ro,
-                                         uint32_t lane_off, const uint32_t (&soff)[4], int n,
-                                         int lane)
+__device__ __forceinline__ void out_step(const unsigned char* Os, const unsigned char* E, const FragOffsets& fo,
+                                         rsrc_t ro, uint32_t lane_off, const uint32_t (&soff)[4], int n, int lane)
 {
-    const float G = wave_scan_dpp(lg);
-    const float GL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
-    scr[lane] = __expf(G - GL);   // gm_r / gm_L
-    const float gmL = __expf(GL);
     s16x8 hb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) hb[kk] = lds_read16(E + 1024 * kk + 16 * lane);
     const s16x8 db0 = lds_read16(E + 4096 + 16 * lane), db1 = lds_read16(E + 5120 + 16 * lane);
+    const float4 g4 = *reinterpret_cast<const float4*>(Os + OS_GM + 16 * n);
     f32x4 Y[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) Y[cb] = zero4();
@@ -910,55 +966,50 @@ __device__ __forceinline__ void out_step(const unsigned char* Sq, const unsigned
     for (int kk = 0; kk < 4; ++kk) {
         s16x8 qf[4];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) qf[cb] = lds_read16(Sq + fo.k[kk] + OR_Q + 256 * sig_tile(cb));
+        for (int cb = 0; cb < 4; ++cb) qf[cb] = lds_read16(Os + OS_Q + fo.k[kk] + 256 * sig_tile(cb));
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) Y[cb] = mfma_bf16(hb[kk], qf[cb], Y[cb]);
     }
-    s16x8 sf[6];
+    s16x8 pf[NFRAG];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) sf[cb] = lds_read16(Sq + fo.t + OR_S + 128 * sig_tile(cb));
-    sf[4] = lds_read16(Sq + fo.t + OR_S + 128 * sig_tile(2) + 64);
-    sf[5] = lds_read16(Sq + fo.t + OR_S + 128 * sig_tile(3) + 64);
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) Y[cb] = Y[cb] * gmL;
+    for (int f = 0; f < NFRAG; ++f) pf[f] = lds_read16(Os + OS_P + 1024 * f + 16 * lane);
     f32x4 O[4];
-    O[0] = mfma_bf16(db0, sf[0], Y[0]);
-    O[1] = mfma_bf16(db0, sf[1], Y[1]);
-    O[2] = mfma_bf16(db0, sf[2], Y[2]);
-    O[3] = mfma_bf16(db0, sf[3], Y[3]);
-    O[2] = mfma_bf16(db1, sf[4], O[2]);
-    O[3] = mfma_bf16(db1, sf[5], O[3]);
-    wave_lds_sync();
-    const int sig0 = 8 * (n >> 2) + (n & 3);
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) O[cb] = O[cb] * scr[sig_tile(cb) + sig0];   // row factor of this lane's row
-    // hardware RNE conversion; rows beyond a partial chunk fall outside `ro`
-    // and are dropped
+    O[0] = mfma_bf16(db0, pf[0], Y[0] * g4.x);
+    O[1] = mfma_bf16(db0, pf[1], Y[1] * g4.y);
+    O[2] = mfma_bf16(db0, pf[2], Y[2] * g4.z);
+    O[3] = mfma_bf16(db0, pf[3], Y[3] * g4.w);
+    O[2] = mfma_bf16(db1, pf[4], O[2]);
+    O[3] = mfma_bf16(db1, pf[5], O[3]);
+    // hardware RNE conversion; rows past a partial chunk fall outside `ro`
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-        const f32x4 o = O[cb];
+        const f32x4 v = O[cb];
         if (kOutF32) {
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(o[0]), __float_as_uint(o[1]),
-                                                          __float_as_uint(o[2]), __float_as_uint(o[3])},
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                          __float_as_uint(v[2]), __float_as_uint(v[3])},
                                                    ro, lane_off, soff[cb], 0);
         } else {
-            const uint32_t lo = (uint16_t)bf16_bits(o[0]) | ((uint32_t)(uint16_t)bf16_bits(o[1]) << 16);
-            const uint32_t hi = (uint16_t)bf16_bits(o[2]) | ((uint32_t)(uint16_t)bf16_bits(o[3]) << 16);
+            const uint32_t lo = (uint16_t)bf16_bits(v[0]) | ((uint32_t)(uint16_t)bf16_bits(v[1]) << 16);
+            const uint32_t hi = (uint16_t)bf16_bits(v[2]) | ((uint32_t)(uint16_t)bf16_bits(v[3]) << 16);
             __builtin_amdgcn_raw_buffer_store_b64(u32x2v{lo, hi}, ro, lane_off, soff[cb], 0);
         }
     }
-    wave_lds_sync();   // the decay scratch is rewritten by the next chunk
+}
+
+// s_waitcnt vmcnt for the output waves' DMA bookkeeping (constant operands)
+template <int J>
+__device__ __forceinline__ void out_wait_rec_only() {   // all but this step's recurrence DMA and stores
+    __builtin_amdgcn_s_waitcnt(GDN_VMCNT((J == 0 ? DMA_REC0 : DMA_REC1) + OUT_STORES));
 }
 
 template <bool kOutF32>
-__global__ void __launch_bounds__(384)
+__global__ void __launch_bounds__(256, 1)
 gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                 const uint16_t* __restrict__ v, const float* __restrict__ log_g,
-                 const float* __restrict__ beta, const float* h0, void* __restrict__ out,
-                 float* h_final, const uint16_t* __restrict__ tslots,
-                 const uint16_t* __restrict__ sslots, int T, int Hk, int Hv,
-                 const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_base,
-                 const int32_t* __restrict__ order, int nc_dense, long n_slots)
+                 const uint16_t* __restrict__ v, const float* h0, void* __restrict__ out, float* h_final,
+                 const unsigned char* __restrict__ tbs, const unsigned char* __restrict__ pps,
+                 int T, int Hk, int Hv, const int32_t* __restrict__ cu,
+                 const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ order,
+                 int nc_dense, long n_slots)
 {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[SPINE_LDS];
     unsigned char* ring = lds;
@@ -971,123 +1022,116 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // one k-head (its v-heads and column tiles) share an XCD and its L2.
     const int W = gridDim.x;
     const int lin = (W % 8 == 0) ? (blockIdx.x % 8) * (W / 8) + blockIdx.x / 8 : blockIdx.x;
-    const int vh = lin / N_TILES;
-    const int tile = lin % N_TILES;
+    SpineArgs a;
+    a.vh = lin / N_TILES;
+    a.tile = lin % N_TILES;
     const int b = order ? order[blockIdx.y] : (int)blockIdx.y;
-    const int kh = vh / (Hv / Hk);
-
-    long row0, len;
-    seq_rows(cu, b, T, &row0, &len);
-    const long slot0 = cu ? (long)chunk_base[b] : (long)b * nc_dense;
-    int nc = (int)((len + C - 1) / C);
+    a.kh = a.vh / (Hv / Hk);
+    a.q = q; a.k = k; a.v = v; a.tbs = tbs; a.pps = pps; a.Hk = Hk; a.Hv = Hv;
+    seq_rows(cu, b, T, &a.row0, &a.len);
+    a.slot0 = cu ? (long)chunk_base[b] : (long)b * nc_dense;
+    int nc = (int)((a.len + C - 1) / C);
     // Only a decreasing cu_seqlens (a broken precondition) can make this
     // bind; it keeps every read inside the workspace.
-    if (slot0 + nc > n_slots) nc = (int)max(0L, n_slots - slot0);
-    const uint16_t* slot_base = tslots + ((size_t)slot0 * Hv + vh) * SLOT_ELEMS;   // T, by chunk
-    const size_t slot_stride = (size_t)Hv * SLOT_ELEMS;
-    const uint16_t* s_base = sslots + ((size_t)slot0 * Hk + kh) * SLOT_ELEMS;      // S, by chunk
-    const size_t s_stride = (size_t)Hk * SLOT_ELEMS;
+    if (a.slot0 + nc > n_slots) nc = (int)max(0L, n_slots - a.slot0);
+    a.nc = nc;
+    const int half = w & 1;   // which 16 of the workgroup's 32 columns
+    const FragOffsets fo = frag_offsets(g, n, half);
+    unsigned char* ex = lds + EX_BASE + 2 * half * EX_BYTES;   // this column half's exchange, parity 0
 
-    if (w >= 4) {   // loader waves
-        const int wl = w - 4;
-        const int cnt = wl == 0 ? DMA_K_WAVE : DMA_TV_WAVE;
+    if (w < 2) {   // output waves: chunk c - 1 in step c, and the DMA
+        const int j = half;
         const LoadOffsets o = load_offsets(lane, Hk, Hv);
-        for (int c = 0; c < 2 && c < nc; ++c)
-            spine_load(ring + c * ST_BYTES, o, k, v, log_g, beta, slot_base + (size_t)c * slot_stride,
-                       row0, len, c, Hk, Hv, kh, vh, tile, wl);
-        if (nc > 0) {
-            wait_vmcnt(nc > 1 ? cnt : 0);
-            if (wl == 0) spine_scan(ring, lane);
+        constexpr uint32_t es = kOutF32 ? 4u : 2u;
+        const uint32_t rs = __builtin_amdgcn_readfirstlane((uint32_t)Hv * D * es);
+        const uint32_t lane_off = (uint32_t)(8 * (n >> 2) + (n & 3)) * rs +
+                                  (uint32_t)(a.tile * TILE_COLS + 16 * half + 4 * g) * es;
+        uint32_t soff[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) soff[cb] = (uint32_t)sig_tile(cb) * rs;
+        const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)a.row0);
+        const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)a.row0 >> 32));
+        char* obase = reinterpret_cast<char*>(out) + ((((size_t)rhi << 32) | rlo) * Hv + a.vh) * D * es;
+        // chunks 0 and 1 in the ring before the first barrier, chunk 2 on its way
+        for (int cc = 0; cc < 3 && cc < nc; ++cc) issue_rec(ring, o, a, cc, j);
+        if (nc > 2) {
+            if (j == 0) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_REC0));
+            else __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_REC1));
+        } else {
+            __builtin_amdgcn_s_waitcnt(GDN_VMCNT(0));
+        }
+        for (int c = 0; c <= nc; ++c) {
+            // the ring holds chunks c and c + 1; output slot (c - 1) % 2 holds chunk c - 1
+            ring_barrier();
+            // slot c % 2 held chunk c - 2, read in step c - 1; stage (c + 3) % 4
+            // held chunk c - 1, whose reads ended in step c - 1
+            if (c < nc) issue_out(lds + OS_BASE + (c & 1) * OS_BYTES, o, a, c, j);
+            const bool rec = c + 3 < nc;
+            if (rec) issue_rec(ring, o, a, c + 3, j);
+            if (c >= 1) {
+                const long rem = a.len - (long)(c - 1) * C;
+                const rsrc_t ro = make_rsrc(obase + (size_t)(c - 1) * C * rs, (uint32_t)min((long)C, rem) * rs);
+                out_step<kOutF32>(lds + OS_BASE + ((c - 1) & 1) * OS_BYTES, ex + ((c - 1) & 1) * EX_BYTES, fo, ro,
+                                  lane_off, soff, n, lane);
+            }
+            // chunk c's slot and chunk c + 2's stage have landed before the next
+            // barrier; chunk c + 3's stage (and this step's stores) may still fly
+            if (rec) {
+                if (c >= 1) { if (j == 0) out_wait_rec_only<0>(); else out_wait_rec_only<1>(); }
+                else if (j == 0) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_REC0));
+                else __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_REC1));
+            } else {
+                if (c >= 1) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(OUT_STORES));
+                else __builtin_amdgcn_s_waitcnt(GDN_VMCNT(0));
+            }
             wait_lgkm0();
         }
-        for (int c = 0; c <= nc; ++c) {
-            // chunk c is ready in the recurrence ring; stage (c+2)%3 and
-            // output slot c%2 are free
-            ring_barrier();
-            if (c < nc)
-                spine_load_out(lds + OR_BASE + (c & 1) * OR_SLOT, o, q, s_base + (size_t)c * s_stride, row0,
-                               len, c, Hk, kh, wl);
-            if (c + 2 < nc)
-                spine_load(ring + ((c + 2) % N_STAGES) * ST_BYTES, o, k, v, log_g, beta,
-                           slot_base + (size_t)(c + 2) * slot_stride, row0, len, c + 2, Hk, Hv, kh,
-                           vh, tile, wl);
-            if (c < nc) {
-                // chunk c's output operands and chunk c+1 have landed
-                wait_vmcnt(c + 2 < nc ? cnt : 0);
-                if (c + 1 < nc && wl == 0) spine_scan(ring + ((c + 1) % N_STAGES) * ST_BYTES, lane);
-                wait_lgkm0();
-            }
-        }
         return;
     }
 
-    const int half = w & 1;   // which 16 of the workgroup's 32 columns
-    const int col = tile * TILE_COLS + 16 * half + n;
-    unsigned char* ex = lds + EX_BASE + half * 2 * EX_SLOT;
-
-    if (w >= 2) {   // recurrence waves
-        f32x4 h[8];
-        const size_t hoff = ((size_t)b * Hv + vh) * D * D;
-        // state row of h[db][r] in this lane: sig(db, 4g + r)
-        if (h0) {   // one uniform branch: all 32 loads in flight together
+    // recurrence waves
+    f32x4 h[8];
+    const int col = a.tile * TILE_COLS + 16 * half + n;
+    const size_t hoff = ((size_t)b * Hv + a.vh) * D * D;
+    // state row of h[db][r] in this lane: sig(db, 4g + r)
+    if (h0) {   // one uniform branch: all 32 loads in flight together
 #pragma unroll
-            for (int db = 0; db < 8; ++db)
+        for (int db = 0; db < 8; ++db)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    h[db][r] = h0[hoff + (size_t)(sig_tile(db) + 8 * g + r) * D + col];
-        } else {
+            for (int r = 0; r < 4; ++r)
+                h[db][r] = h0[hoff + (size_t)(sig_tile(db) + 8 * g + r) * D + col];
+    } else {
 #pragma unroll
-            for (int db = 0; db < 8; ++db) h[db] = zero4();
-        }
-        const FragOffsets fo = frag_offsets(g, n, half);
-        for (int c = 0; c <= nc; ++c) {
-            ring_barrier();
-            if (c < nc) spine_step(ring + (c % N_STAGES) * ST_BYTES, ex + (c & 1) * EX_SLOT, h, g, lane, fo);
-        }
-        if (h_final) {
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    h_final[hoff + (size_t)(sig_tile(db) + 8 * g + r) * D + col] = h[db][r];
-        }
-        return;
+        for (int db = 0; db < 8; ++db) h[db] = zero4();
     }
-
-    // output waves: chunk c - 1 at step c
-    float* scr = reinterpret_cast<float*>(lds + OUT_SCR + 256 * half);
-    constexpr uint32_t es = kOutF32 ? 4u : 2u;
-    const uint32_t rs = __builtin_amdgcn_readfirstlane((uint32_t)Hv * D * es);
-    const uint32_t lane_off = (uint32_t)(8 * (n >> 2) + (n & 3)) * rs +
-                              (uint32_t)(tile * TILE_COLS + 16 * half + 4 * g) * es;
-    uint32_t soff[4];
+    uint32_t tbv[NFRAG];   // T_b granules (out of range above the diagonal)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) soff[cb] = (uint32_t)sig_tile(cb) * rs;
-    const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)row0);
-    const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)row0 >> 32));
-    char* obase = reinterpret_cast<char*>(out) + ((((size_t)rhi << 32) | rlo) * Hv + vh) * D * es;
-    const FragOffsets fo = frag_offsets(g, n, half);
-    float lg = 0.f;
-    auto load_lg = [&](int c) {   // this chunk's log_g, lane = row
-        const long r = row0 + (long)c * C;
-        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)r);
-        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)r >> 32));
-        const size_t ru = ((size_t)hi << 32) | lo;
-        const uint32_t L = __builtin_amdgcn_readfirstlane((uint32_t)min((long)C, len - (long)c * C));
-        const rsrc_t rg = make_rsrc(log_g + ru * Hv + vh, L * Hv * 4u);
-        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)lane * Hv * 4u, 0, 0));
-    };
-    if (nc > 0) lg = load_lg(0);
-    for (int c = 0; c <= nc; ++c) {
+    for (int f = 0; f < NFRAG; ++f) tbv[f] = frag_live(f, lane) ? 16u * lane + 1024u * f : 0x80000000u;
+    RecOps oA, oB;
+    rec_load_mem(oA, tbv, a, 0, lane);
+    // one barrier per step, nc + 1 steps as the output waves; the exchange
+    // writes are complete before each barrier (the LDS operations of one wave
+    // complete in order, and more ring reads than can be in flight follow the
+    // last write).  Written so that the second step of a pair is reachable only
+    // through the first, which keeps the compiler's waits on the prefetched
+    // reads where they are used.
+    ring_barrier();
+    if (nc > 0) rec_read_lds(oA, ring, fo);
+    for (int c = 0; c < nc; c += 2) {
+        rec_step(h, oA, oB, ring + ((c + 1) % N_RS) * RS_BYTES, ex, fo, tbv, a, c + 1, lane);
+        __builtin_amdgcn_s_waitcnt(GDN_LGKMCNT(15));
         ring_barrier();
-        if (c >= 1) {   // chunk c - 1
-            const long rem = len - (long)(c - 1) * C;
-            const rsrc_t ro = make_rsrc(obase + (size_t)(c - 1) * C * rs, (uint32_t)min((long)C, rem) * rs);
-            const float lg_c = lg;
-            if (c < nc) lg = load_lg(c);
-            out_step<kOutF32>(lds + OR_BASE + ((c - 1) & 1) * OR_SLOT, ex + ((c - 1) & 1) * EX_SLOT,
-                              scr, lg_c, fo, ro, lane_off, soff, n, lane);
-        }
+        if (c + 1 >= nc) break;
+        rec_step(h, oB, oA, ring + ((c + 2) % N_RS) * RS_BYTES, ex + EX_BYTES, fo, tbv, a, c + 2, lane);
+        __builtin_amdgcn_s_waitcnt(GDN_LGKMCNT(15));
+        ring_barrier();
+    }
+    if (h_final) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                h_final[hoff + (size_t)(sig_tile(db) + 8 * g + r) * D + col] = h[db][r];
     }
 }
 
@@ -1102,7 +1146,8 @@ long slot_count(int B, int T, bool packed) {
 
 size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv, bool packed)
 {
-    return table_bytes(B) + (size_t)slot_count(B, T, packed) * (Hv + Hk) * SLOT_ELEMS * sizeof(uint16_t);
+    (void)Hk;
+    return table_bytes(B) + (size_t)slot_count(B, T, packed) * Hv * 2 * SLOT_STRIDE;
 }
 
 bool prefill_mfma_accepts(const PrefillArgs& a)
@@ -1112,7 +1157,7 @@ bool prefill_mfma_accepts(const PrefillArgs& a)
 
 Geometry prefill_mfma_geometry(const PrefillArgs& a)
 {
-    Geometry g{"gdn_wy_prep_kernel+gdn_spine_kernel", {(unsigned)(a.Hv * N_TILES), (unsigned)a.B, 1u}, 384u,
+    Geometry g{"gdn_wy_prep_kernel+gdn_spine_kernel", {(unsigned)(a.Hv * N_TILES), (unsigned)a.B, 1u}, 256u,
                (unsigned)SPINE_LDS};
     return g;
 }
@@ -1123,8 +1168,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
     int32_t* base = reinterpret_cast<int32_t*>(a.workspace);
     const int nc_dense = (a.T + C - 1) / C;
     const long n_slots = slot_count(a.B, a.T, packed);
-    uint16_t* tslots = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(a.workspace) + table_bytes(a.B));
-    uint16_t* sslots = tslots + (size_t)n_slots * a.Hv * SLOT_ELEMS;
+    unsigned char* tbs = reinterpret_cast<unsigned char*>(a.workspace) + table_bytes(a.B);
+    unsigned char* pps = tbs + (size_t)n_slots * a.Hv * SLOT_STRIDE;
     const int32_t* order = packed && a.B <= MAX_ORDERED ? base + a.B + 1 : nullptr;
     if (packed) {
         hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.B, a.T, base);
@@ -1134,20 +1179,18 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
         const size_t shmem = prep_lds_bytes(nw);
         hipLaunchKernelGGL(gdn_wy_prep_kernel, dim3((unsigned)n_slots, a.Hk, (unsigned)((G + nw - 1) / nw)),
                            dim3(64 * nw), shmem, s,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, a.log_g, a.beta, tslots, sslots,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, a.log_g, a.beta, tbs, pps,
                            a.B, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense);
     }
     dim3 grid(a.Hv * N_TILES, a.B);
     if (a.out_dtype == 0)
-        hipLaunchKernelGGL((gdn_spine_kernel<true>), grid, dim3(384), 0, s, (const uint16_t*)a.q,
-                           (const uint16_t*)a.k, (const uint16_t*)a.v, a.log_g, a.beta, a.h0, a.out,
-                           a.h_final, tslots, sslots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, order, nc_dense,
-                           n_slots);
+        hipLaunchKernelGGL((gdn_spine_kernel<true>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
+                           (const uint16_t*)a.k, (const uint16_t*)a.v, a.h0, a.out, a.h_final, tbs, pps,
+                           a.T, a.Hk, a.Hv, a.cu_seqlens, base, order, nc_dense, n_slots);
     else
-        hipLaunchKernelGGL((gdn_spine_kernel<false>), grid, dim3(384), 0, s, (const uint16_t*)a.q,
-                           (const uint16_t*)a.k, (const uint16_t*)a.v, a.log_g, a.beta, a.h0, a.out,
-                           a.h_final, tslots, sslots, a.T, a.Hk, a.Hv, a.cu_seqlens, base, order, nc_dense,
-                           n_slots);
+        hipLaunchKernelGGL((gdn_spine_kernel<false>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
+                           (const uint16_t*)a.k, (const uint16_t*)a.v, a.h0, a.out, a.h_final, tbs, pps,
+                           a.T, a.Hk, a.Hv, a.cu_seqlens, base, order, nc_dense, n_slots);
     return hipGetLastError();
 }
 

@@ -185,3 +185,41 @@ def test_packed_equals_separate_bitwise():
         o, h, _ = gpu_prefill(one, 64)
         assert torch.equal(_bits(o[0]), _bits(out[sl])), b
         assert torch.equal(_bits(h[0]), _bits(hf[b])), b
+
+
+@pytest.mark.parametrize("scale", [30.0, 200.0])
+def test_strong_gates(scale):
+    """Gates far stronger than the synthetic ones: log_g scaled by 30 (about -150
+    per 64-token chunk) and by 200 (about -1000 per chunk, decay underflows to
+    zero within a chunk).  Every decay factor the kernels form is exp of a
+    non-positive difference, so nothing overflows: outputs and states stay
+    finite and match the oracle."""
+    inp = synth.prefill_inputs(1, 300, 2, 6, 128, 128, h0=True, seed=903)
+    inp["log_g"] = inp["log_g"] * scale
+    say("strong gates x", scale)
+    out, hf, route = gpu_prefill(inp, 64)
+    assert route.startswith(ROUTE)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(hf).all()
+    check(inp, out, hf)
+
+
+def test_gates_from_the_ba_producer():
+    """The gate/beta producer's output (strongly decaying gates: chunk sums down
+    to about -114 on some v-heads) feeding the prefill, checked against the
+    oracle on the same gates."""
+    import linear_attention_ssm_gated_amd as gdn_
+    T, Hk, Hv, kdim = 320, 2, 6, 512
+    ba = synth.ba_inputs(T, kdim, Hv, seed=1006)
+    x, w = ba["x"].to(dev()), ba["w"].to(dev())
+    gates, _ = gdn_.ba_gates(x, w, ba["a_log"].to(dev()), ba["dt_bias"].to(dev()), Hv, Hv // Hk)
+    torch.cuda.synchronize()
+    inp = synth.prefill_inputs(1, T, Hk, Hv, 128, 128, h0=True, seed=904)
+    g = gates.cpu()
+    inp["log_g"] = g[:, :Hv].reshape(1, T, Hv).contiguous()
+    inp["beta"] = g[:, Hv:].reshape(1, T, Hv).contiguous()
+    sums = inp["log_g"][0, :256].reshape(4, 64, Hv).sum(1)
+    say("ba gates: min chunk sum", float(sums.min()))
+    out, hf, route = gpu_prefill(inp, 64)
+    assert route.startswith(ROUTE)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(hf).all()
+    check(inp, out, hf)

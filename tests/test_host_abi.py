@@ -60,7 +60,7 @@ def prefill_plan(lib, **kw):
 def test_prefill_routes(lib):
     assert prefill_plan(lib) == 0
     r = gdn.last_route()
-    assert r.startswith("gdn_wy_prep_kernel+gdn_spine_kernel grid=[192,1,1] block=384"), r
+    assert r.startswith("gdn_wy_prep_kernel+gdn_spine_kernel grid=[192,1,1] block=256"), r
     assert "lds=" in r
     # fp32 I/O goes to the generic kernel and the line says why
     assert prefill_plan(lib, io=0, od=0, dk=32, dv=32, chunk=32, Hk=1, Hv=1) == 0
@@ -96,13 +96,13 @@ def test_prefill_empty_needs_no_pointers(lib):
 
 
 def test_workspace_and_stash_sizes(lib):
-    # MFMA route: a 256-byte chunk table, then T (64 x 64 bf16) per (chunk, v-head) and
-    # S (64 x 64 bf16) per (chunk, k-head)
-    assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 128, 128, 64, 1) == 256 + 72 * (48 + 16) * 8192
-    assert gdn.gdn_prefill_workspace_bytes(2, 100, 16, 48, 128, 128, 64, 1) == 256 + 2 * 2 * (48 + 16) * 8192
+    # MFMA route: a 256-byte chunk table, then per (chunk, v-head) T diag(beta) and P,
+    # each 64 x 64 bf16 (6 KiB) plus the chunk's per-row decay factors (1 KiB)
+    assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 128, 128, 64, 1) == 256 + 72 * 48 * 2 * 7168
+    assert gdn.gdn_prefill_workspace_bytes(2, 100, 16, 48, 128, 128, 64, 1) == 256 + 2 * 2 * 48 * 2 * 7168
     # packed: ceil(T / 64) + B chunks at most
     assert gdn.gdn_prefill_workspace_bytes(8, 39168, 16, 48, 128, 128, 64, 1, packed=True) == \
-        256 + (612 + 8) * (48 + 16) * 8192
+        256 + (612 + 8) * 48 * 2 * 7168
     # generic route needs none
     assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 128, 128, 64, 0) == 0
     assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 64, 64, 64, 1) == 0
