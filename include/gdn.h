@@ -110,11 +110,12 @@ const char* gdn_last_route(void);
  * and packed = (cu_seqlens != NULL).  The MFMA route keeps a chunk table of
  * packed sequences (their first chunks, and for up to 256 sequences their
  * order by length, longest first, in which the state walks are dispatched),
- * and for every (chunk, v-head) T diag(beta) with T = (I + A)^-1 and
- * P = Gamma o lower_incl(Q K^T), each as 64 x 64 bf16 in MFMA fragment order
- * (6 KiB; the granules above their diagonals are never written or read)
- * followed by the chunk's per-row decay factors exp(G_r), exp(G_L - G_r) and
- * exp(G_L) (1 KiB), 7 KiB per matrix; the generic route needs none.
+ * and for every (chunk, v-head) T_e = diag(exp(G_L - G)) T diag(beta), with
+ * T = (I + A)^-1, and PT = (Gamma o lower_incl(Q K^T)) T diag(beta), each as
+ * 64 x 64 bf16 in MFMA fragment order (6 KiB; the granules above their
+ * diagonals are never written or read) followed by the chunk's per-row decay
+ * factors exp(G_r) (and exp(G_L) after T_e), 7 KiB per matrix; the generic
+ * route needs none.
  * The library reads and writes the workspace only inside the call's stream
  * order; its contents need no initialisation.
  */

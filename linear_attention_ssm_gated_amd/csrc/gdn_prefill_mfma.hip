@@ -7,22 +7,24 @@
 //   producer behind the spine, ssm_gdn_tc_route.rs, doc of the pipe spine):
 //     G = cumsum(log_g), Gamma_rs = exp(G_r - G_s) for s <= r
 //     A = strict_lower(diag(beta) (Gamma o K K^T)),  T = (I + A)^-1   (per v-head)
-//     T_b = T diag(beta),  P = Gamma o lower_incl(Q K^T)              (per v-head)
-//   K K^T and Q K^T run on bf16 MFMA with fp32 accumulation; T is solved in
-//   fp32 (16x16 diagonal blocks by forward substitution on VALU, the blocks
-//   below them on fp32 MFMA); T_b and P are stored as bf16 MFMA fragments in
+//     T_e = diag(el) T diag(beta),  el = exp(G_L - G)                  (per v-head)
+//     PT = (Gamma o lower_incl(Q K^T)) T diag(beta)                    (per v-head)
+//   K K^T, Q K^T and PT run on bf16 MFMA with fp32 accumulation; T is solved
+//   in fp32 (16x16 diagonal blocks by forward substitution on VALU, the blocks
+//   below them on fp32 MFMA); T_e and PT are stored as bf16 MFMA fragments in
 //   the workspace, their granules above the diagonal left unwritten (they are
-//   zero, and the spine never reads them from memory).  P carries the decay
-//   exactly (every factor exp(G_r - G_s) with s <= r is at most 1), so no
-//   rescaling in the spine can overflow, whatever the gates.
+//   zero, and the spine never reads them from memory), each followed by the
+//   chunk's per-row factors gm = exp(G).  Every decay factor formed is exp of
+//   a non-positive difference of cumulative log decays, so nothing can
+//   overflow, whatever the gates.
 //
 // gdn_spine_kernel, one workgroup per (sequence, v-head, 32 dv columns),
 //   walking the chunks in order: the state spine (same page, the tensor-core
 //   spine: bf16 MFMA operands, the fp32 accumulators are the recurrent state,
 //   h stays f32).  Per chunk:
-//     X = K h,  R = V - gm X,  Delta = T_b R      (= U - W h of the WY form)
-//     O = gm (Q h) + P Delta
-//     h <- gamma_L h + K^T (el o Delta),  el = exp(G_L - G), gm = exp(G)
+//     X = K h,  R = V - gm X,  Delta_e = T_e R   (= diag(el) (U - W h) of the WY form)
+//     O = gm (Q h) + PT R
+//     h <- gamma_L h + K^T Delta_e,  gamma_L = exp(G_L)
 //   Columns of h evolve independently (the dv split of the pages' SPLIT
 //   variants), so the workgroups never exchange data.
 //
@@ -253,8 +255,12 @@ constexpr int PREP_STAGE_BYTES = 2 * C * D * 2;           // K then Q, 256-byte 
 __host__ __device__ constexpr int prep_gb_base(int nw) {   // floats
     return PREP_STAGE_BYTES / 4 > nw * PREP_WAVE_FLOATS ? PREP_STAGE_BYTES / 4 : nw * PREP_WAVE_FLOATS;
 }
+// then each wave's P as bf16 MFMA fragments (the B operand of P T_b)
+__host__ __device__ constexpr int prep_p_base(int nw) {   // bytes
+    return (prep_gb_base(nw) + nw * 2 * C) * (int)sizeof(float);
+}
 __host__ __device__ constexpr size_t prep_lds_bytes(int nw) {
-    return (size_t)(prep_gb_base(nw) + nw * 2 * C) * sizeof(float);
+    return (size_t)prep_p_base(nw) + (size_t)nw * SLOT_BYTES;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave on DPP: shifts within
@@ -291,6 +297,7 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     float* lds = prep_lds + w * PREP_WAVE_FLOATS;
     float* sG = prep_lds + prep_gb_base(nw) + w * 2 * C;   // G log2(e) per row
     float* sBt = sG + C;                                        // beta per row
+    unsigned char* sPall = reinterpret_cast<unsigned char*>(prep_lds) + prep_p_base(nw);
 
     int b, c;
     if (!cu) {
@@ -341,18 +348,26 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         sG[lane] = Gl2;
         sBt[lane] = bv;
         if (h < G) {
-            // the spine's per-row decay factors of this (chunk, v-head), rows
-            // past a partial chunk keeping the last row's G: (gm, el, gamma_L)
-            // in recurrence-lane order after T_b, gm in output-lane order
-            // after P (row = sig(t, m))
+            // the spine's per-row decay factors gm = exp(G) of this (chunk,
+            // v-head), rows past a partial chunk keeping the last row's G.
+            // Row sig(t, m) is needed by recurrence lane group m / 4 in
+            // accumulator register m % 4 of tile t, and by output lane m for
+            // tile t: after T_e, gm by lane group ([m / 4][t][m % 4]) and
+            // gamma_L = exp(G_L); after PT, gm by output lane ([m][t]).
             const float GLl2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gl2), 63));
-            const float gm = __builtin_amdgcn_exp2f(Gl2), el = __builtin_amdgcn_exp2f(GLl2 - Gl2);
+            const float gm = __builtin_amdgcn_exp2f(Gl2);
             const int t = 2 * (lane >> 5) + ((lane >> 2) & 1), m = 4 * ((lane >> 3) & 3) + (lane & 3);
-            unsigned char* tb_slot = tbs + ((size_t)x * Hv + vh) * SLOT_STRIDE;
-            unsigned char* pp_slot = pps + ((size_t)x * Hv + vh) * SLOT_STRIDE;
-            *reinterpret_cast<float4*>(tb_slot + SLOT_BYTES + 16 * (16 * (m >> 2) + 4 * t + (m & 3))) =
-                make_float4(gm, el, __builtin_amdgcn_exp2f(GLl2), 0.f);
-            reinterpret_cast<float*>(pp_slot + SLOT_BYTES)[4 * m + t] = gm;
+            float* te_tail = reinterpret_cast<float*>(tbs + ((size_t)x * Hv + vh) * SLOT_STRIDE + SLOT_BYTES);
+            float* pt_tail = reinterpret_cast<float*>(pps + ((size_t)x * Hv + vh) * SLOT_STRIDE + SLOT_BYTES);
+            te_tail[16 * (m >> 2) + 4 * t + (m & 3)] = gm;
+            if (lane == 0) te_tail[64] = __builtin_amdgcn_exp2f(GLl2);
+            pt_tail[4 * m + t] = gm;
+            // granules of this v-head's P wholly above the diagonal, which no
+            // Gram tile writes, are zero (they enter P T_b as an operand)
+#pragma unroll
+            for (int f = 0; f < NFRAG; ++f)
+                if (2 * frag_kk(f) + (g >> 1) > (sig_row(frag_cb(f), n) >> 4))
+                    *reinterpret_cast<s16x8*>(sPall + w * SLOT_BYTES + FRAG_BYTES * f + 16 * lane) = s16x8{};
         }
     }
     // the DMA is inline assembly the compiler does not track: wait for it
@@ -427,8 +442,7 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                         pv[s2] = __builtin_amdgcn_exp2f(gr - gcv[s2]) * kq_acc[s2];
                         if (m == i) pv[s2] = (n >= 4 * g + s2) ? pv[s2] : 0.f;   // P lower with the diagonal
                     }
-                    const int vh2 = kh * G + (int)blockIdx.z * nw + hh;
-                    *reinterpret_cast<s16x4*>(pps + ((size_t)x * Hv + vh2) * SLOT_STRIDE + off) =
+                    *reinterpret_cast<s16x4*>(sPall + hh * SLOT_BYTES + off) =
                         s16x4{bf16_bits(pv[0]), bf16_bits(pv[1]), bf16_bits(pv[2]), bf16_bits(pv[3])};
                 }
             }
@@ -512,9 +526,11 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         wave_lds_sync();
     }
 
-    // T_b = T diag(beta) -> workspace as bf16 fragments: lane l of fragment f
-    // holds row sig(cb, l % 16), columns c0 .. c0 + 7 (c0 = 32 kk + 8 (l / 16)),
-    // when that granule reaches the diagonal
+    // T_e = diag(el) T diag(beta), el = exp(G_L - G) per row -> workspace as
+    // bf16 fragments: lane l of fragment f holds row sig(cb, l % 16), columns
+    // c0 .. c0 + 7 (c0 = 32 kk + 8 (l / 16)), when that granule reaches the
+    // diagonal
+    const float GL2 = sG[C - 1];
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
         if (frag_live(f, lane)) {
@@ -527,9 +543,54 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             const float4 e = *reinterpret_cast<const float4*>(row + 4 * ((q4 + 1) ^ (rr >> 2)));
             const float4 b0 = *reinterpret_cast<const float4*>(sBt + c0);
             const float4 b1 = *reinterpret_cast<const float4*>(sBt + c0 + 4);
+            const float el = __builtin_amdgcn_exp2f(GL2 - sG[r]);
             *reinterpret_cast<s16x8*>(dstT + FRAG_BYTES * f + 16 * lane) =
-                s16x8{bf16_bits(a.x * b0.x), bf16_bits(a.y * b0.y), bf16_bits(a.z * b0.z), bf16_bits(a.w * b0.w),
-                      bf16_bits(e.x * b1.x), bf16_bits(e.y * b1.y), bf16_bits(e.z * b1.z), bf16_bits(e.w * b1.w)};
+                s16x8{bf16_bits(el * (a.x * b0.x)), bf16_bits(el * (a.y * b0.y)), bf16_bits(el * (a.z * b0.z)),
+                      bf16_bits(el * (a.w * b0.w)), bf16_bits(el * (e.x * b1.x)), bf16_bits(el * (e.y * b1.y)),
+                      bf16_bits(el * (e.z * b1.z)), bf16_bits(el * (e.w * b1.w))};
+        }
+    }
+
+    // PT = P T diag(beta), formed transposed (PT^T = (T diag(beta))^T P^T) so
+    // that lane (g, n) ends with four consecutive columns of one row.  Output
+    // tile (a, cb) covers columns 16 a .. 16 a + 15 and rows sig(cb, .); its
+    // k-steps q run over the rows s of T diag(beta) that can be nonzero for
+    // both factors.  A operand (a, q): lane (g, n) holds T[s][16 a + n] beta,
+    // s = 32 q + 8 g + i, gathered from the fp32 blocks (block row 2 q + g / 2;
+    // blocks above the diagonal are zero); B operand (cb, q): P fragment
+    // (cb, q) from LDS.  Granules wholly above the diagonal are not written.
+    const unsigned char* sPw = sPall + w * SLOT_BYTES;
+    unsigned char* dstP = pps + ((size_t)x * Hv + vh) * SLOT_STRIDE;
+    s16x8 ta[6];   // (a, q) = (0, 0) (0, 1) (1, 0) (1, 1) (2, 1) (3, 1)
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+        const int a = u < 4 ? u >> 1 : u - 2;
+        const int q = u < 4 ? u & 1 : 1;
+        const int ib = 2 * q + (g >> 1);
+        const float* blk = lds + (ib == a ? 272 * ib : 1088 + 256 * ((ib - 1) * ib / 2 + a));
+        const float bt = sBt[16 * a + n];
+        float v8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int rr = 8 * (g & 1) + i;
+            v8[i] = ib >= a ? blk[blk_elem(rr, n)] * bt : 0.f;
+        }
+        ta[u] = s16x8{bf16_bits(v8[0]), bf16_bits(v8[1]), bf16_bits(v8[2]), bf16_bits(v8[3]),
+                      bf16_bits(v8[4]), bf16_bits(v8[5]), bf16_bits(v8[6]), bf16_bits(v8[7])};
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const s16x8 p0 = lds_read16(sPw + FRAG_BYTES * cb + 16 * lane);
+        const s16x8 p1 = cb >= 2 ? lds_read16(sPw + FRAG_BYTES * (cb + 2) + 16 * lane) : s16x8{};
+#pragma unroll
+        for (int a = 0; a < (cb < 2 ? 2 : 4); ++a) {
+            f32x4 acc = zero4();
+            if (a < 2) acc = mfma_bf16(ta[2 * a], p0, acc);
+            if (cb >= 2) acc = mfma_bf16(ta[a < 2 ? 2 * a + 1 : a + 2], p1, acc);
+            const int f = a < 2 ? cb : cb + 2, gp = 2 * (a & 1) + (g >> 1);
+            if (frag_live(f, 16 * gp + n))
+                *reinterpret_cast<s16x4*>(dstP + FRAG_BYTES * f + 16 * (16 * gp + n) + 8 * (g & 1)) =
+                    s16x4{bf16_bits(acc[0]), bf16_bits(acc[1]), bf16_bits(acc[2]), bf16_bits(acc[3])};
         }
     }
 }
@@ -537,54 +598,57 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // The state spine.  One workgroup per (sequence, v-head, 32 dv columns), four
 // waves, one per SIMD (wave w runs on SIMD w):
+//   the loader (0): all of the workgroup's memory traffic into LDS, by
+//     buffer->LDS DMA: in step c, chunk c's Q, chunk c + 3's ring stage and
+//     chunk c + 1's output slot.  A DMA blocks the wave that issues it while
+//     the compute unit's vector-memory path is busy, so no other wave issues
+//     any; and the ring and output slots are filled two steps before they are
+//     read, which covers the memory latency.
+//   the output wave (1): one chunk behind the recurrence, O = gm (Q h) + PT R
+//     for all 32 columns (PT R = P Delta).
 //   recurrence waves (2, 3): 16 columns each; the fp32 state h lives in MFMA
 //     accumulators and walks the chunks in order:
-//       X = K h,  R = V - gm X,  Delta = T_b R,  h <- gamma_L h + K^T (el Delta)
-//     where T_b = T diag(beta), so Delta = T_b V - T_b diag(gm) K h is the WY
-//     form's U - W h.  The chunk's bf16 state and Delta go to the output wave
-//     of the same columns through a double-buffered LDS exchange.
-//   output waves (0, 1): one chunk behind, O = gm (Q h) + P Delta for the
-//     same 16 columns (P = Gamma o lower_incl(Q K^T) from the workspace), and
-//     the loaders of the workgroup's LDS rings, wave 0 the K rows and P,
-//     wave 1 the V rows and Q.
-// An LDS read costs ~450 cycles, so a recurrence wave reads every operand of
-// chunk c + 1 while it computes chunk c: the K fragments of X and the
-// transposed K fragments of the update from the ring, V from the ring, and
-// T_b with the per-row decay factors straight from the workspace (seven
-// contiguous 1 KiB loads; the compute unit's vector-memory path is shared
-// with the ring DMA, so the recurrence waves keep their own memory loads few).
-// The per-row factors reach the lanes that need them by a DPP row broadcast:
-// recurrence lane (g, 4 cb + r) holds (gm, el) of row sig(cb, 4g + r), which
-// every lane of its row of 16 needs for accumulator register r of tile cb.
+//       X = K h,  R = V - gm X,  Delta_e = T_e R,  h <- gamma_L h + K^T Delta_e.
+//     The chunk's bf16 state and R go to the output wave through a
+//     double-buffered LDS exchange.  A recurrence wave is bound by its own
+//     instruction issue: every operand of chunk c + 1 comes from LDS, read
+//     while it computes chunk c (K fragments of X, transposed K fragments of
+//     the update, V, T_e, gm), and its VALU work is only what the recurrence
+//     needs: the state's bf16 copy, its decay, R and the two roundings to
+//     bf16.  gm reaches the lanes that need it as a table in LDS: lane group g
+//     reads the 16 factors of its accumulator rows with 4 broadcast reads.
 //
-// LDS (bytes).  Recurrence ring stage (four stages, three chunks ahead):
+// LDS (bytes).  Recurrence ring stage (three stages):
 //   K rows (64 x 256 B), granule q of row r at q ^ fK(r), fK(r) = 4 (r%4) + (r/8)%2
 //   V rows of the workgroup's 32 columns (64 x 64 B)
-// Output ring slot (two slots, each filled one step before it is read): Q
-// rows laid out as K, the six P fragments, gm in output-lane order [n][cb].
+//   T_e fragments (6 KiB), then gm by lane group and gamma_L (1 KiB)
+// Output slot (three): the six PT fragments, gm in output-lane order [n][cb].
+// Q slot (two): Q rows laid out as K.
 // Exchange, per recurrence wave and chunk parity: the bf16 state fragments
-// (4 x 1 KiB) and the bf16 Delta fragments (2 x 1 KiB), lane-major.
+// (4 x 1 KiB) and the bf16 R fragments (2 x 1 KiB), lane-major.
 constexpr int RS_K = 0;
 constexpr int RS_V = 16384;
-constexpr int RS_BYTES = 20480;
-constexpr int N_RS = 4;
+constexpr int RS_TE = 20480;
+constexpr int RS_SC = RS_TE + SLOT_BYTES;
+constexpr int RS_BYTES = RS_SC + 1024;
+constexpr int N_RS = 3;
+constexpr int N_OS = 3;
 constexpr int OS_BASE = N_RS * RS_BYTES;
-constexpr int OS_Q = 0;
-constexpr int OS_P = 16384;
-constexpr int OS_GM = OS_P + SLOT_BYTES;
-constexpr int OS_BYTES = 23552;
-constexpr int EX_BASE = OS_BASE + 2 * OS_BYTES;
+constexpr int OS_P = 0;
+constexpr int OS_GM = SLOT_BYTES;
+constexpr int OS_BYTES = SLOT_BYTES + 256;
+constexpr int QS_BASE = OS_BASE + N_OS * OS_BYTES;
+constexpr int QS_BYTES = 16384;
+constexpr int EX_BASE = QS_BASE + 2 * QS_BYTES;
 constexpr int EX_BYTES = 6144;
 constexpr int SPINE_LDS = EX_BASE + 4 * EX_BYTES;
 static_assert(SPINE_LDS <= 160 * 1024, "the spine's LDS");
-static_assert(OS_GM + 256 <= OS_BYTES, "output slot layout");
-// DMA operations per chunk: output wave 0 loads K (16 pieces) into the ring
-// and P (6 pieces) with gm (1) into an output slot; output wave 1 loads V (4
-// pieces) into the ring and Q (16 pieces) into the output slot.  Each also
-// stores its 16 columns of a chunk's outputs (4 stores).
-constexpr int DMA_REC0 = 16, DMA_OUT0 = 7;
-constexpr int DMA_REC1 = 4, DMA_OUT1 = 16;
-constexpr int OUT_STORES = 4;
+static_assert(OS_GM + 256 <= OS_BYTES && OS_BYTES % 256 == 0, "output slot layout");
+// DMA operations per chunk: K (16 pieces), T_e (6), the recurrence factors (1)
+// and V (4) into a ring stage; PT (6) and gm (1) into an output slot.
+constexpr int DMA_REC = 16 + NFRAG + 1 + 4;
+constexpr int DMA_OUT = NFRAG + 1;
+constexpr int DMA_Q = 16;
 
 // Batches of buffer->LDS DMAs into consecutive 1 KiB pieces of LDS starting at
 // the LDS byte address `lds`: M0 is set once and advanced by one scalar add per
@@ -650,18 +714,13 @@ __device__ __forceinline__ s16x8 join(s16x4 a, s16x4 b) {
     return s16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// Lane j of each row of 16 lanes, to every lane of that row.
-template <int J>
-__device__ __forceinline__ float row_bcast(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xf, 0xf, false));
-}
-
-// Per-lane DMA byte offsets of the output waves, chunk-independent.
+// Per-lane DMA byte offsets of the loader, chunk-independent.
 struct LoadOffsets {
-    uint32_t kv[8], ks[16];   // K and Q pieces 0..15 (lane offsets repeat every 8)
+    uint32_t kv[8], ks[16];   // K pieces 0..15 (lane offsets repeat every 8)
     uint32_t v, vs[4];        // V pieces 0..3
-    uint32_t pv[NFRAG], ps[NFRAG];   // P fragments (granules above the diagonal out of range)
-    uint32_t gmv;             // gm, 64 lanes x 4 bytes
+    uint32_t fv[NFRAG], fs[NFRAG];   // T_e / PT fragments (granules above the diagonal out of range)
+    uint32_t scv;             // the recurrence factors, 1 KiB
+    uint32_t gmv;             // gm in output-lane order, 64 lanes x 4 bytes
 };
 
 __device__ __forceinline__ LoadOffsets load_offsets(int lane, int Hk, int Hv) {
@@ -678,9 +737,10 @@ __device__ __forceinline__ LoadOffsets load_offsets(int lane, int Hk, int Hv) {
     for (int j = 0; j < 4; ++j) o.vs[j] = __builtin_amdgcn_readfirstlane((uint32_t)(16 * j) * v_row);
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
-        o.pv[f] = frag_live(f, lane) ? 16u * lane : 0x80000000u;
-        o.ps[f] = 1024u * f;
+        o.fv[f] = frag_live(f, lane) ? 16u * lane : 0x80000000u;
+        o.fs[f] = 1024u * f;
     }
+    o.scv = (uint32_t)SLOT_BYTES + 16u * lane;
     o.gmv = (uint32_t)SLOT_BYTES + 4u * lane;
     return o;
 }
@@ -705,47 +765,46 @@ struct SpineArgs {
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* v;
-    const unsigned char* tbs;   // T_b slots (fragments, then (gm, el, gamma_L) per recurrence lane)
-    const unsigned char* pps;   // P slots (fragments, then gm per output lane)
+    const unsigned char* tes;   // T_e slots (fragments, then gm by lane group and gamma_L)
+    const unsigned char* pts;   // PT slots (fragments, then gm by output lane)
     long row0, len;
     long slot0;
     int nc, Hk, Hv, kh, vh, tile;
 };
 
-// Output wave j's share of chunk cc's recurrence stage: K (j = 0) or V (j = 1);
-// rows past the chunk read as zero.
-__device__ __forceinline__ void issue_rec(unsigned char* ring, const LoadOffsets& o, const SpineArgs& a,
-                                          int cc, int j) {
+// Chunk cc's ring stage: K, T_e, the recurrence factors and V; rows past the
+// chunk read as zero.
+__device__ __forceinline__ void issue_rec(unsigned char* ring, const LoadOffsets& o, const SpineArgs& a, int cc) {
     const ChunkRows cr = chunk_rows(a.row0, a.len, cc);
-    const uint32_t base = lds_u32(ring + (cc % N_RS) * RS_BYTES);
-    if (j == 0) {
-        const uint32_t k_row = (uint32_t)a.Hk * D * 2u;
-        const Rsrc rk = make_dma_rsrc(a.k + (cr.r0 * a.Hk + a.kh) * D, cr.L * k_row);
-        dma_x8(rk, base + RS_K, o.kv, &o.ks[0]);
-        dma_x8(rk, base + RS_K + 8192, o.kv, &o.ks[8]);
-    } else {
-        const uint32_t v_row = (uint32_t)a.Hv * D * 2u;
-        const Rsrc rv = make_dma_rsrc(a.v + (cr.r0 * a.Hv + a.vh) * D + a.tile * TILE_COLS, cr.L * v_row);
-        dma_x4(rv, base + RS_V, o.v, o.v, o.v, o.v, o.vs[0], o.vs[1], o.vs[2], o.vs[3]);
-    }
+    unsigned char* S = ring + (cc % N_RS) * RS_BYTES;
+    const uint32_t base = lds_u32(S);
+    const uint32_t k_row = (uint32_t)a.Hk * D * 2u;
+    const Rsrc rk = make_dma_rsrc(a.k + (cr.r0 * a.Hk + a.kh) * D, cr.L * k_row);
+    dma_x8(rk, base + RS_K, o.kv, &o.ks[0]);
+    dma_x8(rk, base + RS_K + 8192, o.kv, &o.ks[8]);
+    const Rsrc rt = make_dma_rsrc(a.tes + ((size_t)(a.slot0 + cc) * a.Hv + a.vh) * SLOT_STRIDE, SLOT_STRIDE);
+    dma_x6(rt, base + RS_TE, o.fv, o.fs);
+    dma16(rt, S + RS_SC, o.scv, 0);
+    const uint32_t v_row = (uint32_t)a.Hv * D * 2u;
+    const Rsrc rv = make_dma_rsrc(a.v + (cr.r0 * a.Hv + a.vh) * D + a.tile * TILE_COLS, cr.L * v_row);
+    dma_x4(rv, base + RS_V, o.v, o.v, o.v, o.v, o.vs[0], o.vs[1], o.vs[2], o.vs[3]);
 }
 
-// Output wave j's share of chunk cc's output slot: P and gm (j = 0) or Q (j = 1).
-__device__ __forceinline__ void issue_out(unsigned char* slot, const LoadOffsets& o, const SpineArgs& a,
-                                          int cc, int j) {
+// Chunk cc's output slot: PT and gm.
+__device__ __forceinline__ void issue_out(unsigned char* slot, const LoadOffsets& o, const SpineArgs& a, int cc) {
+    const Rsrc rp = make_dma_rsrc(a.pts + ((size_t)(a.slot0 + cc) * a.Hv + a.vh) * SLOT_STRIDE, SLOT_BYTES + 256);
+    dma_x6(rp, lds_u32(slot) + OS_P, o.fv, o.fs);
+    dma4(rp, slot + OS_GM, o.gmv);
+}
+
+// Chunk cc's Q rows into a Q slot, laid out as K in the ring.
+__device__ __forceinline__ void issue_q(unsigned char* slot, const LoadOffsets& o, const SpineArgs& a, int cc) {
+    const ChunkRows cr = chunk_rows(a.row0, a.len, cc);
+    const uint32_t q_row = (uint32_t)a.Hk * D * 2u;
+    const Rsrc rq = make_dma_rsrc(a.q + (cr.r0 * a.Hk + a.kh) * D, cr.L * q_row);
     const uint32_t base = lds_u32(slot);
-    if (j == 0) {
-        const Rsrc rp = make_dma_rsrc(a.pps + ((size_t)(a.slot0 + cc) * a.Hv + a.vh) * SLOT_STRIDE,
-                                      SLOT_BYTES + 256);
-        dma_x6(rp, base + OS_P, o.pv, o.ps);
-        dma4(rp, slot + OS_GM, o.gmv);
-    } else {
-        const ChunkRows cr = chunk_rows(a.row0, a.len, cc);
-        const uint32_t q_row = (uint32_t)a.Hk * D * 2u;
-        const Rsrc rq = make_dma_rsrc(a.q + (cr.r0 * a.Hk + a.kh) * D, cr.L * q_row);
-        dma_x8(rq, base + OS_Q, o.kv, &o.ks[0]);
-        dma_x8(rq, base + OS_Q + 8192, o.kv, &o.ks[8]);
-    }
+    dma_x8(rq, base, o.kv, &o.ks[0]);
+    dma_x8(rq, base + 8192, o.kv, &o.ks[8]);
 }
 
 // Per-lane byte offsets of the operand reads (chunk-independent).
@@ -771,37 +830,65 @@ __device__ __forceinline__ FragOffsets frag_offsets(int g, int n, int half) {
     return o;
 }
 
-// A recurrence wave's operands of one chunk: from the workspace, the T_b
-// fragments and (gm, el, gamma_L); from the ring, the K fragments of X (by
-// k-step and tile), the transposed K fragments of the update (by state block
-// and k-step) and V in accumulator layout.
+// A recurrence wave's operands of one chunk, all from its ring stage: the K
+// fragments of X (by k-step and tile), the transposed K fragments of the
+// update (by state block and k-step), V in accumulator layout, the T_e
+// fragments, gm of this lane's accumulator rows (by tile) and gamma_L.
 struct RecOps {
-    s16x8 tb[NFRAG];
-    float4 sc;
     s16x8 kx[4][4];
     s16x8 kt[8][2];
     s16x4 vv[4];
+    s16x8 te[NFRAG];
+    f32x4 gm[4];
+    float gl;
 };
 
-// Memory loads of chunk cc's T_b and decay factors (zeros past the last chunk).
-__device__ __forceinline__ void rec_load_mem(RecOps& m, const uint32_t (&tbv)[NFRAG], const SpineArgs& a,
-                                             int cc, int lane) {
-    const bool live = cc < a.nc;
-    const rsrc_t rt = make_rsrc(a.tbs + ((size_t)(a.slot0 + (live ? cc : 0)) * a.Hv + a.vh) * SLOT_STRIDE,
-                                live ? (uint32_t)SLOT_STRIDE : 0u);
+// This lane's read addresses in one ring stage: a handful of 32-bit LDS
+// bases, every read a constant offset from one of them.  The stage's base
+// address passes through readfirstlane, so the compiler takes it as an opaque
+// wave-uniform value and does not rebuild each address from the ring index.
+typedef const __attribute__((address_space(3))) unsigned char* lds_cptr;
+__device__ __forceinline__ lds_cptr lds_at(uint32_t a) { return (lds_cptr)(uintptr_t)a; }
+struct StageAddr {
+    uint32_t k[4];    // K fragments of X, by k-step
+    uint32_t kt[4];   // transposed K fragments, by db / 2
+    uint32_t v;       // V
+    uint32_t te;      // T_e fragments
+    uint32_t gm;      // gm of this lane group's rows
+    uint32_t gl;      // gamma_L (wave-uniform)
+};
+__device__ __forceinline__ StageAddr stage_addr(const unsigned char* S, const FragOffsets& fo, int g, int lane) {
+    const uint32_t sb = __builtin_amdgcn_readfirstlane(lds_addr(S));
+    StageAddr s;
 #pragma unroll
-    for (int f = 0; f < NFRAG; ++f) m.tb[f] = buffer_load16(rt, tbv[f], 0);
-    const u32x4v s = __builtin_amdgcn_raw_buffer_load_b128(rt, (uint32_t)SLOT_BYTES + 16u * lane, 0, 0);
-    m.sc = make_float4(__uint_as_float(s[0]), __uint_as_float(s[1]), __uint_as_float(s[2]), __uint_as_float(s[3]));
+    for (int i = 0; i < 4; ++i) {
+        s.k[i] = sb + RS_K + fo.k[i];
+        s.kt[i] = sb + RS_K + fo.kt[i];
+    }
+    s.v = sb + RS_V + fo.v;
+    s.te = sb + RS_TE + 16 * lane;
+    s.gm = sb + RS_SC + 64 * g;
+    s.gl = sb + RS_SC + 256;
+    return s;
 }
-
-#define GDN_KX(S, kk, cb) lds_read16((S) + RS_K + fo.k[kk] + 256 * sig_tile(cb))
-#define GDN_KT(S, db, kk) join(lds_read_tr((S) + RS_K + fo.kt[(db) >> 1] + 8192 * (kk) + 8 * ((db) & 1)), \
-                               lds_read_tr((S) + RS_K + fo.kt[(db) >> 1] + 8192 * (kk) + 1024 + 8 * ((db) & 1)))
-#define GDN_VV(S, cb) lds_read_tr((S) + RS_V + fo.v + 64 * sig_tile(cb))
+__device__ __forceinline__ s16x8 lds_rd16(uint32_t base, int off) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) s16x8*>(lds_at(base) + off);
+}
+__device__ __forceinline__ s16x4 lds_rdtr(uint32_t base, int off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_at(base) + off));
+}
+#define GDN_KX(A, kk, cb) lds_rd16((A).k[kk], 256 * sig_tile(cb))
+#define GDN_KT(A, db, kk) join(lds_rdtr((A).kt[(db) >> 1], 8192 * (kk) + 8 * ((db) & 1)), \
+                               lds_rdtr((A).kt[(db) >> 1], 8192 * (kk) + 1024 + 8 * ((db) & 1)))
+#define GDN_VV(A, cb) lds_rdtr((A).v, 64 * sig_tile(cb))
+#define GDN_TE(A, f) lds_rd16((A).te, FRAG_BYTES * (f))
+#define GDN_GM(A, cb) (*reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lds_at((A).gm) + 16 * (cb)))
+#define GDN_GL(A) (*reinterpret_cast<const __attribute__((address_space(3))) float*>(lds_at((A).gl)))
 
 // Every ring read of one chunk at once (the first chunk, before the walk).
-__device__ __forceinline__ void rec_read_lds(RecOps& l, const unsigned char* S, const FragOffsets& fo) {
+__device__ __forceinline__ void rec_read_lds(RecOps& l, const unsigned char* S0, const FragOffsets& fo,
+                                             int g, int lane) {
+    const StageAddr S = stage_addr(S0, fo, g, lane);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -812,30 +899,27 @@ __device__ __forceinline__ void rec_read_lds(RecOps& l, const unsigned char* S, 
         for (int kk = 0; kk < 2; ++kk) l.kt[db][kk] = GDN_KT(S, db, kk);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) l.vv[cb] = GDN_VV(S, cb);
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f) l.te[f] = GDN_TE(S, f);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) l.gm[cb] = GDN_GM(S, cb);
+    l.gl = GDN_GL(S);
 }
 
-// R = V - gm X on accumulator register r of tile cb (row sig(cb, 4g + r))
-template <int CB>
-__device__ __forceinline__ void resid(f32x4& x, const s16x4 vv, float gm) {
-    x[0] = bf16_bits_to_f32((uint16_t)vv[0]) - row_bcast<4 * CB + 0>(gm) * x[0];
-    x[1] = bf16_bits_to_f32((uint16_t)vv[1]) - row_bcast<4 * CB + 1>(gm) * x[1];
-    x[2] = bf16_bits_to_f32((uint16_t)vv[2]) - row_bcast<4 * CB + 2>(gm) * x[2];
-    x[3] = bf16_bits_to_f32((uint16_t)vv[3]) - row_bcast<4 * CB + 3>(gm) * x[3];
-}
-template <int CB>
-__device__ __forceinline__ f32x4 scale_rows(const f32x4 x, float el) {
-    return f32x4{row_bcast<4 * CB + 0>(el) * x[0], row_bcast<4 * CB + 1>(el) * x[1],
-                 row_bcast<4 * CB + 2>(el) * x[2], row_bcast<4 * CB + 3>(el) * x[3]};
+// R = V - gm X on tile cb: register r is row sig(cb, 4g + r), whose gm this
+// lane holds in gm[r]
+__device__ __forceinline__ void resid(f32x4& x, const s16x4 vv, const f32x4 gm) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = fmaf(-gm[r], x[r], bf16_bits_to_f32((uint16_t)vv[r]));
 }
 
 // One recurrence step on chunk c (operands o), 16 columns; the next chunk's
-// operands go into on: its ring reads (stage Sn) spread between this step's
-// products, its memory loads issued right away.  The bf16 state and Delta go
-// to exchange slot E.
-__device__ __forceinline__ void rec_step(f32x4 (&h)[8], const RecOps& o, RecOps& on, const unsigned char* Sn,
-                                         unsigned char* E, const FragOffsets& fo, const uint32_t (&tbv)[NFRAG],
-                                         const SpineArgs& a, int cn, int lane)
+// operands go into on, read from ring stage Sn between this step's products.
+// The bf16 state and R go to exchange slot E.
+__device__ __forceinline__ void rec_step(f32x4 (&h)[8], const RecOps& o, RecOps& on, const unsigned char* Sn0,
+                                         unsigned char* E, const FragOffsets& fo, int g, int lane)
 {
+    const StageAddr Sn = stage_addr(Sn0, fo, g, lane);
     // state -> bf16 B operand, and to the output partner
     s16x8 hb[4];
 #pragma unroll
@@ -843,8 +927,6 @@ __device__ __forceinline__ void rec_step(f32x4 (&h)[8], const RecOps& o, RecOps&
         hb[kk] = frag_b(h[2 * kk], h[2 * kk + 1]);
         *reinterpret_cast<s16x8*>(E + 1024 * kk + 16 * lane) = hb[kk];
     }
-    // the next chunk's T_b and decay factors from the workspace
-    rec_load_mem(on, tbv, a, cn, lane);
     sched_fence();
     // X = K h, with the next chunk's update fragments of state blocks 0..3 read
     // in between; h scaled by gamma_L meanwhile (hb holds the state before it)
@@ -862,54 +944,52 @@ __device__ __forceinline__ void rec_step(f32x4 (&h)[8], const RecOps& o, RecOps&
                     on.kt[db][0] = GDN_KT(Sn, db, 0);
                     on.kt[db][1] = GDN_KT(Sn, db, 1);
                 } else {
-                    h[2 * (db - 4)] = h[2 * (db - 4)] * o.sc.z;
-                    h[2 * (db - 4) + 1] = h[2 * (db - 4) + 1] * o.sc.z;
+                    h[2 * (db - 4)] = h[2 * (db - 4)] * o.gl;
+                    h[2 * (db - 4) + 1] = h[2 * (db - 4) + 1] * o.gl;
                 }
             }
             sched_fence();
         }
     }
-    // the next chunk's K fragments of X into the registers X just read
+    // the next chunk's T_e and decay factors, and K fragments of X into the
+    // registers X just read
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f) on.te[f] = GDN_TE(Sn, f);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) on.gm[cb] = GDN_GM(Sn, cb);
+    on.gl = GDN_GL(Sn);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) on.kx[kk][cb] = GDN_KX(Sn, kk, cb);
     sched_fence();
-    // R = V - gm X, rounded to the B operand of Delta = T_b R
-    resid<0>(X[0], o.vv[0], o.sc.x);
-    resid<1>(X[1], o.vv[1], o.sc.x);
-    resid<2>(X[2], o.vv[2], o.sc.x);
-    resid<3>(X[3], o.vv[3], o.sc.x);
+    // R = V - gm X, rounded to the B operand of Delta_e = T_e R, and to the
+    // output partner
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) resid(X[cb], o.vv[cb], o.gm[cb]);
     const s16x8 rb0 = frag_b(X[0], X[1]), rb1 = frag_b(X[2], X[3]);
+    *reinterpret_cast<s16x8*>(E + 4096 + 16 * lane) = rb0;
+    *reinterpret_cast<s16x8*>(E + 5120 + 16 * lane) = rb1;
     sched_fence();
     f32x4 Dl[4];
-    Dl[0] = mfma_bf16(o.tb[0], rb0, zero4());
+    Dl[0] = mfma_bf16(o.te[0], rb0, zero4());
     on.kx[2][0] = GDN_KX(Sn, 2, 0);
     sched_fence();
-    Dl[1] = mfma_bf16(o.tb[1], rb0, zero4());
+    Dl[1] = mfma_bf16(o.te[1], rb0, zero4());
     on.kx[2][1] = GDN_KX(Sn, 2, 1);
     sched_fence();
-    Dl[2] = mfma_bf16(o.tb[2], rb0, zero4());
+    Dl[2] = mfma_bf16(o.te[2], rb0, zero4());
     on.kx[2][2] = GDN_KX(Sn, 2, 2);
     sched_fence();
-    Dl[3] = mfma_bf16(o.tb[3], rb0, zero4());
+    Dl[3] = mfma_bf16(o.te[3], rb0, zero4());
     on.kx[2][3] = GDN_KX(Sn, 2, 3);
     sched_fence();
-    Dl[2] = mfma_bf16(o.tb[4], rb1, Dl[2]);
-    Dl[3] = mfma_bf16(o.tb[5], rb1, Dl[3]);
+    Dl[2] = mfma_bf16(o.te[4], rb1, Dl[2]);
+    Dl[3] = mfma_bf16(o.te[5], rb1, Dl[3]);
     sched_fence();
-    // Delta to the output partner; el Delta as the update's B operand
-    const s16x8 db0 = frag_b(Dl[0], Dl[1]), db1 = frag_b(Dl[2], Dl[3]);
-    *reinterpret_cast<s16x8*>(E + 4096 + 16 * lane) = db0;
-    *reinterpret_cast<s16x8*>(E + 5120 + 16 * lane) = db1;
-    sched_fence();
-    Dl[0] = scale_rows<0>(Dl[0], o.sc.y);
-    Dl[1] = scale_rows<1>(Dl[1], o.sc.y);
-    Dl[2] = scale_rows<2>(Dl[2], o.sc.y);
-    Dl[3] = scale_rows<3>(Dl[3], o.sc.y);
     const s16x8 ds0 = frag_b(Dl[0], Dl[1]), ds1 = frag_b(Dl[2], Dl[3]);
     sched_fence();
-    // h <- gamma_L h + K^T (el Delta), with the rest of the next chunk's ring reads
+    // h <- gamma_L h + K^T Delta_e, with the rest of the next chunk's ring reads
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
         h[db] = mfma_bf16(o.kt[db][0], ds0, h[db]);
@@ -927,86 +1007,108 @@ __device__ __forceinline__ void rec_step(f32x4 (&h)[8], const RecOps& o, RecOps&
         if (db == 1) on.kt[6][1] = GDN_KT(Sn, 6, 1);
         if (db == 2) on.kt[7][0] = GDN_KT(Sn, 7, 0);
         if (db == 3) on.kt[7][1] = GDN_KT(Sn, 7, 1);
-        if (db == 4) on.vv[0] = GDN_VV(Sn, 0);
-        if (db == 5) on.vv[1] = GDN_VV(Sn, 1);
-        if (db == 6) on.vv[2] = GDN_VV(Sn, 2);
-        if (db == 7) on.vv[3] = GDN_VV(Sn, 3);
+        if (db == 4) { on.vv[0] = GDN_VV(Sn, 0); on.vv[1] = GDN_VV(Sn, 1); }
+        if (db == 5) { on.vv[2] = GDN_VV(Sn, 2); on.vv[3] = GDN_VV(Sn, 3); }
         sched_fence();
     }
 }
 #undef GDN_KX
 #undef GDN_KT
 #undef GDN_VV
+#undef GDN_TE
+#undef GDN_GM
+#undef GDN_GL
 // ring reads a recurrence step issues after its last exchange write: K
-// fragments 4 (k-step 3), transposed fragments of state blocks 4..7 (16
-// transposing reads) and V (4)
-constexpr int REC_READS_AFTER_EX = 24;
+// fragments of k-steps 2 and 3 (8), transposed fragments of state blocks 4..7
+// (16 transposing reads) and V (4)
+constexpr int REC_READS_AFTER_EX = 28;
 static_assert(REC_READS_AFTER_EX >= 15, "the wait below then allows at most 15 outstanding");
 
-// One output wave, chunk c: O = gm (Q h) + P Delta for its 16 columns, with Q,
-// P and gm from output slot Os and the bf16 state and Delta from exchange
-// slot E.  The products are formed transposed: a B-operand fragment of h or
-// Delta is the A operand of its transpose and an A-operand fragment of Q or P
-// the B operand of its transpose, so lane (g, n) register r of tile cb ends up
-// holding O[sig(cb, n)][4g + r], four consecutive columns of one row.  `ro`
-// covers exactly the chunk's rows.
+// The output wave, chunk c: O = gm (Q h) + PT R for the workgroup's 32
+// columns, with Q from Q slot Qs, PT and gm from output slot Os, and the bf16
+// state and R of column half u from exchange slot E[u].  The products are
+// formed transposed: a B-operand fragment of h or R is the A operand of its
+// transpose and an A-operand fragment of Q or PT the B operand of its
+// transpose, so lane (g, n) register r of tile cb ends up holding
+// O[sig(cb, n)][4g + r] of its column half, four consecutive columns of one
+// row.  Each Q fragment serves both halves; the next k-step's fragments are
+// read while this one's products run.  `ro` covers exactly the chunk's rows.
 template <bool kOutF32>
-__device__ __forceinline__ void out_step(const unsigned char* Os, const unsigned char* E, const FragOffsets& fo,
-                                         rsrc_t ro, uint32_t lane_off, const uint32_t (&soff)[4], int n, int lane)
+__device__ __forceinline__ void out_step(const unsigned char* Qs, const unsigned char* Os, const unsigned char* E0,
+                                         const unsigned char* E1, const FragOffsets& fo, rsrc_t ro,
+                                         const uint32_t (&lane_off)[2], const uint32_t (&soff)[4], int n, int lane)
 {
-    s16x8 hb[4];
+    s16x8 qf[2][4], hf[2][2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) hb[kk] = lds_read16(E + 1024 * kk + 16 * lane);
-    const s16x8 db0 = lds_read16(E + 4096 + 16 * lane), db1 = lds_read16(E + 5120 + 16 * lane);
-    const float4 g4 = *reinterpret_cast<const float4*>(Os + OS_GM + 16 * n);
-    f32x4 Y[4];
+    for (int cb = 0; cb < 4; ++cb) qf[0][cb] = lds_read16(Qs + fo.k[0] + 256 * sig_tile(cb));
+    hf[0][0] = lds_read16(E0 + 16 * lane);
+    hf[0][1] = lds_read16(E1 + 16 * lane);
+    f32x4 Y[2][4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) Y[cb] = zero4();
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) Y[u][cb] = zero4();
+    s16x8 rb[2][2], pf[NFRAG];
+    float4 g4;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        s16x8 qf[4];
+        const int p = kk & 1;
+        if (kk < 3) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) qf[cb] = lds_read16(Os + OS_Q + fo.k[kk] + 256 * sig_tile(cb));
+            for (int cb = 0; cb < 4; ++cb) qf[p ^ 1][cb] = lds_read16(Qs + fo.k[kk + 1] + 256 * sig_tile(cb));
+            hf[p ^ 1][0] = lds_read16(E0 + 1024 * (kk + 1) + 16 * lane);
+            hf[p ^ 1][1] = lds_read16(E1 + 1024 * (kk + 1) + 16 * lane);
+        }
+        if (kk == 2) {
+            g4 = *reinterpret_cast<const float4*>(Os + OS_GM + 16 * n);
+            rb[0][0] = lds_read16(E0 + 4096 + 16 * lane);
+            rb[1][0] = lds_read16(E1 + 4096 + 16 * lane);
+            rb[0][1] = lds_read16(E0 + 5120 + 16 * lane);
+            rb[1][1] = lds_read16(E1 + 5120 + 16 * lane);
+        }
+        if (kk == 3) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) Y[cb] = mfma_bf16(hb[kk], qf[cb], Y[cb]);
+            for (int f = 0; f < NFRAG; ++f) pf[f] = lds_read16(Os + OS_P + 1024 * f + 16 * lane);
+        }
+        sched_fence();
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            Y[0][cb] = mfma_bf16(hf[p][0], qf[p][cb], Y[0][cb]);
+            Y[1][cb] = mfma_bf16(hf[p][1], qf[p][cb], Y[1][cb]);
+        }
+        sched_fence();
     }
-    s16x8 pf[NFRAG];
 #pragma unroll
-    for (int f = 0; f < NFRAG; ++f) pf[f] = lds_read16(Os + OS_P + 1024 * f + 16 * lane);
-    f32x4 O[4];
-    O[0] = mfma_bf16(db0, pf[0], Y[0] * g4.x);
-    O[1] = mfma_bf16(db0, pf[1], Y[1] * g4.y);
-    O[2] = mfma_bf16(db0, pf[2], Y[2] * g4.z);
-    O[3] = mfma_bf16(db0, pf[3], Y[3] * g4.w);
-    O[2] = mfma_bf16(db1, pf[4], O[2]);
-    O[3] = mfma_bf16(db1, pf[5], O[3]);
-    // hardware RNE conversion; rows past a partial chunk fall outside `ro`
+    for (int u = 0; u < 2; ++u) {
+        f32x4 O[4];
+        O[0] = mfma_bf16(rb[u][0], pf[0], Y[u][0] * g4.x);
+        O[1] = mfma_bf16(rb[u][0], pf[1], Y[u][1] * g4.y);
+        O[2] = mfma_bf16(rb[u][0], pf[2], Y[u][2] * g4.z);
+        O[3] = mfma_bf16(rb[u][0], pf[3], Y[u][3] * g4.w);
+        O[2] = mfma_bf16(rb[u][1], pf[4], O[2]);
+        O[3] = mfma_bf16(rb[u][1], pf[5], O[3]);
+        // hardware RNE conversion; rows past a partial chunk fall outside `ro`
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        const f32x4 v = O[cb];
-        if (kOutF32) {
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(v[0]), __float_as_uint(v[1]),
-                                                          __float_as_uint(v[2]), __float_as_uint(v[3])},
-                                                   ro, lane_off, soff[cb], 0);
-        } else {
-            const uint32_t lo = (uint16_t)bf16_bits(v[0]) | ((uint32_t)(uint16_t)bf16_bits(v[1]) << 16);
-            const uint32_t hi = (uint16_t)bf16_bits(v[2]) | ((uint32_t)(uint16_t)bf16_bits(v[3]) << 16);
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2v{lo, hi}, ro, lane_off, soff[cb], 0);
+        for (int cb = 0; cb < 4; ++cb) {
+            const f32x4 v = O[cb];
+            if (kOutF32) {
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                              __float_as_uint(v[2]), __float_as_uint(v[3])},
+                                                       ro, lane_off[u], soff[cb], 0);
+            } else {
+                const uint32_t lo = (uint16_t)bf16_bits(v[0]) | ((uint32_t)(uint16_t)bf16_bits(v[1]) << 16);
+                const uint32_t hi = (uint16_t)bf16_bits(v[2]) | ((uint32_t)(uint16_t)bf16_bits(v[3]) << 16);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2v{lo, hi}, ro, lane_off[u], soff[cb], 0);
+            }
         }
     }
-}
-
-// s_waitcnt vmcnt for the output waves' DMA bookkeeping (constant operands)
-template <int J>
-__device__ __forceinline__ void out_wait_rec_only() {   // all but this step's recurrence DMA and stores
-    __builtin_amdgcn_s_waitcnt(GDN_VMCNT((J == 0 ? DMA_REC0 : DMA_REC1) + OUT_STORES));
 }
 
 template <bool kOutF32>
 __global__ void __launch_bounds__(256, 1)
 gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const float* h0, void* __restrict__ out, float* h_final,
-                 const unsigned char* __restrict__ tbs, const unsigned char* __restrict__ pps,
+                 const unsigned char* __restrict__ tes, const unsigned char* __restrict__ pts,
                  int T, int Hk, int Hv, const int32_t* __restrict__ cu,
                  const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ order,
                  int nc_dense, long n_slots)
@@ -1027,7 +1129,7 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     a.tile = lin % N_TILES;
     const int b = order ? order[blockIdx.y] : (int)blockIdx.y;
     a.kh = a.vh / (Hv / Hk);
-    a.q = q; a.k = k; a.v = v; a.tbs = tbs; a.pps = pps; a.Hk = Hk; a.Hv = Hv;
+    a.q = q; a.k = k; a.v = v; a.tes = tes; a.pts = pts; a.Hk = Hk; a.Hv = Hv;
     seq_rows(cu, b, T, &a.row0, &a.len);
     a.slot0 = cu ? (long)chunk_base[b] : (long)b * nc_dense;
     int nc = (int)((a.len + C - 1) / C);
@@ -1039,51 +1141,58 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const FragOffsets fo = frag_offsets(g, n, half);
     unsigned char* ex = lds + EX_BASE + 2 * half * EX_BYTES;   // this column half's exchange, parity 0
 
-    if (w < 2) {   // output waves: chunk c - 1 in step c, and the DMA
-        const int j = half;
+    if (w == 0) {   // the loader: in step c, chunk c's Q, chunk c + 3's ring stage and chunk c + 1's output slot
         const LoadOffsets o = load_offsets(lane, Hk, Hv);
+        for (int cc = 0; cc < 2 && cc < nc; ++cc) issue_rec(ring, o, a, cc);
+        __builtin_amdgcn_s_waitcnt(GDN_VMCNT(0));
+        ring_barrier();   // chunks 0 and 1 are in the ring
+        if (2 < nc) issue_rec(ring, o, a, 2);
+        if (0 < nc) issue_out(lds + OS_BASE, o, a, 0);
+        for (int c = 0; c <= nc; ++c) {
+            ring_barrier();
+            // stage c % 3 held chunk c, whose ring reads ended in step c - 1 (in
+            // the prologue for chunk 0); slot (c + 1) % 3 held chunk c - 2, read
+            // in step c - 1
+            // Q slot c % 2 held chunk c - 2, read in step c - 1
+            if (c < nc) issue_q(lds + QS_BASE + (c & 1) * QS_BYTES, o, a, c);
+            const bool rr = c + 3 < nc, oo = c + 1 < nc;
+            if (rr) issue_rec(ring, o, a, c + 3);
+            if (oo) issue_out(lds + OS_BASE + ((c + 1) % N_OS) * OS_BYTES, o, a, c + 1);
+            // chunk c's Q and what was issued before this step (chunk c + 2's
+            // stage, chunk c's slot) land before the next barrier
+            if (rr && oo) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_REC + DMA_OUT));
+            else if (rr) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_REC));
+            else if (oo) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_OUT));
+            else __builtin_amdgcn_s_waitcnt(GDN_VMCNT(0));
+        }
+        return;
+    }
+    if (w == 1) {   // the output wave: chunk c - 1 in step c
         constexpr uint32_t es = kOutF32 ? 4u : 2u;
         const uint32_t rs = __builtin_amdgcn_readfirstlane((uint32_t)Hv * D * es);
-        const uint32_t lane_off = (uint32_t)(8 * (n >> 2) + (n & 3)) * rs +
-                                  (uint32_t)(a.tile * TILE_COLS + 16 * half + 4 * g) * es;
+        uint32_t lane_off[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            lane_off[u] = (uint32_t)(8 * (n >> 2) + (n & 3)) * rs + (uint32_t)(a.tile * TILE_COLS + 16 * u + 4 * g) * es;
         uint32_t soff[4];
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) soff[cb] = (uint32_t)sig_tile(cb) * rs;
         const uint32_t rlo = __builtin_amdgcn_readfirstlane((uint32_t)a.row0);
         const uint32_t rhi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)a.row0 >> 32));
         char* obase = reinterpret_cast<char*>(out) + ((((size_t)rhi << 32) | rlo) * Hv + a.vh) * D * es;
-        // chunks 0 and 1 in the ring before the first barrier, chunk 2 on its way
-        for (int cc = 0; cc < 3 && cc < nc; ++cc) issue_rec(ring, o, a, cc, j);
-        if (nc > 2) {
-            if (j == 0) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_REC0));
-            else __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_REC1));
-        } else {
-            __builtin_amdgcn_s_waitcnt(GDN_VMCNT(0));
-        }
+        const FragOffsets fq = frag_offsets(g, n, 0);
+        ring_barrier();   // the prologue
         for (int c = 0; c <= nc; ++c) {
-            // the ring holds chunks c and c + 1; output slot (c - 1) % 2 holds chunk c - 1
             ring_barrier();
-            // slot c % 2 held chunk c - 2, read in step c - 1; stage (c + 3) % 4
-            // held chunk c - 1, whose reads ended in step c - 1
-            if (c < nc) issue_out(lds + OS_BASE + (c & 1) * OS_BYTES, o, a, c, j);
-            const bool rec = c + 3 < nc;
-            if (rec) issue_rec(ring, o, a, c + 3, j);
             if (c >= 1) {
                 const long rem = a.len - (long)(c - 1) * C;
                 const rsrc_t ro = make_rsrc(obase + (size_t)(c - 1) * C * rs, (uint32_t)min((long)C, rem) * rs);
-                out_step<kOutF32>(lds + OS_BASE + ((c - 1) & 1) * OS_BYTES, ex + ((c - 1) & 1) * EX_BYTES, fo, ro,
+                const int par = (c - 1) & 1;
+                out_step<kOutF32>(lds + QS_BASE + par * QS_BYTES, lds + OS_BASE + ((c + 2) % N_OS) * OS_BYTES,
+                                  lds + EX_BASE + par * EX_BYTES, lds + EX_BASE + (2 + par) * EX_BYTES, fq, ro,
                                   lane_off, soff, n, lane);
             }
-            // chunk c's slot and chunk c + 2's stage have landed before the next
-            // barrier; chunk c + 3's stage (and this step's stores) may still fly
-            if (rec) {
-                if (c >= 1) { if (j == 0) out_wait_rec_only<0>(); else out_wait_rec_only<1>(); }
-                else if (j == 0) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_REC0));
-                else __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_REC1));
-            } else {
-                if (c >= 1) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(OUT_STORES));
-                else __builtin_amdgcn_s_waitcnt(GDN_VMCNT(0));
-            }
+            // every read of this step's slots and exchange is done before the barrier
             wait_lgkm0();
         }
         return;
@@ -1104,25 +1213,27 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
         for (int db = 0; db < 8; ++db) h[db] = zero4();
     }
-    uint32_t tbv[NFRAG];   // T_b granules (out of range above the diagonal)
-#pragma unroll
-    for (int f = 0; f < NFRAG; ++f) tbv[f] = frag_live(f, lane) ? 16u * lane + 1024u * f : 0x80000000u;
     RecOps oA, oB;
-    rec_load_mem(oA, tbv, a, 0, lane);
-    // one barrier per step, nc + 1 steps as the output waves; the exchange
+    // one barrier per step after the prologue's, nc + 1 steps as the other
+    // waves; the exchange
     // writes are complete before each barrier (the LDS operations of one wave
     // complete in order, and more ring reads than can be in flight follow the
     // last write).  Written so that the second step of a pair is reachable only
     // through the first, which keeps the compiler's waits on the prefetched
     // reads where they are used.
-    ring_barrier();
-    if (nc > 0) rec_read_lds(oA, ring, fo);
+    ring_barrier();   // the prologue: chunks 0 and 1 are in the ring
+    if (nc > 0) rec_read_lds(oA, ring, fo, g, lane);
+    // everything loaded before the walk has arrived (chunk 0's stage is free
+    // for the loader from step 0 on): the loop's waits then account only for
+    // the walk's own reads
+    __builtin_amdgcn_s_waitcnt(0);
+    ring_barrier();   // step 0
     for (int c = 0; c < nc; c += 2) {
-        rec_step(h, oA, oB, ring + ((c + 1) % N_RS) * RS_BYTES, ex, fo, tbv, a, c + 1, lane);
+        rec_step(h, oA, oB, ring + ((c + 1) % N_RS) * RS_BYTES, ex, fo, g, lane);
         __builtin_amdgcn_s_waitcnt(GDN_LGKMCNT(15));
         ring_barrier();
         if (c + 1 >= nc) break;
-        rec_step(h, oB, oA, ring + ((c + 2) % N_RS) * RS_BYTES, ex + EX_BYTES, fo, tbv, a, c + 2, lane);
+        rec_step(h, oB, oA, ring + ((c + 2) % N_RS) * RS_BYTES, ex + EX_BYTES, fo, g, lane);
         __builtin_amdgcn_s_waitcnt(GDN_LGKMCNT(15));
         ring_barrier();
     }
@@ -1168,8 +1279,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
     int32_t* base = reinterpret_cast<int32_t*>(a.workspace);
     const int nc_dense = (a.T + C - 1) / C;
     const long n_slots = slot_count(a.B, a.T, packed);
-    unsigned char* tbs = reinterpret_cast<unsigned char*>(a.workspace) + table_bytes(a.B);
-    unsigned char* pps = tbs + (size_t)n_slots * a.Hv * SLOT_STRIDE;
+    unsigned char* tbs = reinterpret_cast<unsigned char*>(a.workspace) + table_bytes(a.B);   // T_e slots
+    unsigned char* pps = tbs + (size_t)n_slots * a.Hv * SLOT_STRIDE;                       // PT slots
     const int32_t* order = packed && a.B <= MAX_ORDERED ? base + a.B + 1 : nullptr;
     if (packed) {
         hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.B, a.T, base);
