@@ -52,7 +52,7 @@ typedef enum gdn_status {
     GDN_ERR_STASH = 7,         /* stash_seq_floats smaller than gdn_stash_seq_floats() */
     GDN_ERR_K_ROWS = 8,        /* k_rows outside 1..8 */
     GDN_ERR_STRIDE = 9,        /* a row stride shorter than the heads it must hold */
-    GDN_ERR_UNSUPPORTED = 10,  /* a documented branch that this library does not build */
+    GDN_ERR_SLABS = 10,        /* slab_entries smaller than k_rows (parent verify, fold restore) */
     GDN_ERR_HIP = 11           /* the HIP runtime refused a launch (text: gdn_last_route()) */
 } gdn_status;
 
@@ -189,9 +189,14 @@ int gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v,
  * Fold:
  *   na_tab: device int32 [B], accepted rows per sequence, clamped to 0..K;
  *           na = 0 leaves the state's bytes unchanged.
- *   hi_tables / slab_entries: the restore branch of a non-write-on-accept
- *           verify (word not set).  Not built here: hi_tables must be NULL,
- *           and with the word clear the fold changes nothing.
+ *   hi_tables / slab_entries: the restore branch, for a verify that ran in
+ *           parent mode (gdn_decode_verify_parent below, which leaves the
+ *           word clear).  NULL: with the word clear the fold changes nothing.
+ *           Otherwise, with the word clear, na = na_tab[b] < K puts back
+ *           slab na of sequence b (the state after its first na rows) as a
+ *           bitwise copy, and na = K keeps the state (which the parent verify
+ *           advanced through all K rows); with the word set the slabs are not
+ *           read.  slab_entries >= k_rows, else GDN_ERR_SLABS.
  *   k_rows: K of the verify that filled the stash, 1..8.
  * Errors: GDN_ERR_K_ROWS for k_rows outside 1..8; the others as below.
  */
@@ -217,7 +222,38 @@ int gdn_fold(float* const* h_table, const float* stash, const int32_t* na_tab,
              int k_rows, int B, int Hk, int Hv, int dk, int dv, int stash_seq_floats,
              int io_dtype, hipStream_t stream);
 
+/* Parent-mode verify (ssm_gdn_woa.rs, doc of gdn_wy4_fold: when the engaged
+ * word is clear "the parent kernel ran, and a partial accept (na < k_rows)
+ * restores Hi(na - 1) from hi_tables").  The pages give neither the parent
+ * kernel nor the slab layout; this library's reading, with Hi(r) the state
+ * after rows 0..r:
+ *   - it writes the outputs and the stash exactly as gdn_decode_verify does,
+ *     and leaves the engaged word alone (the caller clears it first, so the
+ *     fold takes the restore branch);
+ *   - it writes slab j = Hi(j - 1), the state after the first j rows, for
+ *     j = 0 .. k_rows - 1 (slab 0 is a copy of the state before the verify);
+ *   - it advances each state in place to Hi(k_rows - 1), the state after all
+ *     k_rows rows (the full accept).
+ *   hi_tables: device array [B] of device pointers; slab j of sequence b,
+ *           v-head vh, is the [dk][dv] fp32 block at
+ *           hi_tables[b] + (j*Hv + vh)*dk*dv floats (slabs laid out as states).
+ *   slab_entries: slabs behind each hi_tables[b]; at least k_rows
+ *           (GDN_ERR_SLABS otherwise).
+ * Every other argument as gdn_decode_verify.  The caller owns the slabs; the
+ * library writes slabs 0 .. k_rows - 1 of each sequence and nothing else. */
+int gdn_decode_verify_parent(float* const* h_table, float* const* hi_tables, int slab_entries,
+                             const void* q, const void* k, const void* v, const float* gate,
+                             const float* beta, void* out, float* stash, int B, int Hk, int Hv,
+                             int dk, int dv, int k_rows, int qk_stride, int v_stride, int gb_stride,
+                             int stash_seq_floats, int io_dtype, int out_dtype, hipStream_t stream);
+
 /* Validation of the calls above without launching (same return codes). */
+int gdn_decode_verify_parent_plan(float* const* h_table, float* const* hi_tables, int slab_entries,
+                                  const void* q, const void* k, const void* v, const float* gate,
+                                  const float* beta, void* out, float* stash, int B, int Hk, int Hv,
+                                  int dk, int dv, int k_rows, int qk_stride, int v_stride,
+                                  int gb_stride, int stash_seq_floats, int io_dtype, int out_dtype);
+
 int gdn_decode_verify_plan(float* const* h_table, const void* q, const void* k,
                            const void* v, const float* gate, const float* beta, void* out,
                            float* stash, int B, int Hk, int Hv, int dk, int dv, int k_rows,

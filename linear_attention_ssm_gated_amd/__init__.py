@@ -24,7 +24,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
 _STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_HEAD_GROUPS",
     4: "GDN_ERR_DIM_LIMIT", 5: "GDN_ERR_DTYPE", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_STASH",
-    8: "GDN_ERR_K_ROWS", 9: "GDN_ERR_STRIDE", 10: "GDN_ERR_UNSUPPORTED", 11: "GDN_ERR_HIP",
+    8: "GDN_ERR_K_ROWS", 9: "GDN_ERR_STRIDE", 10: "GDN_ERR_SLABS", 11: "GDN_ERR_HIP",
 }
 
 # name -> (restype, argtypes) of every entry point include/gdn.h declares
@@ -42,6 +42,8 @@ SIGNATURES = {
     "gdn_decode_verify_plan": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P, I, I]),
     "gdn_decode_verify_k4": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, I, I, P]),
     "gdn_decode_verify_k4_plan": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, I, I]),
+    "gdn_decode_verify_parent": (I, [P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, I, P]),
+    "gdn_decode_verify_parent_plan": (I, [P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, I]),
     "gdn_fold": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, I, P]),
     "gdn_fold_plan": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, I]),
     "gdn_decode_step": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, P]),
@@ -167,6 +169,16 @@ def gdn_decode_verify(h_table, q, k, v, gate, beta, out, stash, B, Hk, Hv, dk, d
         _ptr(h_table), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(out), _ptr(stash),
         B, Hk, Hv, dk, dv, k_rows, qk_stride, v_stride, gb_stride, stash_seq_floats,
         _ptr(engaged_flag), _dtype_code(q), _dtype_code(out), _stream(stream)))
+    return last_route()
+
+
+def gdn_decode_verify_parent(h_table, hi_tables, slab_entries, q, k, v, gate, beta, out, stash, B, Hk,
+                             Hv, dk, dv, k_rows, qk_stride, v_stride, gb_stride, stash_seq_floats,
+                             stream=None):
+    _check(library().gdn_decode_verify_parent(
+        _ptr(h_table), _ptr(hi_tables), slab_entries, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+        _ptr(beta), _ptr(out), _ptr(stash), B, Hk, Hv, dk, dv, k_rows, qk_stride, v_stride,
+        gb_stride, stash_seq_floats, _dtype_code(q), _dtype_code(out), _stream(stream)))
     return last_route()
 
 

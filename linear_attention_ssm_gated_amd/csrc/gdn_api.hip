@@ -93,13 +93,14 @@ int check_prefill(const gdn::PrefillArgs& a, bool* mfma, const char** why)
     return GDN_OK;
 }
 
-int check_verify(const gdn::VerifyArgs& a)
+// Validation of a verify; the parent verify (need_flag false) leaves the word
+// alone and takes no flag.
+int check_verify(const gdn::VerifyArgs& a, const char* who = "gdn_decode_verify", bool need_flag = true)
 {
-    const char* who = "gdn_decode_verify_k4";
     if (bad_dtype(a.io_dtype) || bad_dtype(a.out_dtype))
         return refuse(GDN_ERR_DTYPE, who, "io_dtype/out_dtype must be GDN_F32 or GDN_BF16");
-    if (!a.h_table || !a.stash || !a.engaged_flag)
-        return refuse(GDN_ERR_NULL, who, "null table/stash/flag");
+    if (!a.h_table || !a.stash || (need_flag && !a.engaged_flag))
+        return refuse(GDN_ERR_NULL, who, need_flag ? "null table/stash/flag" : "null table/stash");
     if (!a.q || !a.k || !a.v || !a.gate || !a.beta || !a.out)
         return refuse(GDN_ERR_NULL, who, "q, k, v, gate, beta and out are required");
     if (a.B < 1 || a.Hk < 1 || a.Hv < 1 || a.dk < 1 || a.dv < 1)
@@ -118,14 +119,14 @@ int check_verify(const gdn::VerifyArgs& a)
     return GDN_OK;
 }
 
-int check_fold(const gdn::FoldArgs& a, float* const* hi_tables)
+int check_fold(const gdn::FoldArgs& a, float* const* hi_tables, int slab_entries)
 {
     const char* who = "gdn_fold";
     if (bad_dtype(a.io_dtype)) return refuse(GDN_ERR_DTYPE, who, "io_dtype must be GDN_F32 or GDN_BF16");
     if (a.k_rows < 1 || a.k_rows > gdn::kMaxVerifyRows)
         return refuse(GDN_ERR_K_ROWS, who, "k_rows must be 1..8");
-    if (hi_tables)
-        return refuse(GDN_ERR_UNSUPPORTED, who, "the restore branch of a non-write-on-accept verify is not built; pass hi_tables = NULL");
+    if (hi_tables && slab_entries < a.k_rows)
+        return refuse(GDN_ERR_SLABS, who, "slab_entries < k_rows: the restore reads slabs 0 .. k_rows - 1");
     if (!a.h_table || !a.stash || !a.na_tab || !a.engaged_flag)
         return refuse(GDN_ERR_NULL, who, "null table/stash/na_tab/flag");
     if (a.B < 1 || a.Hk < 1 || a.Hv < 1 || a.dk < 1 || a.dv < 1)
@@ -213,7 +214,7 @@ const char* gdn_status_string(int status)
     case GDN_ERR_STASH: return "GDN_ERR_STASH: stash_seq_floats too small";
     case GDN_ERR_K_ROWS: return "GDN_ERR_K_ROWS: k_rows must be 1..8";
     case GDN_ERR_STRIDE: return "GDN_ERR_STRIDE: a row stride is shorter than its row";
-    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: branch not built";
+    case GDN_ERR_SLABS: return "GDN_ERR_SLABS: slab_entries smaller than k_rows";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: the HIP runtime refused a launch";
     default: return "unknown gdn status";
     }
@@ -362,12 +363,11 @@ int gdn_fold_plan(float* const* h_table, const float* stash, const int32_t* na_t
                   int k_rows, int B, int Hk, int Hv, int dk, int dv, int stash_seq_floats,
                   int io_dtype)
 {
-    (void)slab_entries;
     gdn::FoldArgs a = make_fold(h_table, stash, na_tab, engaged_flag, k_rows, B, Hk, Hv, dk, dv,
                                 stash_seq_floats, io_dtype);
-    int st = check_fold(a, hi_tables);
+    int st = check_fold(a, hi_tables, slab_entries);
     if (st != GDN_OK) return st;
-    route_geometry(gdn::fold_geometry(a), "");
+    route_geometry(gdn::fold_geometry(a), hi_tables ? "(+gdn_restore_kernel: word clear restores slab na)" : "");
     return GDN_OK;
 }
 
@@ -376,13 +376,74 @@ int gdn_fold(float* const* h_table, const float* stash, const int32_t* na_tab,
              int B, int Hk, int Hv, int dk, int dv, int stash_seq_floats, int io_dtype,
              hipStream_t stream)
 {
-    (void)slab_entries;
     gdn::FoldArgs a = make_fold(h_table, stash, na_tab, engaged_flag, k_rows, B, Hk, Hv, dk, dv,
                                 stash_seq_floats, io_dtype);
-    int st = check_fold(a, hi_tables);
+    int st = check_fold(a, hi_tables, slab_entries);
     if (st != GDN_OK) return st;
-    route_geometry(gdn::fold_geometry(a), "");
+    route_geometry(gdn::fold_geometry(a), hi_tables ? "(+gdn_restore_kernel: word clear restores slab na)" : "");
+    // each kernel reads the word: the restore acts when it is clear, the fold
+    // when it is set
+    if (hi_tables) {
+        st = launched(gdn::launch_restore(a, hi_tables, stream));
+        if (st != GDN_OK) return st;
+    }
     return launched(gdn::launch_fold(a, stream));
+}
+
+// Validation of a parent verify (shared by the call and its plan).
+static int check_parent(const gdn::ParentArgs& p)
+{
+    const char* who = "gdn_decode_verify_parent";
+    int st = check_verify(p.v, who, false);
+    if (st != GDN_OK) return st;
+    if (!p.hi_tables) return refuse(GDN_ERR_NULL, who, "null hi_tables");
+    if (p.slab_entries < p.v.k_rows)
+        return refuse(GDN_ERR_SLABS, who, "slab_entries < k_rows: the verify writes slabs 0 .. k_rows - 1");
+    return GDN_OK;
+}
+
+static gdn::ParentArgs make_parent(float* const* h_table, float* const* hi_tables, int slab_entries,
+                                   const void* q, const void* k, const void* v, const float* gate,
+                                   const float* beta, void* out, float* stash, int B, int Hk, int Hv,
+                                   int dk, int dv, int k_rows, int qk_stride, int v_stride,
+                                   int gb_stride, int stash_seq_floats, int io_dtype, int out_dtype)
+{
+    gdn::ParentArgs p;
+    p.v = make_verify(h_table, q, k, v, gate, beta, out, stash, B, Hk, Hv, dk, dv, k_rows, qk_stride,
+                      v_stride, gb_stride, stash_seq_floats, nullptr, io_dtype, out_dtype);
+    p.hi_tables = hi_tables;
+    p.slab_entries = slab_entries;
+    return p;
+}
+
+int gdn_decode_verify_parent_plan(float* const* h_table, float* const* hi_tables, int slab_entries,
+                                  const void* q, const void* k, const void* v, const float* gate,
+                                  const float* beta, void* out, float* stash, int B, int Hk, int Hv,
+                                  int dk, int dv, int k_rows, int qk_stride, int v_stride,
+                                  int gb_stride, int stash_seq_floats, int io_dtype, int out_dtype)
+{
+    gdn::ParentArgs p = make_parent(h_table, hi_tables, slab_entries, q, k, v, gate, beta, out, stash, B,
+                                    Hk, Hv, dk, dv, k_rows, qk_stride, v_stride, gb_stride,
+                                    stash_seq_floats, io_dtype, out_dtype);
+    int st = check_parent(p);
+    if (st != GDN_OK) return st;
+    route_geometry(gdn::parent_geometry(p), "");
+    return GDN_OK;
+}
+
+int gdn_decode_verify_parent(float* const* h_table, float* const* hi_tables, int slab_entries,
+                             const void* q, const void* k, const void* v, const float* gate,
+                             const float* beta, void* out, float* stash, int B, int Hk, int Hv, int dk,
+                             int dv, int k_rows, int qk_stride, int v_stride, int gb_stride,
+                             int stash_seq_floats, int io_dtype, int out_dtype, hipStream_t stream)
+{
+    gdn::ParentArgs p = make_parent(h_table, hi_tables, slab_entries, q, k, v, gate, beta, out, stash, B,
+                                    Hk, Hv, dk, dv, k_rows, qk_stride, v_stride, gb_stride,
+                                    stash_seq_floats, io_dtype, out_dtype);
+    int st = check_parent(p);
+    if (st != GDN_OK) return st;
+    route_geometry(gdn::parent_geometry(p), "");
+    return launched(gdn::launch_parent(p, stream));
 }
 
 // Validation of a gate/beta producer call (shared by the call and its plan).

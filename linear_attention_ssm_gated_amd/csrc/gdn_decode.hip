@@ -1,8 +1,11 @@
 // Decode: the write-on-accept verify of K draft rows (K = 1..8, the pages'
 // K = 4 among them), its post-verdict fold, the clear of the engaged word
 // (ssm_gdn_woa.rs: docs of gdn_decode_wy4_woa, gdn_wy4_fold and
-// gdn_wy4_flag_clear), and the single-token (K = 1) decode step that updates
-// the state in place.
+// gdn_wy4_flag_clear), the parent-mode verify with its per-prefix state slabs
+// and the fold's restore branch (the same page, doc of gdn_wy4_fold: when the
+// word is clear the parent kernel ran, and a partial accept restores
+// Hi(na - 1) from hi_tables), and the single-token (K = 1) decode step that
+// updates the state in place.
 //
 // Verify, per (v-head, sequence): the K draft rows are one chunk of the
 // chunked form with L = K and start state h0 = *(h_table[b]) + vh*dk*dv:
@@ -13,6 +16,12 @@
 // It writes the outputs and stashes Delta, G and the keys; it writes no state.
 // Fold: h <- exp(G_{na-1}) h0 + sum_{s<na} exp(G_{na-1} - G_s) k_s Delta_s^T,
 // the state after the first na rows, reading and writing the state once.
+// Parent verify: the verify above (outputs and stash, the word left alone),
+// then one pass over each state that writes slab j = the state after the
+// first j rows (j = 0 .. K-1; slab 0 is the state before the verify) and
+// advances the state itself through all K rows:
+//   x_r = exp(G_r - G_{r-1}) x_{r-1} + k_r Delta_r^T,  x_{-1} = h0,  G_{-1} = 0.
+// Restore (fold, word clear): na < K puts back slab na, a bitwise copy.
 // Step (K = 1): the verify and the fold of its one row in one pass,
 //   delta = beta (v - alpha h^T k),  o = alpha h^T q + (q.k) delta,
 //   h <- alpha h + k delta^T,        alpha = exp(gate).
@@ -154,7 +163,7 @@ gdn_verify_kernel(float* const* __restrict__ h_table, const TIn* __restrict__ q,
     } else {
         for (int e = tid; e < KR * dk; e += kThreads) sk_out[e] = sk[e / dk][e % dk];
     }
-    if (vh == 0 && b == 0 && tid == 0) engaged_flag[0] = 1u;
+    if (engaged_flag && vh == 0 && b == 0 && tid == 0) engaged_flag[0] = 1u;
 }
 
 template <bool kBf16Keys, int KR>
@@ -563,7 +572,7 @@ gdn_verify_d128_kernel(float* const* __restrict__ h_table, const TIn* q, const T
                                                       live ? kbase + 4u * e : 0x7fffffffu, 0u, 0);
         }
     }
-    if (vh == 0 && b == 0 && tid == 0) engaged_flag[0] = 1u;
+    if (engaged_flag && vh == 0 && b == 0 && tid == 0) engaged_flag[0] = 1u;
 }
 
 // dk = dv = 128 fold: laid out like the verify (thread t updates rows
@@ -817,6 +826,77 @@ __global__ void __launch_bounds__(64) gdn_flag_clear_kernel(uint32_t* flag)
     if (threadIdx.x == 0) flag[0] = 0u;
 }
 
+// ---------------------------------------------------------------------------
+// The parent verify's slabs, from the stash its verify just wrote (row deltas,
+// cumulative log decays G, keys): slab j of sequence b, v-head vh, at
+// hi_tables[b] + (j Hv + vh) dk dv floats, laid out as the state.  Thread t
+// takes float4 column group t % (dv / 4) of rows t / (dv / 4) + m (256 / (dv / 4));
+// every state element is read once and written K + 1 times.  Any dk, dv <= 128
+// with dv a multiple of 4.
+template <bool kBf16Keys, int KR>
+__global__ void __launch_bounds__(kThreads)
+gdn_slab_kernel(float* const* __restrict__ h_table, float* const* __restrict__ hi_tables,
+                const float* __restrict__ stash, int Hv, int dk, int dv, int stash_seq_floats)
+{
+    __shared__ float sk[KR][kMaxD];
+    __shared__ float sd[KR][kMaxD];
+    __shared__ float sa[KR];
+    const int vh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const float* st = stash + (size_t)b * stash_seq_floats + (size_t)vh * stash_head_floats(dk, dv, kBf16Keys, KR);
+    for (int e = tid; e < KR * dv; e += kThreads) sd[e / dv][e % dv] = st[e];
+    const float* sk_in = st + KR * dv + KR;
+    for (int e = tid; e < KR * dk; e += kThreads) {
+        float x;
+        if (kBf16Keys) x = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sk_in)[e]);
+        else x = sk_in[e];
+        sk[e / dk][e % dk] = x;
+    }
+    // the decay of row r: exp(G_r - G_{r-1}) = exp(gate_r) <= 1
+    if (tid < KR) sa[tid] = __expf(st[KR * dv + tid] - (tid > 0 ? st[KR * dv + tid - 1] : 0.f));
+    __syncthreads();
+
+    float* h = h_table[b] + (size_t)vh * dk * dv;
+    float* slab = hi_tables[b] + (size_t)vh * dk * dv;
+    const size_t sstride = (size_t)Hv * dk * dv;
+    const int ncg = dv / 4;
+    for (int e = tid; e < dk * ncg; e += kThreads) {
+        const int i = e / ncg, c4 = (e % ncg) * 4;
+        const size_t off = (size_t)i * dv + c4;
+        float4 x = load_global4(h + off);
+        store_global4(slab + off, x);
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            const float a = sa[r], kr = sk[r][i];
+            x.x = fmaf(a, x.x, kr * sd[r][c4]);
+            x.y = fmaf(a, x.y, kr * sd[r][c4 + 1]);
+            x.z = fmaf(a, x.z, kr * sd[r][c4 + 2]);
+            x.w = fmaf(a, x.w, kr * sd[r][c4 + 3]);
+            if (r + 1 < KR) store_global4(slab + (size_t)(r + 1) * sstride + off, x);
+        }
+        store_global4(h + off, x);
+    }
+}
+
+// The fold's restore branch.  With the word clear (the parent verify ran, not
+// the write-on-accept one), a partial accept na < K puts back slab na, the
+// state after the first na rows, as a bitwise copy; na = K keeps the state,
+// which the parent verify advanced through all K rows.  With the word set it
+// does nothing (the write-on-accept fold applies the stashed rows).
+__global__ void __launch_bounds__(kThreads)
+gdn_restore_kernel(float* const* __restrict__ h_table, float* const* __restrict__ hi_tables,
+                   const int32_t* __restrict__ na_tab, const uint32_t* __restrict__ engaged_flag,
+                   int k_rows, int Hv, int dk, int dv)
+{
+    const int vh = blockIdx.x, b = blockIdx.y;
+    if (engaged_flag[0] != 0u) return;
+    const int na = min(max(na_tab[b], 0), k_rows);
+    if (na == k_rows) return;
+    const float* src = hi_tables[b] + ((size_t)na * Hv + vh) * dk * dv;
+    float* dst = h_table[b] + (size_t)vh * dk * dv;
+    for (int e = threadIdx.x; e < dk * dv / 4; e += kThreads)
+        store_global4(dst + 4 * (size_t)e, load_global4(src + 4 * (size_t)e));
+}
+
 // ---- launchers -------------------------------------------------------------
 
 template <typename TIn, typename TOut, int KR>
@@ -893,6 +973,30 @@ hipError_t launch_step_typed(const StepArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
+template <bool kBf16Keys, int KR>
+hipError_t launch_slab_rows(const ParentArgs& a, hipStream_t s)
+{
+    hipLaunchKernelGGL((gdn_slab_kernel<kBf16Keys, KR>), dim3(a.v.Hv, a.v.B), dim3(kThreads), 0, s,
+                       a.v.h_table, a.hi_tables, a.v.stash, a.v.Hv, a.v.dk, a.v.dv, a.v.stash_seq_floats);
+    return hipGetLastError();
+}
+
+template <bool kBf16Keys>
+hipError_t launch_slab_typed(const ParentArgs& a, hipStream_t s)
+{
+    switch (a.v.k_rows) {
+    case 1: return launch_slab_rows<kBf16Keys, 1>(a, s);
+    case 2: return launch_slab_rows<kBf16Keys, 2>(a, s);
+    case 3: return launch_slab_rows<kBf16Keys, 3>(a, s);
+    case 4: return launch_slab_rows<kBf16Keys, 4>(a, s);
+    case 5: return launch_slab_rows<kBf16Keys, 5>(a, s);
+    case 6: return launch_slab_rows<kBf16Keys, 6>(a, s);
+    case 7: return launch_slab_rows<kBf16Keys, 7>(a, s);
+    case 8: return launch_slab_rows<kBf16Keys, 8>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 // Static LDS of the kernels above, for the route line.
 unsigned verify_lds(int kr, bool d128)
 {
@@ -964,6 +1068,33 @@ hipError_t launch_step(const StepArgs& a, hipStream_t s)
     if (a.io_dtype == 0 && a.out_dtype == 1) return launch_step_typed<float, uint16_t>(a, s);
     if (a.io_dtype == 1 && a.out_dtype == 0) return launch_step_typed<uint16_t, float>(a, s);
     return launch_step_typed<uint16_t, uint16_t>(a, s);
+}
+
+Geometry parent_geometry(const ParentArgs& a)
+{
+    Geometry g = verify_geometry(a.v);
+    g.entry = a.v.dk == kD && a.v.dv == kD ? "gdn_verify_d128_kernel+gdn_slab_kernel" : "gdn_verify_kernel+gdn_slab_kernel";
+    return g;
+}
+
+Geometry restore_geometry(const FoldArgs& a)
+{
+    Geometry g{"gdn_restore_kernel", {(unsigned)a.Hv, (unsigned)a.B, 1u}, kThreads, 0u};
+    return g;
+}
+
+hipError_t launch_parent(const ParentArgs& a, hipStream_t s)
+{
+    hipError_t e = launch_verify(a.v, s);   // a.v.engaged_flag is NULL: the word is left alone
+    if (e != hipSuccess) return e;
+    return a.v.io_dtype == 1 ? launch_slab_typed<true>(a, s) : launch_slab_typed<false>(a, s);
+}
+
+hipError_t launch_restore(const FoldArgs& a, float* const* hi_tables, hipStream_t s)
+{
+    hipLaunchKernelGGL(gdn_restore_kernel, dim3(a.Hv, a.B), dim3(kThreads), 0, s, a.h_table, hi_tables,
+                       a.na_tab, a.engaged_flag, a.k_rows, a.Hv, a.dk, a.dv);
+    return hipGetLastError();
 }
 
 hipError_t launch_flag_clear(uint32_t* flag, hipStream_t s)

@@ -51,6 +51,14 @@ struct FoldArgs {
     int k_rows;
 };
 
+// The parent-mode verify: the verify's arguments (engaged_flag NULL: the
+// word is left alone) and the per-sequence slab tables.
+struct ParentArgs {
+    VerifyArgs v;
+    float* const* hi_tables;
+    int slab_entries;
+};
+
 struct StepArgs {
     float* const* h_table;
     const void* q;
@@ -95,6 +103,8 @@ Geometry verify_geometry(const VerifyArgs& a);
 Geometry fold_geometry(const FoldArgs& a);
 Geometry step_geometry(const StepArgs& a);
 Geometry flag_clear_geometry();
+Geometry parent_geometry(const ParentArgs& a);
+Geometry restore_geometry(const FoldArgs& a);
 size_t ba_gates_workspace_bytes(int m, int n, int k);
 Geometry ba_gates_geometry(const BaArgs& a);
 
@@ -104,6 +114,8 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, hipStream_t s);
 hipError_t launch_flag_clear(uint32_t* flag, hipStream_t s);
+hipError_t launch_parent(const ParentArgs& a, hipStream_t s);
+hipError_t launch_restore(const FoldArgs& a, float* const* hi_tables, hipStream_t s);
 hipError_t launch_ba_gates(const BaArgs& a, hipStream_t s);
 
 // Per-v-head stash floats of a k_rows-row verify: delta [k_rows][dv] fp32,

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in gdn.h but not exported"
     assert set(names) == set(gdn.SIGNATURES), "binding and header disagree"
@@ -189,14 +189,46 @@ def test_fold_plan(lib):
         assert fold_plan(lib, k_rows=k_rows, ssf=ssf) == 0
     assert fold_plan(lib, dk=64, dv=64, ssf=48 * (256 + 4 + 128)) == 0
     assert gdn.last_route().startswith("gdn_fold_kernel grid=[48,16,1]")
+    # the restore branch: slabs 0 .. k_rows - 1 must exist
+    assert fold_plan(lib, hi=X, slab=4) == 0
+    assert "gdn_restore_kernel" in gdn.last_route()
+    assert fold_plan(lib, hi=X, slab=9) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(k_rows=0), 8), (dict(k_rows=9), 8), (dict(k_rows=5), 7), (dict(hi=X), 10), (dict(na=None), 1), (dict(ht=None), 1),
+    (dict(k_rows=0), 8), (dict(k_rows=9), 8), (dict(k_rows=5), 7), (dict(hi=X), 10), (dict(hi=X, slab=3), 10),
+    (dict(na=None), 1), (dict(ht=None), 1),
     (dict(ssf=10), 7), (dict(Hv=47), 3), (dict(io=9), 5),
 ])
 def test_fold_refusals(lib, kw, status):
     assert fold_plan(lib, **kw) == status
+    assert "refused" in gdn.last_route()
+
+
+def parent_plan(lib, **kw):
+    a = dict(ht=X, hi=X, slab=4, q=X, k=X, v=X, gate=X, beta=X, out=X, stash=X, B=16, Hk=16, Hv=48,
+             dk=128, dv=128, k_rows=4, qks=16 * 128, vs=48 * 128, gbs=48, ssf=48 * (512 + 4 + 256),
+             io=1, od=1)
+    a.update(kw)
+    return lib.gdn_decode_verify_parent_plan(a["ht"], a["hi"], a["slab"], a["q"], a["k"], a["v"],
+                                             a["gate"], a["beta"], a["out"], a["stash"], a["B"], a["Hk"],
+                                             a["Hv"], a["dk"], a["dv"], a["k_rows"], a["qks"], a["vs"],
+                                             a["gbs"], a["ssf"], a["io"], a["od"])
+
+
+def test_parent_verify_plan(lib):
+    assert parent_plan(lib) == 0
+    assert gdn.last_route().startswith("gdn_verify_d128_kernel+gdn_slab_kernel grid=[48,16,1] block=256")
+    assert parent_plan(lib, dk=64, dv=64, qks=16 * 64, vs=48 * 64, ssf=48 * (256 + 4 + 128)) == 0
+    assert gdn.last_route().startswith("gdn_verify_kernel+gdn_slab_kernel grid=[48,16,1]")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hi=None), 1), (dict(ht=None), 1), (dict(stash=None), 1), (dict(slab=3), 10), (dict(slab=0), 10),
+    (dict(k_rows=9), 8), (dict(ssf=10), 7), (dict(Hv=47), 3), (dict(io=9), 5), (dict(qks=100), 9),
+])
+def test_parent_verify_refusals(lib, kw, status):
+    assert parent_plan(lib, **kw) == status
     assert "refused" in gdn.last_route()
 
 
