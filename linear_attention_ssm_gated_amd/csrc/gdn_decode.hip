@@ -298,6 +298,11 @@ gdn_step_kernel(float* const* __restrict__ h_table, const TIn* __restrict__ q,
 // through LDS.  The state is read with nontemporal loads (it is read once).
 constexpr int kLookahead = 4;       // state rows in flight per thread: verify, fold
 constexpr int kLookaheadStep = 8;   // and in the K = 1 step (measured best for each)
+// The fold's workgroups per state (each takes 128 / kFoldSplit of its rows):
+// the accepted sequences are an uneven share of the grid, and finer
+// workgroups spread them evenly over the compute units (measured: 4 beats 1
+// and 2 on the B = 16, Hv = 48 fold).
+constexpr int kFoldSplit = 4;
 constexpr int kD = 128;
 constexpr int kKP = kD + 16;    // key rows padded: rows read together fall in different banks
 constexpr int kSP = 20;         // keys of slice s at [s][m] = row s + 8 m, padded
@@ -580,7 +585,7 @@ gdn_verify_d128_kernel(float* const* __restrict__ h_table, const TIn* q, const T
 // go out first, then the state rows, pipelined kLookahead rows ahead of the
 // update; each row is written back as soon as it is updated.  The state is
 // read and written with nontemporal accesses.
-template <bool kBf16Keys, int KR>
+template <bool kBf16Keys, int KR, int S>
 __global__ void __launch_bounds__(kThreads)
 gdn_fold_d128_kernel(float* const* __restrict__ h_table, const float* stash,
                      const int32_t* __restrict__ na_tab, const uint32_t* __restrict__ engaged_flag,
@@ -591,6 +596,9 @@ gdn_fold_d128_kernel(float* const* __restrict__ h_table, const float* stash,
     __shared__ __attribute__((aligned(16))) float sk2[KR][kSlices * SP];
 
     const int vh = blockIdx.x, b = blockIdx.y;
+    constexpr int NM = 16 / S;                   // state rows per thread: this workgroup's share
+    constexpr int LA = kLookahead < NM ? kLookahead : NM;
+    const int m0 = (int)blockIdx.z * NM;
     // the word, the accept count and the state pointer are independent loads:
     // issue all three before the first branch, so that their latencies overlap
     const uint32_t engaged = engaged_flag[0];
@@ -626,9 +634,9 @@ gdn_fold_d128_kernel(float* const* __restrict__ h_table, const float* stash,
     }
     mem_fence_here();
 
-    float4 hv[16];
+    float4 hv[NM];
 #pragma unroll
-    for (int m = 0; m < kLookahead; ++m) hv[m] = state_row(rs, sl + 8 * m, cg);
+    for (int m = 0; m < LA; ++m) hv[m] = state_row(rs, sl + 8 * (m0 + m), cg);
     mem_fence_here();
 
 #pragma unroll
@@ -647,17 +655,17 @@ gdn_fold_d128_kernel(float* const* __restrict__ h_table, const float* stash,
     __syncthreads();
 
 #pragma unroll
-    for (int m4 = 0; m4 < 4; ++m4) {
+    for (int m4 = 0; m4 < NM / 4; ++m4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int m = 4 * m4 + e + kLookahead;
-            if (m < 16) hv[m] = state_row(rs, sl + 8 * m, cg);
+            const int m = 4 * m4 + e + LA;
+            if (m < NM) hv[m] = state_row(rs, sl + 8 * (m0 + m), cg);
         }
         mem_fence_here();
         float kk[KR][4];
 #pragma unroll
         for (int r = 0; r < KR; ++r) {
-            const float4 a4 = f4_of(&sk2[r][sl * SP + 4 * m4]);
+            const float4 a4 = f4_of(&sk2[r][sl * SP + m0 + 4 * m4]);
             kk[r][0] = a4.x; kk[r][1] = a4.y; kk[r][2] = a4.z; kk[r][3] = a4.w;
         }
 #pragma unroll
@@ -672,7 +680,7 @@ gdn_fold_d128_kernel(float* const* __restrict__ h_table, const float* stash,
                     x.x += ks * dl[s2][0]; x.y += ks * dl[s2][1]; x.z += ks * dl[s2][2]; x.w += ks * dl[s2][3];
                 }
             }
-            state_store(rs, sl + 8 * m, cg, x);
+            state_store(rs, sl + 8 * (m0 + m), cg, x);
         }
         mem_fence_here();
     }
@@ -935,7 +943,7 @@ template <bool kBf16Keys, int KR>
 hipError_t launch_fold_rows(const FoldArgs& a, hipStream_t s)
 {
     if (a.dk == kD && a.dv == kD)
-        hipLaunchKernelGGL((gdn_fold_d128_kernel<kBf16Keys, KR>), dim3(a.Hv, a.B), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((gdn_fold_d128_kernel<kBf16Keys, KR, kFoldSplit>), dim3(a.Hv, a.B, kFoldSplit), dim3(kThreads), 0, s,
                            a.h_table, a.stash, a.na_tab, a.engaged_flag, a.stash_seq_floats);
     else
         hipLaunchKernelGGL((gdn_fold_kernel<kBf16Keys, KR>), dim3(a.Hv, a.B), dim3(kThreads), 0, s,
@@ -1021,7 +1029,7 @@ Geometry verify_geometry(const VerifyArgs& a)
 Geometry fold_geometry(const FoldArgs& a)
 {
     if (a.dk == kD && a.dv == kD) {
-        Geometry g{"gdn_fold_d128_kernel", {(unsigned)a.Hv, (unsigned)a.B, 1u}, kThreads,
+        Geometry g{"gdn_fold_d128_kernel", {(unsigned)a.Hv, (unsigned)a.B, (unsigned)kFoldSplit}, kThreads,
                    (unsigned)(sizeof(float) * a.k_rows * kSlices * kSP)};
         return g;
     }

@@ -24,8 +24,10 @@ def test_tiny_f32_workload():
     out, hf, route = gpu_prefill(inp, w.chunk)
     assert route.startswith("gdn_prefill_generic_kernel grid=[1,1,1]"), route
     ro, rh = oracle_prefill(inp)
-    assert rel_err(out, ro) <= TOL
-    assert rel_err(hf, rh) <= TOL
+    eo, eh = rel_err(out, ro), rel_err(hf, rh)
+    say(f"  out err {eo:.3e}  state err {eh:.3e}")
+    assert eo <= TOL
+    assert eh <= TOL
 
 
 CASES = [

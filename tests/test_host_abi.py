@@ -183,7 +183,7 @@ def fold_plan(lib, **kw):
 
 def test_fold_plan(lib):
     assert fold_plan(lib) == 0
-    assert gdn.last_route().startswith("gdn_fold_d128_kernel grid=[48,16,1] block=256")
+    assert gdn.last_route().startswith("gdn_fold_d128_kernel grid=[48,16,4] block=256")
     for k_rows in (1, 3, 8):
         ssf = gdn.gdn_stash_seq_floats(48, 128, 128, k_rows, 1)
         assert fold_plan(lib, k_rows=k_rows, ssf=ssf) == 0
