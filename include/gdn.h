@@ -115,7 +115,10 @@ const char* gdn_last_route(void);
  * 64 x 64 bf16 in MFMA fragment order (6 KiB; the granules above their
  * diagonals are never written or read) followed by the chunk's per-row decay
  * factors exp(G_r) (and exp(G_L) after T_e), 7 KiB per matrix; the generic
- * route needs none.
+ * route needs none.  The size returned covers gdn_chunk_prefill_segmented
+ * too: where its segment scan is taken, 3 fp32 128 x 128 matrices per
+ * (segment, v-head) follow the slots (gdn_chunk_prefill itself asks only the
+ * slots, and gdn_chunk_prefill_noalloc uses only those).
  * The library reads and writes the workspace only inside the call's stream
  * order; its contents need no initialisation.
  */
@@ -162,6 +165,37 @@ int gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v,
                               int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                               const int32_t* cu_seqlens, int io_dtype, int out_dtype,
                               hipStream_t stream);
+
+/* Segment-scan prefill (ssm_gdn_tc_route.rs, doc of the spine entries: the
+ * spine walks the chunk states S_c in order, and the map from one chunk's
+ * start state to the next is affine in the state).  Same arguments, layouts,
+ * workspace (gdn_prefill_workspace_bytes covers both routes) and results as
+ * gdn_chunk_prefill, to rounding: on the MFMA route, for dense input
+ * (cu_seqlens == NULL) whose spine workgroups (B * Hv * 4) would fill at most
+ * a third of the 256 compute units, each sequence is cut into S segments of
+ * whole chunks (3 <= S <= 10, the most whose 2 S - 3 map walks per sequence
+ * fit in 256 workgroups).  One spine launch walks segment 0 from h0 (its end
+ * state N_0) and segments 1 .. S-2 both from zero (N_s) and from the identity
+ * with V read as zero (the linear part M_s); a combine kernel applies the
+ * maps in order per sequence (start(1) = N_0, start(s) = M_{s-1} start(s-1) +
+ * N_{s-1}, in products of bf16 splits of the fp32 operands, about 16 bits
+ * each); a second spine launch walks every segment from its start state,
+ * writing the outputs, the last segment writing h_final.  Elsewhere it runs
+ * the route gdn_chunk_prefill would, and the route line says why.
+ * Deterministic run to run; not bitwise equal to gdn_chunk_prefill. */
+int gdn_chunk_prefill_segmented(const void* q, const void* k, const void* v,
+                                const float* log_g, const float* beta, const float* h0,
+                                void* out, float* h_final, int B, int T, int Hk, int Hv,
+                                int dk, int dv, int chunk, const int32_t* cu_seqlens,
+                                int io_dtype, int out_dtype, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+int gdn_chunk_prefill_segmented_plan(const void* q, const void* k, const void* v,
+                                     const float* log_g, const float* beta, const float* h0,
+                                     void* out, float* h_final, int B, int T, int Hk, int Hv,
+                                     int dk, int dv, int chunk, const int32_t* cu_seqlens,
+                                     int io_dtype, int out_dtype, void* workspace,
+                                     size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------ */
 /* Write-on-accept decode verify of K draft rows (the pages' K = 4, and any K

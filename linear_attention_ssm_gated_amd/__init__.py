@@ -35,6 +35,8 @@ SIGNATURES = {
     "gdn_prefill_workspace_bytes": (Z, [I, I, I, I, I, I, I, I, I]),
     "gdn_chunk_prefill": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, I, I, P, Z, P]),
     "gdn_chunk_prefill_plan": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, I, I, P, Z]),
+    "gdn_chunk_prefill_segmented": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, I, I, P, Z, P]),
+    "gdn_chunk_prefill_segmented_plan": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, I, I, P, Z]),
     "gdn_chunk_prefill_noalloc": (I, [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, I, I, P]),
     "gdn_stash_seq_floats": (Z, [I, I, I, I, I]),
     "gdn_flag_clear": (I, [P, P]),
@@ -128,6 +130,17 @@ def gdn_chunk_prefill(q, k, v, log_g, beta, h0, out, h_final, B, T, Hk, Hv, dk, 
     """Enqueue one chunked prefill (layouts in include/gdn.h).  Returns the route line."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().gdn_chunk_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta), _ptr(h0), _ptr(out), _ptr(h_final),
+        B, T, Hk, Hv, dk, dv, chunk, _ptr(cu_seqlens), _dtype_code(q), _dtype_code(out),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return last_route()
+
+
+def gdn_chunk_prefill_segmented(q, k, v, log_g, beta, h0, out, h_final, B, T, Hk, Hv, dk, dv, chunk,
+                                cu_seqlens=None, workspace=None, stream=None):
+    """Enqueue one segment-scan prefill (include/gdn.h).  Returns the route line."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().gdn_chunk_prefill_segmented(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta), _ptr(h0), _ptr(out), _ptr(h_final),
         B, T, Hk, Hv, dk, dv, chunk, _ptr(cu_seqlens), _dtype_code(q), _dtype_code(out),
         _ptr(workspace), ws_bytes, _stream(stream)))
@@ -235,8 +248,9 @@ def ba_gates(x, w, a_log, dt_bias, nv, vheads_per_group, gate_stride=None, strea
 
 
 def chunk_prefill(q, k, v, log_g, beta, h0=None, cu_seqlens=None, chunk=64, out_dtype=None,
-                  want_state=True, stream=None):
-    """Allocate out/h_final with torch and run gdn_chunk_prefill.
+                  want_state=True, stream=None, segmented=False):
+    """Allocate out/h_final with torch and run gdn_chunk_prefill (or, with
+    segmented=True, gdn_chunk_prefill_segmented).
 
     Dense q, k [B, T, Hk, dk], v [B, T, Hv, dv], log_g/beta [B, T, Hv]; or
     packed q, k [N, Hk, dk] ... with cu_seqlens [B+1] (int32, on the GPU).
@@ -253,6 +267,7 @@ def chunk_prefill(q, k, v, log_g, beta, h0=None, cu_seqlens=None, chunk=64, out_
     ws_n = gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, _dtype_code(q),
                                        packed=cu_seqlens is not None)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=v.device) if ws_n else None
-    route = gdn_chunk_prefill(q, k, v, log_g, beta, h0, out, hf, B, T, Hk, Hv, dk, dv, chunk,
-                              cu_seqlens=cu_seqlens, workspace=ws, stream=stream)
+    call = gdn_chunk_prefill_segmented if segmented else gdn_chunk_prefill
+    route = call(q, k, v, log_g, beta, h0, out, hf, B, T, Hk, Hv, dk, dv, chunk,
+                 cu_seqlens=cu_seqlens, workspace=ws, stream=stream)
     return out, hf, route

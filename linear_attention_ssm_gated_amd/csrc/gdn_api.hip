@@ -80,8 +80,8 @@ int check_prefill(const gdn::PrefillArgs& a, bool* mfma, const char** why)
         return refuse(GDN_ERR_DIM_LIMIT, who, "dk, dv <= 128 and chunk <= 64");
     if (a.T > 0 && (!a.q || !a.k || !a.v || !a.log_g || !a.beta || !a.out))
         return refuse(GDN_ERR_NULL, who, "q, k, v, log_g, beta and out are required when T > 0");
-    const size_t need = gdn_prefill_workspace_bytes(a.B, a.T, a.Hk, a.Hv, a.dk, a.dv, a.chunk,
-                                                    a.io_dtype, a.cu_seqlens != nullptr);
+    const size_t need = gdn::prefill_workspace_need(a.B, a.T, a.Hk, a.Hv, a.dk, a.dv, a.chunk, a.io_dtype,
+                                                    a.cu_seqlens != nullptr, a.segmented);
     if (need > 0 && (!a.workspace || a.workspace_bytes < need))
         return refuse(GDN_ERR_WORKSPACE, who, "workspace smaller than gdn_prefill_workspace_bytes()");
     *why = "";
@@ -179,6 +179,7 @@ gdn::PrefillArgs make_prefill(const void* q, const void* k, const void* v, const
     a.h_final = h_final; a.B = B; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv;
     a.chunk = chunk; a.cu_seqlens = cu_seqlens; a.io_dtype = io_dtype; a.out_dtype = out_dtype;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.segmented = false;
     return a;
 }
 
@@ -225,11 +226,8 @@ const char* gdn_last_route(void) { return t_route; }
 size_t gdn_prefill_workspace_bytes(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                    int io_dtype, int packed)
 {
-    if (B < 1 || T < 0 || Hk < 1 || Hv < 1) return 0;
-    gdn::PrefillArgs a{};
-    a.io_dtype = io_dtype; a.dk = dk; a.dv = dv; a.chunk = chunk;
-    if (!gdn::prefill_mfma_accepts(a)) return 0;  // the generic kernel keeps everything in LDS
-    return gdn::prefill_mfma_workspace_bytes(B, T, Hk, Hv, packed != 0);
+    // enough for either entry point
+    return gdn::prefill_workspace_need(B, T, Hk, Hv, dk, dv, chunk, io_dtype, packed != 0, true);
 }
 
 int gdn_chunk_prefill_plan(const void* q, const void* k, const void* v, const float* log_g,
@@ -264,6 +262,51 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* 
     if (st != GDN_OK) return st;
     route_geometry(mfma ? gdn::prefill_mfma_geometry(a) : gdn::prefill_generic_geometry(a), why);
     return launched(mfma ? gdn::launch_prefill_mfma(a, stream) : gdn::launch_prefill_generic(a, stream));
+}
+
+// The segment-scan twin: the same validation and routes, and on the MFMA
+// route the segment scan where segment_cut takes it (dense input, few spine
+// workgroups); the route line names the route that runs.
+static int prefill_segmented(bool launch, const void* q, const void* k, const void* v, const float* log_g,
+                             const float* beta, const float* h0, void* out, float* h_final, int B, int T,
+                             int Hk, int Hv, int dk, int dv, int chunk, const int32_t* cu_seqlens,
+                             int io_dtype, int out_dtype, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream)
+{
+    gdn::PrefillArgs a = make_prefill(q, k, v, log_g, beta, h0, out, h_final, B, T, Hk, Hv, dk, dv,
+                                      chunk, cu_seqlens, io_dtype, out_dtype, workspace,
+                                      workspace_bytes);
+    a.segmented = true;
+    bool mfma = false;
+    const char* why = "";
+    int st = check_prefill(a, &mfma, &why);
+    if (st != GDN_OK) return st;
+    if (mfma && gdn::prefill_mfma_segments(a) == 0)
+        why = cu_seqlens ? "(plain spine: the segment scan takes dense input)"
+                         : "(plain spine: the spine's workgroups fill the chip, or too few chunks)";
+    route_geometry(mfma ? gdn::prefill_mfma_geometry(a) : gdn::prefill_generic_geometry(a), why);
+    if (!launch) return GDN_OK;
+    return launched(mfma ? gdn::launch_prefill_mfma(a, stream) : gdn::launch_prefill_generic(a, stream));
+}
+
+int gdn_chunk_prefill_segmented(const void* q, const void* k, const void* v, const float* log_g,
+                                const float* beta, const float* h0, void* out, float* h_final, int B,
+                                int T, int Hk, int Hv, int dk, int dv, int chunk,
+                                const int32_t* cu_seqlens, int io_dtype, int out_dtype, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream)
+{
+    return prefill_segmented(true, q, k, v, log_g, beta, h0, out, h_final, B, T, Hk, Hv, dk, dv, chunk,
+                             cu_seqlens, io_dtype, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int gdn_chunk_prefill_segmented_plan(const void* q, const void* k, const void* v, const float* log_g,
+                                     const float* beta, const float* h0, void* out, float* h_final,
+                                     int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                                     const int32_t* cu_seqlens, int io_dtype, int out_dtype,
+                                     void* workspace, size_t workspace_bytes)
+{
+    return prefill_segmented(false, q, k, v, log_g, beta, h0, out, h_final, B, T, Hk, Hv, dk, dv, chunk,
+                             cu_seqlens, io_dtype, out_dtype, workspace, workspace_bytes, nullptr);
 }
 
 size_t gdn_stash_seq_floats(int Hv, int dk, int dv, int k_rows, int io_dtype)

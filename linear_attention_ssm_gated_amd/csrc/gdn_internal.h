@@ -23,6 +23,7 @@ struct PrefillArgs {
     int io_dtype, out_dtype;
     void* workspace;
     size_t workspace_bytes;
+    bool segmented;   // the segment-scan route where it applies (gdn_chunk_prefill_segmented)
 };
 
 struct VerifyArgs {
@@ -96,9 +97,14 @@ struct Geometry {
 
 // Kernel choice and geometry of a prefill call (no launch).
 bool prefill_mfma_accepts(const PrefillArgs& a);
-size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv, bool packed);
+size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv, bool packed, bool segmented);
+// Workspace bytes one prefill call needs: the plain route's, or with
+// segmented the segment scan's where it is taken (which covers the plain one).
+size_t prefill_workspace_need(int B, int T, int Hk, int Hv, int dk, int dv, int chunk, int io_dtype,
+                              bool packed, bool segmented);
 Geometry prefill_generic_geometry(const PrefillArgs& a);
 Geometry prefill_mfma_geometry(const PrefillArgs& a);
+int prefill_mfma_segments(const PrefillArgs& a);   // segments per sequence of the segment scan, 0 = plain spine
 Geometry verify_geometry(const VerifyArgs& a);
 Geometry fold_geometry(const FoldArgs& a);
 Geometry step_geometry(const StepArgs& a);

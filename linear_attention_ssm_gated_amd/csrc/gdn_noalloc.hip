@@ -54,8 +54,8 @@ extern "C" int gdn_chunk_prefill_noalloc(const void* q, const void* k, const voi
 {
     // Shapes first (the plan touches no device), then the size limit, then the
     // device lookup: a refusal never reaches the runtime.
-    const size_t need = gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, chunk, io_dtype,
-                                                    cu_seqlens != nullptr);
+    const size_t need = gdn::prefill_workspace_need(B, T, Hk, Hv, dk, dv, chunk, io_dtype,
+                                                    cu_seqlens != nullptr, false);
     void* const probe = need ? reinterpret_cast<void*>(static_cast<uintptr_t>(256)) : nullptr;
     int st = gdn_chunk_prefill_plan(q, k, v, log_g, beta, h0, out, h_final, B, T, Hk, Hv, dk, dv,
                                     chunk, cu_seqlens, io_dtype, out_dtype, probe, need);

@@ -761,6 +761,24 @@ __device__ __forceinline__ ChunkRows chunk_rows(long row0, long len, int cc) {
     return cr;
 }
 
+// Per-workgroup walk options (the segment scan's walks): V rows read as
+// zero; no outputs written; the initial state is the identity; the final
+// state is written as two bf16 planes (hi = bf16(x), then lo = bf16(x - hi)).
+constexpr int SPINE_V_ZERO = 1, SPINE_NO_OUT = 2, SPINE_H0_EYE = 4, SPINE_SPLIT_OUT = 8;
+
+// The segment scan's cut and buffers, passed to the spine and the combine.
+// Each dense sequence b is cut into S segments of L chunks (the last one
+// shorter); segment j covers tokens [j L C, min((j + 1) L C, T)).  maps
+// holds, per (b S + j, v-head), the matrix N_j (fp32) and from map_m on the
+// matrix M_j (bf16 planes); starts holds the start state of segment j >= 2.
+struct SegWalk {
+    int S, L;
+    int phase;             // 0: not a segment walk; 1: the map walks; 2: the output walks
+    float* maps;
+    long map_m;            // floats from maps to the M matrices: B S Hv D D
+    const float* starts;
+};
+
 struct SpineArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -770,6 +788,7 @@ struct SpineArgs {
     long row0, len;
     long slot0;
     int nc, Hk, Hv, kh, vh, tile;
+    int flags;
 };
 
 // Chunk cc's ring stage: K, T_e, the recurrence factors and V; rows past the
@@ -786,7 +805,8 @@ __device__ __forceinline__ void issue_rec(unsigned char* ring, const LoadOffsets
     dma_x6(rt, base + RS_TE, o.fv, o.fs);
     dma16(rt, S + RS_SC, o.scv, 0);
     const uint32_t v_row = (uint32_t)a.Hv * D * 2u;
-    const Rsrc rv = make_dma_rsrc(a.v + (cr.r0 * a.Hv + a.vh) * D + a.tile * TILE_COLS, cr.L * v_row);
+    const Rsrc rv = make_dma_rsrc(a.v + (cr.r0 * a.Hv + a.vh) * D + a.tile * TILE_COLS,
+                                  (a.flags & SPINE_V_ZERO) ? 0u : cr.L * v_row);
     dma_x4(rv, base + RS_V, o.v, o.v, o.v, o.v, o.vs[0], o.vs[1], o.vs[2], o.vs[3]);
 }
 
@@ -1111,7 +1131,7 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const unsigned char* __restrict__ tes, const unsigned char* __restrict__ pts,
                  int T, int Hk, int Hv, const int32_t* __restrict__ cu,
                  const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ order,
-                 int nc_dense, long n_slots)
+                 int nc_dense, long n_slots, SegWalk sw)
 {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[SPINE_LDS];
     unsigned char* ring = lds;
@@ -1127,16 +1147,52 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     SpineArgs a;
     a.vh = lin / N_TILES;
     a.tile = lin % N_TILES;
-    const int b = order ? order[blockIdx.y] : (int)blockIdx.y;
     a.kh = a.vh / (Hv / Hk);
     a.q = q; a.k = k; a.v = v; a.tes = tes; a.pts = pts; a.Hk = Hk; a.Hv = Hv;
-    seq_rows(cu, b, T, &a.row0, &a.len);
-    a.slot0 = cu ? (long)chunk_base[b] : (long)b * nc_dense;
+    const size_t DD = (size_t)D * D;
+    // the start state read, the final state written (per v-head matrices)
+    const float* hin;
+    float* hout;
+    int flags = 0;
+    if (sw.phase == 0) {
+        const int b = order ? order[blockIdx.y] : (int)blockIdx.y;
+        seq_rows(cu, b, T, &a.row0, &a.len);
+        a.slot0 = cu ? (long)chunk_base[b] : (long)b * nc_dense;
+        hin = h0 ? h0 + ((size_t)b * Hv + a.vh) * DD : nullptr;
+        hout = h_final ? h_final + ((size_t)b * Hv + a.vh) * DD : nullptr;
+    } else {
+        // phase 1, per sequence: N_0 .. N_{S-2} (N_0 walked from h0), then
+        // M_1 .. M_{S-2}; phase 2: segment j from its start state, the last
+        // one writing the final state
+        int b, j;
+        if (sw.phase == 1) {
+            const int per_seq = 2 * sw.S - 3, r = (int)blockIdx.y % per_seq;
+            b = (int)blockIdx.y / per_seq;
+            const bool m = r >= sw.S - 1;
+            j = m ? r - sw.S + 2 : r;
+            const size_t mat = ((size_t)b * sw.S + j) * Hv + a.vh;
+            hin = !m && j == 0 && h0 ? h0 + ((size_t)b * Hv + a.vh) * DD : nullptr;
+            hout = m ? sw.maps + sw.map_m + mat * DD : sw.maps + mat * DD;
+            flags = m ? SPINE_V_ZERO | SPINE_NO_OUT | SPINE_H0_EYE | SPINE_SPLIT_OUT : SPINE_NO_OUT;
+        } else {
+            b = (int)blockIdx.y / sw.S;
+            j = (int)blockIdx.y % sw.S;
+            const size_t mat = ((size_t)b * sw.S + j) * Hv + a.vh;
+            hin = j == 0 ? (h0 ? h0 + ((size_t)b * Hv + a.vh) * DD : nullptr)
+                         : j == 1 ? sw.maps + (mat - Hv) * DD : sw.starts + mat * DD;
+            hout = j == sw.S - 1 && h_final ? h_final + ((size_t)b * Hv + a.vh) * DD : nullptr;
+        }
+        const long t0 = (long)j * sw.L * C;
+        a.row0 = (long)b * T + t0;
+        a.len = min((long)sw.L * C, (long)T - t0);
+        a.slot0 = (long)b * nc_dense + (long)j * sw.L;
+    }
     int nc = (int)((a.len + C - 1) / C);
     // Only a decreasing cu_seqlens (a broken precondition) can make this
     // bind; it keeps every read inside the workspace.
     if (a.slot0 + nc > n_slots) nc = (int)max(0L, n_slots - a.slot0);
     a.nc = nc;
+    a.flags = flags;
     const int half = w & 1;   // which 16 of the workgroup's 32 columns
     const FragOffsets fo = frag_offsets(g, n, half);
     unsigned char* ex = lds + EX_BASE + 2 * half * EX_BYTES;   // this column half's exchange, parity 0
@@ -1186,7 +1242,8 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             ring_barrier();
             if (c >= 1) {
                 const long rem = a.len - (long)(c - 1) * C;
-                const rsrc_t ro = make_rsrc(obase + (size_t)(c - 1) * C * rs, (uint32_t)min((long)C, rem) * rs);
+                const rsrc_t ro = make_rsrc(obase + (size_t)(c - 1) * C * rs,
+                                            (flags & SPINE_NO_OUT) ? 0u : (uint32_t)min((long)C, rem) * rs);
                 const int par = (c - 1) & 1;
                 out_step<kOutF32>(lds + QS_BASE + par * QS_BYTES, lds + OS_BASE + ((c + 2) % N_OS) * OS_BYTES,
                                   lds + EX_BASE + par * EX_BYTES, lds + EX_BASE + (2 + par) * EX_BYTES, fq, ro,
@@ -1201,14 +1258,18 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // recurrence waves
     f32x4 h[8];
     const int col = a.tile * TILE_COLS + 16 * half + n;
-    const size_t hoff = ((size_t)b * Hv + a.vh) * D * D;
     // state row of h[db][r] in this lane: sig(db, 4g + r)
-    if (h0) {   // one uniform branch: all 32 loads in flight together
+    if (hin) {   // one uniform branch: all 32 loads in flight together
 #pragma unroll
         for (int db = 0; db < 8; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                h[db][r] = h0[hoff + (size_t)(sig_tile(db) + 8 * g + r) * D + col];
+                h[db][r] = hin[(size_t)(sig_tile(db) + 8 * g + r) * D + col];
+    } else if (flags & SPINE_H0_EYE) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) h[db][r] = sig_tile(db) + 8 * g + r == col ? 1.f : 0.f;
     } else {
 #pragma unroll
         for (int db = 0; db < 8; ++db) h[db] = zero4();
@@ -1237,12 +1298,148 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         __builtin_amdgcn_s_waitcnt(GDN_LGKMCNT(15));
         ring_barrier();
     }
-    if (h_final) {
+    if (hout && (flags & SPINE_SPLIT_OUT)) {
+        uint16_t* hi = reinterpret_cast<uint16_t*>(hout);
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const size_t e = (size_t)(sig_tile(db) + 8 * g + r) * D + col;
+                const short x = bf16_bits(h[db][r]);
+                hi[e] = (uint16_t)x;
+                hi[DD + e] = (uint16_t)bf16_bits(h[db][r] - bf16_bits_to_f32((uint16_t)x));
+            }
+    } else if (hout) {
 #pragma unroll
         for (int db = 0; db < 8; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                h_final[hoff + (size_t)(sig_tile(db) + 8 * g + r) * D + col] = h[db][r];
+                hout[(size_t)(sig_tile(db) + 8 * g + r) * D + col] = h[db][r];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The segment scan (ssm_gdn_tc_route.rs, the spine entries: the spine walks
+// the chunk states S_c in order; the map of one chunk, h -> M_c h + N_c, is
+// affine in h).  When the spine's workgroups fill only a small part of the
+// chip (few sequences and v-heads), each dense sequence is cut into S
+// segments of whole chunks and:
+//   1. one spine launch walks, all at once, segment 0 from h0 (its end state
+//      N_0), segments 1 .. S-2 from h = 0 (N_j) and segments 1 .. S-2 from
+//      h = I with V read as zero (the linear part M_j, written as bf16 hi/lo
+//      planes); no outputs are written;
+//   2. gdn_segment_combine_kernel runs the maps in order per (sequence,
+//      v-head, 32 columns): start(1) = N_0, start(j) = M_{j-1} start(j-1) +
+//      N_{j-1};
+//   3. a second spine launch walks every segment from its start state,
+//      writing the outputs, and the last segment writes the final state.
+// The WY prep runs once; every walk reads the same workspace slots.  The
+// products in 2. are formed from bf16 splits of both fp32 operands
+// (x = hi + lo; A B ~ Ahi Bhi + Ahi Blo + Alo Bhi), about 16 bits of each.
+
+// One workgroup per (sequence, v-head, 32 columns); wave w of 8 forms rows
+// 16 w .. 16 w + 15 of each product.  The start state lives in LDS as bf16 hi
+// and lo planes, column-major ([32 columns][128 rows + 8]) so that an MFMA B
+// fragment (8 consecutive rows of one column) is one 16-byte read.  The
+// operands of step j + 2 are loaded while step j runs.
+constexpr int CMB_LD = D + 8;
+constexpr int CMB_WAVES = 8;
+constexpr int CMB_RING = 4;
+constexpr int CMB_MAX_STEPS = 8;   // S - 2 <= 8: at most 10 segments per sequence
+
+struct CombineOps {
+    s16x8 a[4][2];       // M_j rows 16 w + n, k = 32 kk + 8 g .. + 7; hi, lo
+    float nv[2][4];      // N_j rows 16 w + 4 g + r, column 16 ct + n
+};
+
+__global__ void __launch_bounds__(64 * CMB_WAVES)
+gdn_segment_combine_kernel(SegWalk sw, int Hv)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t sh[2][TILE_COLS][CMB_LD];
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const int vh = blockIdx.x / N_TILES, tile = blockIdx.x % N_TILES, b = blockIdx.y;
+    const int c0 = tile * TILE_COLS;
+    const size_t DD = (size_t)D * D;
+    const int row = 16 * w + 4 * g;   // this lane's first accumulator row
+    auto mat = [&](int j) { return ((size_t)b * sw.S + j) * Hv + vh; };
+    auto load = [&](CombineOps& o, int j) {
+        const uint16_t* m = reinterpret_cast<const uint16_t*>(sw.maps + sw.map_m + mat(j) * DD);
+        const float* nj = sw.maps + mat(j) * DD;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                o.a[kk][p] = *reinterpret_cast<const s16x8*>(m + p * DD + (size_t)(16 * w + n) * D + 32 * kk + 8 * g);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o.nv[ct][r] = nj[(size_t)(row + r) * D + c0 + 16 * ct + n];
+    };
+    // x (rows row .. row + 3 of column c) into the planes
+    auto put = [&](const float (&x)[4], int c) {
+        s16x4 hi, lo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            hi[r] = bf16_bits(x[r]);
+            lo[r] = bf16_bits(x[r] - bf16_bits_to_f32((uint16_t)hi[r]));
+        }
+        *reinterpret_cast<s16x4*>(&sh[0][c][row]) = hi;
+        *reinterpret_cast<s16x4*>(&sh[1][c][row]) = lo;
+    };
+    // step j: start(j) = M_{j-1} start(j-1) + N_{j-1}, with o = (M_{j-1}, N_{j-1})
+    auto step = [&](const CombineOps& o, int j) {
+        f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const s16x8 bh = *reinterpret_cast<const s16x8*>(&sh[0][16 * ct + n][32 * kk + 8 * g]);
+                const s16x8 bl = *reinterpret_cast<const s16x8*>(&sh[1][16 * ct + n][32 * kk + 8 * g]);
+                acc[ct] = mfma_bf16(o.a[kk][0], bh, acc[ct]);
+                acc[ct] = mfma_bf16(o.a[kk][0], bl, acc[ct]);
+                acc[ct] = mfma_bf16(o.a[kk][1], bh, acc[ct]);
+            }
+        // every wave has read start(j - 1) (its MFMAs took the values); a
+        // plain barrier, which leaves the operand loads of later steps in flight
+        ring_barrier();
+        float* st = const_cast<float*>(sw.starts) + mat(j) * DD;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                x[r] = acc[ct][r] + o.nv[ct][r];
+                st[(size_t)(row + r) * D + c0 + 16 * ct + n] = x[r];
+            }
+            put(x, 16 * ct + n);
+        }
+        wait_lgkm0();
+        ring_barrier();
+    };
+    // the operands of up to CMB_RING steps in flight; the walk is unrolled
+    // in full, so that each step waits only for its own operands
+    const int last = sw.S - 2;
+    CombineOps o[CMB_RING];
+    float x[2][4];
+    {   // start(1) = N_0
+        const float* n0 = sw.maps + mat(0) * DD;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[ct][r] = n0[(size_t)(row + r) * D + c0 + 16 * ct + n];
+    }
+#pragma unroll
+    for (int i = 0; i < CMB_RING; ++i) load(o[i], min(1 + i, last));   // past the last map: read it again
+    put(x[0], n);
+    put(x[1], 16 + n);
+    wait_lgkm0();
+    ring_barrier();
+#pragma unroll
+    for (int t = 0; t < CMB_MAX_STEPS; ++t) {
+        if (2 + t >= sw.S) break;
+        step(o[t % CMB_RING], 2 + t);
+        if (t + CMB_RING < CMB_MAX_STEPS) load(o[t % CMB_RING], min(1 + t + CMB_RING, last));
     }
 }
 
@@ -1253,12 +1450,41 @@ long slot_count(int B, int T, bool packed) {
     return packed ? (long)(T + C - 1) / C + B : (long)B * ((T + C - 1) / C);
 }
 
+// The segment scan's cut of dense sequences: segments per sequence (0: the
+// plain spine) and chunks per segment.  It is taken when the spine's
+// workgroups (B Hv 4) fill at most a third of the 256 compute units; S is
+// the largest count whose map walks (2 S - 3 per sequence and v-head tile)
+// still fit on the chip in one pass, at least 3 and at most 10 (the combine's
+// unrolled steps).
+struct SegmentCut { int S, L; };
+SegmentCut segment_cut(int B, int T, int Hv, bool packed) {
+    SegmentCut sc{0, 0};
+    if (packed || T <= 0) return sc;
+    const int nc = (T + C - 1) / C;
+    const long wgs = (long)B * Hv * N_TILES;
+    const long s0 = min(min((long)nc, (256L / max(wgs, 1L) + 3) / 2), (long)CMB_MAX_STEPS + 2);
+    if (s0 < 3) return sc;
+    const int L = (int)((nc + s0 - 1) / s0);
+    const int S = (nc + L - 1) / L;
+    if (S < 3) return sc;
+    sc.S = S;
+    sc.L = L;
+    return sc;
+}
+
 }  // namespace
 
-size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv, bool packed)
+size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv, bool packed, bool segmented)
 {
     (void)Hk;
-    return table_bytes(B) + (size_t)slot_count(B, T, packed) * Hv * 2 * SLOT_STRIDE;
+    const size_t slots = (size_t)slot_count(B, T, packed) * Hv * 2 * SLOT_STRIDE;
+    const SegmentCut sc = segmented ? segment_cut(B, T, Hv, packed) : SegmentCut{0, 0};
+    const size_t plain = table_bytes(B) + slots;
+    if (sc.S == 0) return plain;
+    // the segment scan's: the slots, then N_j, M_j and start(j) per (segment,
+    // v-head); the size covers both routes
+    const size_t seg = slots + 3 * (size_t)B * sc.S * Hv * D * D * sizeof(float);
+    return seg > plain ? seg : plain;
 }
 
 bool prefill_mfma_accepts(const PrefillArgs& a)
@@ -1266,16 +1492,96 @@ bool prefill_mfma_accepts(const PrefillArgs& a)
     return a.io_dtype == 1 && a.dk == D && a.dv == D && a.chunk == C;
 }
 
+size_t prefill_workspace_need(int B, int T, int Hk, int Hv, int dk, int dv, int chunk, int io_dtype,
+                              bool packed, bool segmented)
+{
+    if (B < 1 || T < 0 || Hk < 1 || Hv < 1) return 0;
+    PrefillArgs a{};
+    a.io_dtype = io_dtype; a.dk = dk; a.dv = dv; a.chunk = chunk;
+    if (!prefill_mfma_accepts(a)) return 0;  // the generic kernel keeps everything in LDS
+    return prefill_mfma_workspace_bytes(B, T, Hk, Hv, packed, segmented);
+}
+
 Geometry prefill_mfma_geometry(const PrefillArgs& a)
 {
+    const SegmentCut sc = a.segmented ? segment_cut(a.B, a.T, a.Hv, a.cu_seqlens != nullptr) : SegmentCut{0, 0};
+    if (sc.S > 0) {
+        Geometry g{"gdn_wy_prep_kernel+gdn_spine_kernel(segment maps)+gdn_segment_combine_kernel"
+                   "+gdn_spine_kernel(segment outputs)",
+                   {(unsigned)(a.Hv * N_TILES), (unsigned)(a.B * sc.S), 1u}, 256u, (unsigned)SPINE_LDS};
+        return g;
+    }
     Geometry g{"gdn_wy_prep_kernel+gdn_spine_kernel", {(unsigned)(a.Hv * N_TILES), (unsigned)a.B, 1u}, 256u,
                (unsigned)SPINE_LDS};
     return g;
 }
 
+int prefill_mfma_segments(const PrefillArgs& a)
+{
+    return a.segmented ? segment_cut(a.B, a.T, a.Hv, a.cu_seqlens != nullptr).S : 0;
+}
+
+namespace {
+template <bool kOutF32>
+void launch_spine(const PrefillArgs& a, dim3 grid, const float* h0, float* h_final, const unsigned char* tbs,
+                  const unsigned char* pps, const int32_t* base, const int32_t* order, int nc_dense, long n_slots,
+                  SegWalk sw, hipStream_t s)
+{
+    hipLaunchKernelGGL((gdn_spine_kernel<kOutF32>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, h0, a.out, h_final, tbs, pps, a.T, a.Hk,
+                       a.Hv, a.cu_seqlens, base, order, nc_dense, n_slots, sw);
+}
+
+void launch_spine(const PrefillArgs& a, dim3 grid, const float* h0, float* h_final, const unsigned char* tbs,
+                  const unsigned char* pps, const int32_t* base, const int32_t* order, int nc_dense, long n_slots,
+                  SegWalk sw, hipStream_t s)
+{
+    if (a.out_dtype == 0)
+        launch_spine<true>(a, grid, h0, h_final, tbs, pps, base, order, nc_dense, n_slots, sw, s);
+    else
+        launch_spine<false>(a, grid, h0, h_final, tbs, pps, base, order, nc_dense, n_slots, sw, s);
+}
+
+void launch_prep(const PrefillArgs& a, unsigned char* tbs, unsigned char* pps, const int32_t* base,
+                 int nc_dense, long n_slots, hipStream_t s)
+{
+    const int G = a.Hv / a.Hk, nw = G < 4 ? G : 4;
+    hipLaunchKernelGGL(gdn_wy_prep_kernel, dim3((unsigned)n_slots, a.Hk, (unsigned)((G + nw - 1) / nw)),
+                       dim3(64 * nw), prep_lds_bytes(nw), s,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, a.log_g, a.beta, tbs, pps,
+                       a.B, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense);
+}
+
+hipError_t launch_prefill_segmented(const PrefillArgs& a, SegmentCut sc, hipStream_t s)
+{
+    const int nc = (a.T + C - 1) / C;
+    const long n_slots = (long)a.B * nc;
+    unsigned char* tbs = reinterpret_cast<unsigned char*>(a.workspace);
+    unsigned char* pps = tbs + (size_t)n_slots * a.Hv * SLOT_STRIDE;
+    SegWalk sw{};
+    sw.S = sc.S;
+    sw.L = sc.L;
+    sw.maps = reinterpret_cast<float*>(pps + (size_t)n_slots * a.Hv * SLOT_STRIDE);
+    sw.map_m = (long)a.B * sc.S * a.Hv * D * D;
+    sw.starts = sw.maps + 2 * sw.map_m;
+    launch_prep(a, tbs, pps, nullptr, nc, n_slots, s);
+    sw.phase = 1;
+    launch_spine(a, dim3(a.Hv * N_TILES, a.B * (2 * sc.S - 3)), a.h0, nullptr, tbs, pps, nullptr, nullptr, nc,
+                 n_slots, sw, s);
+    hipLaunchKernelGGL(gdn_segment_combine_kernel, dim3(a.Hv * N_TILES, a.B), dim3(64 * CMB_WAVES), 0, s, sw,
+                       a.Hv);
+    sw.phase = 2;
+    launch_spine(a, dim3(a.Hv * N_TILES, a.B * sc.S), a.h0, a.h_final, tbs, pps, nullptr, nullptr, nc, n_slots,
+                 sw, s);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
 {
     const bool packed = a.cu_seqlens != nullptr;
+    const SegmentCut sc = a.segmented ? segment_cut(a.B, a.T, a.Hv, packed) : SegmentCut{0, 0};
+    if (sc.S > 0) return launch_prefill_segmented(a, sc, s);
     int32_t* base = reinterpret_cast<int32_t*>(a.workspace);
     const int nc_dense = (a.T + C - 1) / C;
     const long n_slots = slot_count(a.B, a.T, packed);
@@ -1285,23 +1591,9 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s)
     if (packed) {
         hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.B, a.T, base);
     }
-    if (n_slots > 0) {
-        const int G = a.Hv / a.Hk, nw = G < 4 ? G : 4;
-        const size_t shmem = prep_lds_bytes(nw);
-        hipLaunchKernelGGL(gdn_wy_prep_kernel, dim3((unsigned)n_slots, a.Hk, (unsigned)((G + nw - 1) / nw)),
-                           dim3(64 * nw), shmem, s,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, a.log_g, a.beta, tbs, pps,
-                           a.B, a.T, a.Hk, a.Hv, a.cu_seqlens, base, nc_dense);
-    }
-    dim3 grid(a.Hv * N_TILES, a.B);
-    if (a.out_dtype == 0)
-        hipLaunchKernelGGL((gdn_spine_kernel<true>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
-                           (const uint16_t*)a.k, (const uint16_t*)a.v, a.h0, a.out, a.h_final, tbs, pps,
-                           a.T, a.Hk, a.Hv, a.cu_seqlens, base, order, nc_dense, n_slots);
-    else
-        hipLaunchKernelGGL((gdn_spine_kernel<false>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
-                           (const uint16_t*)a.k, (const uint16_t*)a.v, a.h0, a.out, a.h_final, tbs, pps,
-                           a.T, a.Hk, a.Hv, a.cu_seqlens, base, order, nc_dense, n_slots);
+    if (n_slots > 0) launch_prep(a, tbs, pps, base, nc_dense, n_slots, s);
+    launch_spine(a, dim3(a.Hv * N_TILES, a.B), a.h0, a.h_final, tbs, pps, base, order, nc_dense, n_slots,
+                 SegWalk{}, s);
     return hipGetLastError();
 }
 

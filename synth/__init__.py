@@ -42,9 +42,9 @@ def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
     return x / np.linalg.norm(x, axis=-1, keepdims=True)
 
 
-def _gates(rng: np.random.Generator, shape):
+def _gates(rng: np.random.Generator, shape, scale=0.1):
     x = rng.standard_normal(shape)
-    log_g = -np.logaddexp(0.0, x) * 0.1          # -softplus(x) * 0.1
+    log_g = -np.logaddexp(0.0, x) * scale        # -softplus(x) * scale
     y = rng.standard_normal(shape)
     beta = 1.0 / (1.0 + np.exp(-y))              # sigmoid(y)
     return log_g, beta
@@ -81,6 +81,9 @@ WORKLOADS = {
         Workload("prefill_t4576_h0", "prefill", B=1, T=4576, Hk=16, Hv=48, dk=128, dv=128, chunk=64,
                  io=torch.bfloat16, h0=True, seed=1002,
                  note="one 4576-token prefill call with an initial state"),
+        Workload("prefill_t4576_hv6", "prefill", B=1, T=4576, Hk=2, Hv=6, dk=128, dv=128, chunk=64,
+                 io=torch.bfloat16, h0=True, seed=1007,
+                 note="one 4576-token prefill call of a narrow layer: 6 v-heads over 2 k-heads"),
         Workload("varlen_b8", "prefill", B=8, T=0, Hk=16, Hv=48, dk=128, dv=128, chunk=64,
                  io=torch.bfloat16, h0=True, seed=1003, packed=(1600, 8192),
                  note="8 packed sequences of 1600..8192 tokens, per-sequence states"),
@@ -119,8 +122,11 @@ def packed_lengths(B: int, lo: int, hi: int, seed: int) -> np.ndarray:
     return rng.integers(lo, hi + 1, size=B)
 
 
-def prefill_inputs(B, T, Hk, Hv, dk, dv, io=torch.bfloat16, h0=False, seed=0, lengths=None):
-    """Inputs of one prefill call as CPU tensors.
+def prefill_inputs(B, T, Hk, Hv, dk, dv, io=torch.bfloat16, h0=False, seed=0, lengths=None,
+                   gate_scale=0.1):
+    """Inputs of one prefill call as CPU tensors (log_g = -gate_scale
+    softplus(x), x standard normal: a mean decay of about 0.08 per token at
+    the default, so a state forgets most of itself within ~50 tokens).
 
     Dense (lengths is None): q, k [B, T, Hk, dk]; v [B, T, Hv, dv];
     log_g, beta [B, T, Hv].  Packed (lengths given): rows of all sequences
@@ -138,7 +144,7 @@ def prefill_inputs(B, T, Hk, Hv, dk, dv, io=torch.bfloat16, h0=False, seed=0, le
     q = _unit_rows(rng, rows + (Hk, dk))
     k = _unit_rows(rng, rows + (Hk, dk))
     v = rng.standard_normal(rows + (Hv, dv))
-    log_g, beta = _gates(rng, rows + (Hv,))
+    log_g, beta = _gates(rng, rows + (Hv,), gate_scale)
     d = dict(q=_round(q, io), k=_round(k, io), v=_round(v, io),
              log_g=_round(log_g, torch.float32), beta=_round(beta, torch.float32),
              h0=None, cu_seqlens=cu)

@@ -27,12 +27,13 @@ def to_dev(d):
     return {k: (v.to(dev()) if torch.is_tensor(v) else v) for k, v in d.items()}
 
 
-def gpu_prefill(inp, chunk, out_dtype=None, want_state=True, h0=None):
+def gpu_prefill(inp, chunk, out_dtype=None, want_state=True, h0=None, segmented=False):
     g = to_dev(inp)
     h0 = g["h0"] if h0 is None else h0
     out, hf, route = gdn.chunk_prefill(g["q"], g["k"], g["v"], g["log_g"], g["beta"], h0,
                                        cu_seqlens=g["cu_seqlens"], chunk=chunk,
-                                       out_dtype=out_dtype, want_state=want_state)
+                                       out_dtype=out_dtype, want_state=want_state,
+                                       segmented=segmented)
     torch.cuda.synchronize()
     return out, hf, route
 

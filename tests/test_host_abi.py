@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in gdn.h but not exported"
     assert set(names) == set(gdn.SIGNATURES), "binding and header disagree"
@@ -74,6 +74,63 @@ def test_prefill_routes(lib):
     assert "grid=[144,1,1]" in r  # 48 v-heads x 3 column slices of 32
     assert prefill_plan(lib, chunk=32) == 0
     assert "chunk = 64" in gdn.last_route()
+
+
+def segmented_plan(lib, **kw):
+    a = dict(q=X, k=X, v=X, log_g=X, beta=X, h0=None, out=X, h_final=X, B=1, T=4576, Hk=2, Hv=6,
+             dk=128, dv=128, chunk=64, cu=None, io=1, od=1, ws=X, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.gdn_chunk_prefill_segmented_plan(a["q"], a["k"], a["v"], a["log_g"], a["beta"], a["h0"],
+                                                a["out"], a["h_final"], a["B"], a["T"], a["Hk"], a["Hv"],
+                                                a["dk"], a["dv"], a["chunk"], a["cu"], a["io"], a["od"],
+                                                a["ws"], a["ws_bytes"])
+
+
+SEG_ROUTE = ("gdn_wy_prep_kernel+gdn_spine_kernel(segment maps)+gdn_segment_combine_kernel"
+             "+gdn_spine_kernel(segment outputs)")
+
+
+@pytest.mark.parametrize("B,T,Hv,S", [
+    (1, 4576, 6, 6),      # 24 spine workgroups: (256 // 24 + 3) // 2 = 6 segments of 12 chunks
+    (2, 2373, 3, 6),      # 38 chunks: 6 segments of 7 chunks, the last one of 3
+    (1, 2560, 2, 10),     # capped at 10 segments (the combine's 8 unrolled steps)
+    (1, 192, 1, 3),       # 3 chunks: 3 one-chunk segments
+    (1, 577, 6, 5),       # 10 chunks, the last holding one row: 5 segments of 2
+])
+def test_segment_cut(lib, B, T, Hv, S):
+    assert segmented_plan(lib, B=B, T=T, Hk=1, Hv=Hv) == 0
+    r = gdn.last_route()
+    assert r.startswith(f"{SEG_ROUTE} grid=[{Hv * 4},{B * S},1]"), r
+
+
+def test_segmented_falls_back(lib):
+    # packed input, a spine that fills more than a third of the chip, and too
+    # few chunks for three segments: the plain spine, and the line says why
+    assert segmented_plan(lib, B=2, T=1000, cu=X) == 0
+    r = gdn.last_route()
+    assert r.startswith("gdn_wy_prep_kernel+gdn_spine_kernel grid=[24,2,1]") and "dense input" in r, r
+    assert segmented_plan(lib, Hk=4, Hv=24, T=700) == 0
+    r = gdn.last_route()
+    assert r.startswith("gdn_wy_prep_kernel+gdn_spine_kernel grid=[96,1,1]") and "fill the chip" in r, r
+    assert segmented_plan(lib, T=128) == 0
+    assert gdn.last_route().startswith("gdn_wy_prep_kernel+gdn_spine_kernel grid=[24,1,1]")
+    # other shapes run the generic kernel, as gdn_chunk_prefill would
+    assert segmented_plan(lib, dk=64, dv=64) == 0
+    assert gdn.last_route().startswith("gdn_prefill_generic_kernel")
+
+
+def test_segmented_workspace(lib):
+    # the public size covers the segment scan: the slots, then 3 fp32 128 x 128
+    # matrices per (segment, v-head); the plain route asks only its own size
+    plain = 256 + 72 * 6 * 2 * 7168
+    full = gdn.gdn_prefill_workspace_bytes(1, 4576, 2, 6, 128, 128, 64, 1)
+    assert full == 72 * 6 * 2 * 7168 + 3 * 6 * 6 * 128 * 128 * 4
+    assert segmented_plan(lib, ws_bytes=full) == 0
+    assert segmented_plan(lib, ws_bytes=full - 1) == 6
+    assert prefill_plan(lib, T=4576, Hk=2, Hv=6, ws_bytes=plain) == 0
+    assert prefill_plan(lib, T=4576, Hk=2, Hv=6, ws_bytes=plain - 1) == 6
+    # where the cut is not taken, both routes ask the same
+    assert gdn.gdn_prefill_workspace_bytes(1, 4576, 16, 48, 128, 128, 64, 1) == 256 + 72 * 48 * 2 * 7168
 
 
 @pytest.mark.parametrize("kw,status", [
