@@ -258,11 +258,13 @@ def bench_prefill(w, args, torch):
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=d)
     route = []
 
+    call = gdn.gdn_chunk_prefill_segmented if args.segmented else gdn.gdn_chunk_prefill
+
     def launch(i):   # on the current stream (the capture stream while a graph is recorded)
         g = sets[i]
-        r = gdn.gdn_chunk_prefill(g["q"], g["k"], g["v"], g["log_g"], g["beta"], g["h0"], g["out"],
-                                  g["hf"], w.B, T_arg, w.Hk, w.Hv, w.dk, w.dv, w.chunk,
-                                  cu_seqlens=g["cu_seqlens"], workspace=ws, stream=None)
+        r = call(g["q"], g["k"], g["v"], g["log_g"], g["beta"], g["h0"], g["out"],
+                 g["hf"], w.B, T_arg, w.Hk, w.Hv, w.dk, w.dv, w.chunk,
+                 cu_seqlens=g["cu_seqlens"], workspace=ws, stream=None)
         if not route:
             route.append(r)
 
@@ -278,7 +280,7 @@ def bench_prefill(w, args, torch):
     got = sets[(args.steps - 1) % n_sets]["out"].float().cpu().numpy()
     err = synth.max_rel_err(np.take(got, heads, axis=-2), np.take(ro, heads, axis=-2))
     ach = byt / (kern_ms * 1e-3) / 1e9
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name + ("_segmented" if args.segmented else ""))
     rec = {
         "metric": (f"GDN chunked-prefill tokens/s (Hv={w.Hv}, d={w.dk}, "
                    + (f"T={w.T}" if inp["cu_seqlens"] is None else f"{w.B} packed sequences, N={N}")
@@ -291,6 +293,7 @@ def bench_prefill(w, args, torch):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": N, "Hk": w.Hk, "Hv": w.Hv, "dk": w.dk,
                    "dv": w.dv, "chunk": w.chunk, "h0": w.h0, "out": "bf16", "h_final": "fp32",
+                   "entry": "gdn_chunk_prefill_segmented" if args.segmented else "gdn_chunk_prefill",
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
@@ -503,6 +506,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="with the default workload, skip the extra verify/fold keys")
+    ap.add_argument("--segmented", action="store_true",
+                    help="time a prefill workload through gdn_chunk_prefill_segmented (the segment "
+                         "scan where it is taken, e.g. --workload prefill_t4576_hv6)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run plain device-to-device copies of MIB MiB (the known-size "
                          "kernel that scales FETCH_SIZE / WRITE_SIZE counters) and exit")

@@ -770,7 +770,8 @@ constexpr int SPINE_V_ZERO = 1, SPINE_NO_OUT = 2, SPINE_H0_EYE = 4, SPINE_SPLIT_
 // Each dense sequence b is cut into S segments of L chunks (the last one
 // shorter); segment j covers tokens [j L C, min((j + 1) L C, T)).  maps
 // holds, per (b S + j, v-head), the matrix N_j (fp32) and from map_m on the
-// matrix M_j (bf16 planes); starts holds the start state of segment j >= 2.
+// matrix M_j (bf16 hi and lo planes in the combine's A-fragment order);
+// starts holds the start state of segment j >= 2.
 struct SegWalk {
     int S, L;
     int phase;             // 0: not a segment walk; 1: the map walks; 2: the output walks
@@ -1299,15 +1300,20 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         ring_barrier();
     }
     if (hout && (flags & SPINE_SPLIT_OUT)) {
-        uint16_t* hi = reinterpret_cast<uint16_t*>(hout);
+        // the combine's A-fragment order: element (row, col) in fragment
+        // (row / 16, col / 32), plane p, lane 16 ((col % 32) / 8) + row % 16,
+        // element col % 8, each fragment 1 KiB
+        uint16_t* m16 = reinterpret_cast<uint16_t*>(hout);
+        const int kk = col >> 5, gc = (col & 31) >> 3, ec = col & 7;
 #pragma unroll
         for (int db = 0; db < 8; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const size_t e = (size_t)(sig_tile(db) + 8 * g + r) * D + col;
+                const int row = sig_tile(db) + 8 * g + r;
+                const size_t e = ((size_t)(((row >> 4) * 4 + kk) * 2) * 64 + 16 * gc + (row & 15)) * 8 + ec;
                 const short x = bf16_bits(h[db][r]);
-                hi[e] = (uint16_t)x;
-                hi[DD + e] = (uint16_t)bf16_bits(h[db][r] - bf16_bits_to_f32((uint16_t)x));
+                m16[e] = (uint16_t)x;
+                m16[e + 512] = (uint16_t)bf16_bits(h[db][r] - bf16_bits_to_f32((uint16_t)x));
             }
     } else if (hout) {
 #pragma unroll
@@ -1351,6 +1357,9 @@ struct CombineOps {
     s16x8 a[4][2];       // M_j rows 16 w + n, k = 32 kk + 8 g .. + 7; hi, lo
     float nv[2][4];      // N_j rows 16 w + 4 g + r, column 16 ct + n
 };
+// M_j as the map walk writes it: per 16-row block w and 32-column step kk,
+// the hi then the lo plane of the A fragment, 64 lanes x 16 bytes each, so
+// that every fragment load is one contiguous 1 KiB.
 
 __global__ void __launch_bounds__(64 * CMB_WAVES)
 gdn_segment_combine_kernel(SegWalk sw, int Hv)
@@ -1370,7 +1379,7 @@ gdn_segment_combine_kernel(SegWalk sw, int Hv)
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int p = 0; p < 2; ++p)
-                o.a[kk][p] = *reinterpret_cast<const s16x8*>(m + p * DD + (size_t)(16 * w + n) * D + 32 * kk + 8 * g);
+                o.a[kk][p] = *reinterpret_cast<const s16x8*>(m + ((size_t)((w * 4 + kk) * 2 + p) * 64 + lane) * 8);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -1400,8 +1409,9 @@ gdn_segment_combine_kernel(SegWalk sw, int Hv)
                 acc[ct] = mfma_bf16(o.a[kk][0], bl, acc[ct]);
                 acc[ct] = mfma_bf16(o.a[kk][1], bh, acc[ct]);
             }
-        // every wave has read start(j - 1) (its MFMAs took the values); a
-        // plain barrier, which leaves the operand loads of later steps in flight
+        // every wave has read start(j - 1); a plain barrier, which leaves the
+        // operand loads of later steps in flight
+        wait_lgkm0();
         ring_barrier();
         float* st = const_cast<float*>(sw.starts) + mat(j) * DD;
 #pragma unroll
@@ -1429,12 +1439,16 @@ gdn_segment_combine_kernel(SegWalk sw, int Hv)
 #pragma unroll
             for (int r = 0; r < 4; ++r) x[ct][r] = n0[(size_t)(row + r) * D + c0 + 16 * ct + n];
     }
-#pragma unroll
-    for (int i = 0; i < CMB_RING; ++i) load(o[i], min(1 + i, last));   // past the last map: read it again
+    // the first step's operands ahead of the barrier, the others after it:
+    // every wave's N_0 rows then reach the compute unit ahead of the bulk of
+    // the fragment loads
+    load(o[0], 1);
     put(x[0], n);
     put(x[1], 16 + n);
     wait_lgkm0();
     ring_barrier();
+#pragma unroll
+    for (int i = 1; i < CMB_RING; ++i) load(o[i], min(1 + i, last));   // past the last map: read it again
 #pragma unroll
     for (int t = 0; t < CMB_MAX_STEPS; ++t) {
         if (2 + t >= sw.S) break;
