@@ -121,12 +121,16 @@ def time_launches(launch, n_sets, warmup, steps, torch, extra_replays=10):
     The timed launches are captured into one HIP graph and the graph is replayed
     between two events on the replay stream, so the kernels run back to back as
     under a serving loop; eagerly, the Python launch path (tens of microseconds
-    per call) would leave the GPU idle between short kernels.  Returns
-    (total_ms, average ms per launch, eager ms per launch, spread), the third
-    from an event pair around each of `steps` eager launches, for reference.
-    The first replay alone is the measurement; `extra_replays` more, each timed
-    on its own afterwards, give the spread of the per-launch average (median,
-    p10, p90 over the replays)."""
+    per call) would leave the GPU idle between short kernels.  The graph is
+    replayed 1 + `extra_replays` times, each replay timed on its own (exactly
+    `steps` launches between its events, synchronized before and after); the
+    measurement is the median replay.  The first timed replay runs up to ~8%
+    slower than the rest for the short decode kernels (the clocks settle again
+    after each host synchronization), so a single replay would report that
+    transient rather than the steady state a serving loop sees; it stays in the
+    spread as `first_replay_us`.  Returns (median replay ms, median ms per
+    launch, eager ms per launch, spread), the third from an event pair around
+    each of `steps` eager launches, for reference."""
     for i in range(warmup):
         launch(i % n_sets)
     torch.cuda.synchronize()
@@ -146,33 +150,26 @@ def time_launches(launch, n_sets, warmup, steps, torch, extra_replays=10):
             for i in range(steps):
                 launch(i % n_sets)
     torch.cuda.synchronize()
-    # untimed: the first replay uploads the graph, and the first timed replay
-    # after a single warm one still ran ~5% slower than the rest (clocks and
-    # queues settling); three warm replays make the timed one a steady-state one
+    # untimed: the first replay uploads the graph
     for _ in range(3):
         graph.replay()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    graph.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total = t0.elapsed_time(t1)
     per = []
-    for _ in range(extra_replays):
+    for _ in range(1 + extra_replays):
+        torch.cuda.synchronize()
         t0.record(stream)
         graph.replay()
         t1.record(stream)
         torch.cuda.synchronize()
         per.append(t0.elapsed_time(t1) / steps * 1e3)
-    spread = None
-    if per:
-        q = sorted(per)
-        pick = lambda f: q[min(len(q) - 1, int(round(f * (len(q) - 1))))]
-        spread = {"median_us": pick(0.5), "p10_us": pick(0.1), "p90_us": pick(0.9),
-                  "replays": len(q), "launches_per_replay": steps}
-    return total, total / steps, eager, spread
+    q = sorted(per)
+    pick = lambda f: q[min(len(q) - 1, int(round(f * (len(q) - 1))))]
+    med_us = pick(0.5)
+    spread = {"median_us": med_us, "p10_us": pick(0.1), "p90_us": pick(0.9), "first_replay_us": per[0],
+              "replays": len(q), "launches_per_replay": steps}
+    return med_us * steps / 1e3, med_us / 1e3, eager, spread
 
 
 def achievable_copy_gbs(torch, mib=1024, reps=10):
@@ -307,7 +304,7 @@ def bench_prefill(w, args, torch):
                                            "the target is stated as a fraction of MFMA peak"},
                      "kernel_ms": kern_ms, "eager_launch_ms": eager_ms, "spread": spread,
                      "kernel": route[0].split(" ")[0] if route else None},
-        "timing": "HIP events around one replay of a graph of the K launches",
+        "timing": "median of 11 replays of a HIP graph of the K launches, HIP events around each replay",
         "route": route[0] if route else None,
         "parity_max_rel_err_sampled_heads": err,
         "input_sets_rotated": n_sets,
@@ -377,7 +374,7 @@ def bench_verify(w, args, torch):
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "algorithmic_bytes": byt, "kernel_ms": kern_ms, "eager_launch_ms": eager_ms, "spread": spread},
-        "timing": "HIP events around one replay of a graph of the K launches",
+        "timing": "median of 11 replays of a HIP graph of the K launches, HIP events around each replay",
         "draft_tokens_per_s": w.B * K / (kern_ms * 1e-3),
         "parity_max_rel_err_out": err,
         "fold": {"kernel_ms": fold_ms, "eager_launch_ms": fold_eager_ms, "spread": fold_spread, "algorithmic_bytes": fbyt, "achieved": fbyt / (fold_ms * 1e-3) / 1e9,
@@ -432,7 +429,7 @@ def bench_step(w, args, torch):
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "algorithmic_bytes": byt, "kernel_ms": kern_ms, "eager_launch_ms": eager_ms, "spread": spread},
-        "timing": "HIP events around one replay of a graph of the K launches",
+        "timing": "median of 11 replays of a HIP graph of the K launches, HIP events around each replay",
         "tokens_per_s": w.B / (kern_ms * 1e-3),
         "parity_max_rel_err_out": err_out, "parity_max_rel_err_state": err_state,
         "route": route[0] if route else None,
@@ -480,7 +477,7 @@ def bench_ba(args, torch):
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(wl["name"]),
                      "algorithmic_bytes": byt, "algorithmic_flops": 2.0 * m * k * 2 * nv,
                      "kernel_ms": kern_ms, "eager_launch_ms": eager_ms, "spread": spread},
-        "timing": "HIP events around one replay of a graph of the K launches",
+        "timing": "median of 11 replays of a HIP graph of the K launches, HIP events around each replay",
         "tokens_per_s": m / (kern_ms * 1e-3),
         "parity_max_rel_err_sampled_tokens": err,
         "route": route[0] if route else None,

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 def _args(workload):
     return argparse.Namespace(gpus=1, steps=3, warmup=1, workload=workload, no_cpu_baseline=True,
-                              copy_calibration=0)
+                              copy_calibration=0, segmented=False, prefill_only=True)
 
 
 def _common(rec, workload):
@@ -37,7 +37,8 @@ def _common(rec, workload):
     assert r["frac_of_copy"] == pytest.approx(r["achieved"] / r["copy_GBs"])
     assert 0 < r["frac"] < 1 and 0 < r["copy_GBs"] < r["peak"]
     s = r["spread"]
-    assert s["replays"] == 10 and s["p10_us"] <= s["median_us"] <= s["p90_us"]
+    assert s["replays"] == 11 and s["p10_us"] <= s["median_us"] <= s["p90_us"] and s["first_replay_us"] > 0
+    assert r["kernel_ms"] == pytest.approx(s["median_us"] / 1e3)
     assert "cpu_baseline" not in rec
 
 
@@ -59,7 +60,7 @@ def test_verify_line():
     _common(rec, w.name)
     assert rec["value"] == pytest.approx(rec["roofline"]["achieved"])
     assert rec["parity_max_rel_err_out"] <= 2e-2
-    assert rec["fold"]["kernel_ms"] > 0 and rec["fold"]["spread"]["replays"] == 10
+    assert rec["fold"]["kernel_ms"] > 0 and rec["fold"]["spread"]["replays"] == 11
 
 
 def test_step_line():
