@@ -94,6 +94,18 @@ def test_cuts(B, T, Hk, Hv, h0, f32, gs):
     check(inp, out, hf)
 
 
+def test_without_final_state():
+    """h_final NULL: the output walks still run from the combined start states."""
+    inp = synth.prefill_inputs(1, 64 * 20 + 17, 1, 3, 128, 128, h0=True, seed=1150, gate_scale=0.002)
+    say("segment scan, no final state")
+    out, hf, route = gpu_prefill(inp, 64, want_state=False, segmented=True)
+    assert hf is None and route.startswith(SEG), route
+    ro, _ = oracle_prefill(inp)
+    e = rel_err(out, ro)
+    say(f"  out err {e:.3e}")
+    assert e <= TOL
+
+
 def test_falls_back_to_the_plain_spine():
     inp = synth.prefill_inputs(2, 0, 1, 2, 128, 128, h0=True, seed=1201, lengths=[300, 700])
     say("segment scan refused: packed")
