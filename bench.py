@@ -288,7 +288,7 @@ def bench_prefill(w, args, torch):
         "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "T": N, "Hk": w.Hk, "Hv": w.Hv, "dk": w.dk,
+        "config": {"workload": w.name, "seed": w.seed, "B": w.B, "T": N, "Hk": w.Hk, "Hv": w.Hv, "dk": w.dk,
                    "dv": w.dv, "chunk": w.chunk, "h0": w.h0, "out": "bf16", "h_final": "fp32",
                    "entry": "gdn_chunk_prefill_segmented" if args.segmented else "gdn_chunk_prefill",
                    "parallelism": "none (1 GPU)"},
@@ -370,7 +370,8 @@ def bench_verify(w, args, torch):
         "value": ach, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32 state, bf16 q/k/v", "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "K": K, "Hk": w.Hk, "Hv": w.Hv, "dk": w.dk, "dv": w.dv},
+        "config": {"workload": w.name, "seed": w.seed, "B": w.B, "K": K, "Hk": w.Hk, "Hv": w.Hv, "dk": w.dk,
+                   "dv": w.dv},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "algorithmic_bytes": byt, "kernel_ms": kern_ms, "eager_launch_ms": eager_ms, "spread": spread},
@@ -425,7 +426,8 @@ def bench_step(w, args, torch):
         "value": ach, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": total_ms / args.steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32 state, bf16 q/k/v", "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "K": 1, "Hk": w.Hk, "Hv": w.Hv, "dk": w.dk, "dv": w.dv},
+        "config": {"workload": w.name, "seed": w.seed, "B": w.B, "K": 1, "Hk": w.Hk, "Hv": w.Hv, "dk": w.dk,
+                   "dv": w.dv},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "algorithmic_bytes": byt, "kernel_ms": kern_ms, "eager_launch_ms": eager_ms, "spread": spread},
@@ -472,7 +474,8 @@ def bench_ba(args, torch):
         "value": ach, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": total_ms / args.steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 x and weight, fp32 accumulation and gates", "data": "synthetic",
-        "config": {"workload": wl["name"], "m": m, "k": k, "n": 2 * nv, "nv": nv, "vheads_per_group": G},
+        "config": {"workload": wl["name"], "seed": wl["seed"], "m": m, "k": k, "n": 2 * nv, "nv": nv,
+                   "vheads_per_group": G},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(wl["name"]),
                      "algorithmic_bytes": byt, "algorithmic_flops": 2.0 * m * k * 2 * nv,
