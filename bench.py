@@ -8,8 +8,11 @@ already sit in HBM.  The default workload is one 4576-token sequence with 48
 v-heads over 16 k-heads, d = 128, chunk 64, bf16 q/k/v, fp32 gates, an fp32
 initial state and fp32 final states.  Inputs rotate over enough copies
 (> 512 MB in total) that the 256 MB Infinity Cache cannot hold them between
-steps.  Prints one JSON line.  --workload verify_k4_b16 times the K = 4
-verify instead (HBM-bound; metric GB/s).
+steps.  Prints one JSON line; the default run adds the K = 4 verify's and the
+fold's HBM rooflines as extra keys.  Other workloads: prefill_t1168,
+varlen_b8 and prefill_t4576_hv6 (prefill, tokens/s; --segmented times
+gdn_chunk_prefill_segmented), verify_k4_b16, step_b16 and ba_gates_t4576
+(HBM-bound; metric GB/s).
 """
 from __future__ import annotations
 
