@@ -597,6 +597,7 @@ gdn_fold_d128_kernel(float* const* __restrict__ h_table, const float* stash,
 
     const int vh = blockIdx.x, b = blockIdx.y;
     constexpr int NM = 16 / S;                   // state rows per thread: this workgroup's share
+    static_assert(16 % S == 0 && NM % 4 == 0, "the row loop takes whole groups of four rows per thread");
     constexpr int LA = kLookahead < NM ? kLookahead : NM;
     const int m0 = (int)blockIdx.z * NM;
     // the word, the accept count and the state pointer are independent loads:

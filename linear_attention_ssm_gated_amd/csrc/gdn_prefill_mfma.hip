@@ -1,6 +1,7 @@
 // bf16 MFMA chunked prefill for dk = dv = 128, chunk = 64 (gfx950).
 //
-// Two kernels on the caller's stream:
+// Two kernels on the caller's stream (the segment scan for narrow layers,
+// further down, adds a second spine launch and a combine kernel):
 //
 // gdn_wy_prep_kernel, one workgroup per (chunk, k-head), all chunks at once:
 //   the intra-chunk terms that do not depend on the state (the pages' W/U
@@ -941,13 +942,10 @@ __device__ __forceinline__ void rec_step(f32x4 (&h)[8], const RecOps& o, RecOps&
                                          unsigned char* E, const FragOffsets& fo, int g, int lane)
 {
     const StageAddr Sn = stage_addr(Sn0, fo, g, lane);
-    // state -> bf16 B operand, and to the output partner
+    // state -> bf16 B operand (to the output partner after X is issued)
     s16x8 hb[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        hb[kk] = frag_b(h[2 * kk], h[2 * kk + 1]);
-        *reinterpret_cast<s16x8*>(E + 1024 * kk + 16 * lane) = hb[kk];
-    }
+    for (int kk = 0; kk < 4; ++kk) hb[kk] = frag_b(h[2 * kk], h[2 * kk + 1]);
     sched_fence();
     // X = K h, with the next chunk's update fragments of state blocks 0..3 read
     // in between; h scaled by gamma_L meanwhile (hb holds the state before it)
@@ -972,6 +970,9 @@ __device__ __forceinline__ void rec_step(f32x4 (&h)[8], const RecOps& o, RecOps&
             sched_fence();
         }
     }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<s16x8*>(E + 1024 * kk + 16 * lane) = hb[kk];
+    sched_fence();
     // the next chunk's T_e and decay factors, and K fragments of X into the
     // registers X just read
 #pragma unroll
@@ -984,13 +985,11 @@ __device__ __forceinline__ void rec_step(f32x4 (&h)[8], const RecOps& o, RecOps&
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) on.kx[kk][cb] = GDN_KX(Sn, kk, cb);
     sched_fence();
-    // R = V - gm X, rounded to the B operand of Delta_e = T_e R, and to the
-    // output partner
+    // R = V - gm X, rounded to the B operand of Delta_e = T_e R (and to the
+    // output partner once Delta_e is issued)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) resid(X[cb], o.vv[cb], o.gm[cb]);
     const s16x8 rb0 = frag_b(X[0], X[1]), rb1 = frag_b(X[2], X[3]);
-    *reinterpret_cast<s16x8*>(E + 4096 + 16 * lane) = rb0;
-    *reinterpret_cast<s16x8*>(E + 5120 + 16 * lane) = rb1;
     sched_fence();
     f32x4 Dl[4];
     Dl[0] = mfma_bf16(o.te[0], rb0, zero4());
@@ -1007,6 +1006,9 @@ __device__ __forceinline__ void rec_step(f32x4 (&h)[8], const RecOps& o, RecOps&
     sched_fence();
     Dl[2] = mfma_bf16(o.te[4], rb1, Dl[2]);
     Dl[3] = mfma_bf16(o.te[5], rb1, Dl[3]);
+    sched_fence();
+    *reinterpret_cast<s16x8*>(E + 4096 + 16 * lane) = rb0;
+    *reinterpret_cast<s16x8*>(E + 5120 + 16 * lane) = rb1;
     sched_fence();
     const s16x8 ds0 = frag_b(Dl[0], Dl[1]), ds1 = frag_b(Dl[2], Dl[3]);
     sched_fence();
@@ -1039,10 +1041,10 @@ __device__ __forceinline__ void rec_step(f32x4 (&h)[8], const RecOps& o, RecOps&
 #undef GDN_TE
 #undef GDN_GM
 #undef GDN_GL
-// ring reads a recurrence step issues after its last exchange write: K
-// fragments of k-steps 2 and 3 (8), transposed fragments of state blocks 4..7
-// (16 transposing reads) and V (4)
-constexpr int REC_READS_AFTER_EX = 28;
+// ring reads a recurrence step issues after its last exchange write (R, after
+// Delta_e): K fragments of k-step 3 (4), transposed fragments of state blocks
+// 4..7 (16 transposing reads) and V (4)
+constexpr int REC_READS_AFTER_EX = 24;
 static_assert(REC_READS_AFTER_EX >= 15, "the wait below then allows at most 15 outstanding");
 
 // The output wave, chunk c: O = gm (Q h) + PT R for the workgroup's 32
