@@ -778,7 +778,7 @@ struct SegWalk {
     int phase;             // 0: not a segment walk; 1: the map walks; 2: the output walks
     float* maps;
     long map_m;            // floats from maps to the M matrices: B S Hv D D
-    const float* starts;
+    float* starts;
 };
 
 struct SpineArgs {
@@ -1415,7 +1415,7 @@ gdn_segment_combine_kernel(SegWalk sw, int Hv)
         // operand loads of later steps in flight
         wait_lgkm0();
         ring_barrier();
-        float* st = const_cast<float*>(sw.starts) + mat(j) * DD;
+        float* st = sw.starts + mat(j) * DD;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             float x[4];
