@@ -772,7 +772,9 @@ constexpr int SPINE_V_ZERO = 1, SPINE_NO_OUT = 2, SPINE_H0_EYE = 4, SPINE_SPLIT_
 // shorter); segment j covers tokens [j L C, min((j + 1) L C, T)).  maps
 // holds, per (b S + j, v-head), the matrix N_j (fp32) and from map_m on the
 // matrix M_j (bf16 hi and lo planes in the combine's A-fragment order);
-// starts holds the start state of segment j >= 2.
+// starts holds the start state of segment j >= 2, and for j = 0 the
+// combine's copy of h0 (the output walks never read h0 itself, so that
+// h_final may alias it).
 struct SegWalk {
     int S, L;
     int phase;             // 0: not a segment walk; 1: the map walks; 2: the output walks
@@ -1181,7 +1183,9 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             b = (int)blockIdx.y / sw.S;
             j = (int)blockIdx.y % sw.S;
             const size_t mat = ((size_t)b * sw.S + j) * Hv + a.vh;
-            hin = j == 0 ? (h0 ? h0 + ((size_t)b * Hv + a.vh) * DD : nullptr)
+            // segment 0 starts from the combine's copy of h0: h_final, which
+            // the last segment writes in this same launch, may alias h0
+            hin = j == 0 ? (h0 ? sw.starts + mat * DD : nullptr)
                          : j == 1 ? sw.maps + (mat - Hv) * DD : sw.starts + mat * DD;
             hout = j == sw.S - 1 && h_final ? h_final + ((size_t)b * Hv + a.vh) * DD : nullptr;
         }
@@ -1340,7 +1344,9 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 //      v-head, 32 columns): start(1) = N_0, start(j) = M_{j-1} start(j-1) +
 //      N_{j-1};
 //   3. a second spine launch walks every segment from its start state,
-//      writing the outputs, and the last segment writes the final state.
+//      writing the outputs, and the last segment writes the final state
+//      (segment 0 starts from the combine's copy of h0, so h_final may
+//      alias h0 as in the plain route).
 // The WY prep runs once; every walk reads the same workspace slots.  The
 // products in 2. are formed from bf16 splits of both fp32 operands
 // (x = hi + lo; A B ~ Ahi Bhi + Ahi Blo + Alo Bhi), about 16 bits of each.
@@ -1364,7 +1370,7 @@ struct CombineOps {
 // that every fragment load is one contiguous 1 KiB.
 
 __global__ void __launch_bounds__(64 * CMB_WAVES)
-gdn_segment_combine_kernel(SegWalk sw, int Hv)
+gdn_segment_combine_kernel(SegWalk sw, const float* __restrict__ h0, int Hv)
 {
     __shared__ __attribute__((aligned(16))) uint16_t sh[2][TILE_COLS][CMB_LD];
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1374,6 +1380,15 @@ gdn_segment_combine_kernel(SegWalk sw, int Hv)
     const size_t DD = (size_t)D * D;
     const int row = 16 * w + 4 * g;   // this lane's first accumulator row
     auto mat = [&](int j) { return ((size_t)b * sw.S + j) * Hv + vh; };
+    if (h0) {   // h0's tile into segment 0's start slot
+        const float* src = h0 + ((size_t)b * Hv + vh) * DD + c0;
+        float* dst = sw.starts + mat(0) * DD + c0;
+        for (int e = threadIdx.x; e < D * TILE_COLS / 4; e += 64 * CMB_WAVES) {
+            const int r = e / (TILE_COLS / 4), c4 = 4 * (e % (TILE_COLS / 4));
+            *reinterpret_cast<float4*>(dst + (size_t)r * D + c4) =
+                *reinterpret_cast<const float4*>(src + (size_t)r * D + c4);
+        }
+    }
     auto load = [&](CombineOps& o, int j) {
         const uint16_t* m = reinterpret_cast<const uint16_t*>(sw.maps + sw.map_m + mat(j) * DD);
         const float* nj = sw.maps + mat(j) * DD;
@@ -1585,7 +1600,7 @@ hipError_t launch_prefill_segmented(const PrefillArgs& a, SegmentCut sc, hipStre
     launch_spine(a, dim3(a.Hv * N_TILES, a.B * (2 * sc.S - 3)), a.h0, nullptr, tbs, pps, nullptr, nullptr, nc,
                  n_slots, sw, s);
     hipLaunchKernelGGL(gdn_segment_combine_kernel, dim3(a.Hv * N_TILES, a.B), dim3(64 * CMB_WAVES), 0, s, sw,
-                       a.Hv);
+                       a.h0, a.Hv);
     sw.phase = 2;
     launch_spine(a, dim3(a.Hv * N_TILES, a.B * sc.S), a.h0, a.h_final, tbs, pps, nullptr, nullptr, nc, n_slots,
                  sw, s);

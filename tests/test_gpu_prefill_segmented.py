@@ -10,7 +10,8 @@ affine state maps are combined in order.  Checks:
     combined maps untested) and the workload's own gates;
   * the narrow 4576-token workload (6 v-heads over 2 k-heads) on every v-head,
     and against the plain spine's result on the same input;
-  * ragged tails, no initial state, fp32 outputs, two sequences;
+  * ragged tails, no initial state, fp32 outputs, two sequences, no final
+    state, and the final state written over the initial one (in place);
   * two runs give the same bytes;
   * the cut itself (segments and chunks per segment) from the route's grid;
   * packed input and wide layers fall back to the plain spine and say why.
@@ -18,8 +19,9 @@ affine state maps are combined in order.  Checks:
 import pytest
 import torch
 
+import linear_attention_ssm_gated_amd as gdn
 import synth
-from gpu_common import gpu_prefill, oracle_prefill, rel_err, say
+from gpu_common import dev, gpu_prefill, oracle_prefill, rel_err, say
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -104,6 +106,24 @@ def test_without_final_state():
     e = rel_err(out, ro)
     say(f"  out err {e:.3e}")
     assert e <= TOL
+
+
+def test_in_place_state():
+    """h_final aliasing h0, as the plain route allows: the last segment's
+    walk writes the final state while segment 0's walk starts from h0."""
+    B, T, Hk, Hv = 2, 64 * 30 + 9, 1, 3
+    inp = synth.prefill_inputs(B, T, Hk, Hv, 128, 128, h0=True, seed=1160, gate_scale=0.002)
+    g = {k: (v.to(dev()) if torch.is_tensor(v) else v) for k, v in inp.items()}
+    h = g["h0"].clone()
+    out = torch.empty_like(g["v"])
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(B, T, Hk, Hv, 128, 128, 64, gdn.GDN_BF16),
+                     dtype=torch.uint8, device=dev())
+    say("segment scan in place")
+    route = gdn.gdn_chunk_prefill_segmented(g["q"], g["k"], g["v"], g["log_g"], g["beta"], h, out, h,
+                                            B, T, Hk, Hv, 128, 128, 64, workspace=ws)
+    torch.cuda.synchronize()
+    assert route.startswith(SEG), route
+    check(inp, out, h)
 
 
 def test_falls_back_to_the_plain_spine():
