@@ -53,6 +53,18 @@ def test_prefill_line():
     assert rec["parity_max_rel_err_sampled_heads"] <= 2e-2
 
 
+def test_segmented_prefill_line():
+    say("bench contract: prefill_t4576_hv6 --segmented")
+    w = synth.WORKLOADS["prefill_t4576_hv6"]
+    args = _args(w.name)
+    args.segmented = True
+    rec = bench.with_copy_yardstick(bench.bench_prefill(w, args, torch), torch)
+    _common(rec, w.name)
+    assert rec["config"]["entry"] == "gdn_chunk_prefill_segmented"
+    assert "gdn_segment_combine_kernel" in rec["route"], rec["route"]
+    assert rec["parity_max_rel_err_sampled_heads"] <= 2e-2
+
+
 def test_verify_line():
     say("bench contract: verify_k4_b16")
     w = synth.WORKLOADS["verify_k4_b16"]
