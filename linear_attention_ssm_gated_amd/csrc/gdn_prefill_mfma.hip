@@ -772,9 +772,9 @@ constexpr int SPINE_V_ZERO = 1, SPINE_NO_OUT = 2, SPINE_H0_EYE = 4, SPINE_SPLIT_
 // shorter); segment j covers tokens [j L C, min((j + 1) L C, T)).  maps
 // holds, per (b S + j, v-head), the matrix N_j (fp32) and from map_m on the
 // matrix M_j (bf16 hi and lo planes in the combine's A-fragment order);
-// starts holds the start state of segment j >= 2, and for j = 0 the
-// combine's copy of h0 (the output walks never read h0 itself, so that
-// h_final may alias it).
+// starts holds the start state of segment j >= 2, and for j = 0 the map
+// walk's copy of h0 (the output walks never read h0 itself, so that h_final
+// may alias it).
 struct SegWalk {
     int S, L;
     int phase;             // 0: not a segment walk; 1: the map walks; 2: the output walks
@@ -1158,6 +1158,7 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // the start state read, the final state written (per v-head matrices)
     const float* hin;
     float* hout;
+    float* hcopy = nullptr;   // where the start state is also written (segment 0's copy of h0)
     int flags = 0;
     if (sw.phase == 0) {
         const int b = order ? order[blockIdx.y] : (int)blockIdx.y;
@@ -1177,13 +1178,16 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             j = m ? r - sw.S + 2 : r;
             const size_t mat = ((size_t)b * sw.S + j) * Hv + a.vh;
             hin = !m && j == 0 && h0 ? h0 + ((size_t)b * Hv + a.vh) * DD : nullptr;
+            // segment 0's walk also copies h0 for the output walks, which
+            // never read h0 itself (h_final may alias it)
+            if (hin) hcopy = sw.starts + mat * DD;
             hout = m ? sw.maps + sw.map_m + mat * DD : sw.maps + mat * DD;
             flags = m ? SPINE_V_ZERO | SPINE_NO_OUT | SPINE_H0_EYE | SPINE_SPLIT_OUT : SPINE_NO_OUT;
         } else {
             b = (int)blockIdx.y / sw.S;
             j = (int)blockIdx.y % sw.S;
             const size_t mat = ((size_t)b * sw.S + j) * Hv + a.vh;
-            // segment 0 starts from the combine's copy of h0: h_final, which
+            // segment 0 starts from the map walk's copy of h0: h_final, which
             // the last segment writes in this same launch, may alias h0
             hin = j == 0 ? (h0 ? sw.starts + mat * DD : nullptr)
                          : j == 1 ? sw.maps + (mat - Hv) * DD : sw.starts + mat * DD;
@@ -1272,6 +1276,12 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 h[db][r] = hin[(size_t)(sig_tile(db) + 8 * g + r) * D + col];
+        if (hcopy) {
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) hcopy[(size_t)(sig_tile(db) + 8 * g + r) * D + col] = h[db][r];
+        }
     } else if (flags & SPINE_H0_EYE) {
 #pragma unroll
         for (int db = 0; db < 8; ++db)
@@ -1345,8 +1355,8 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 //      N_{j-1};
 //   3. a second spine launch walks every segment from its start state,
 //      writing the outputs, and the last segment writes the final state
-//      (segment 0 starts from the combine's copy of h0, so h_final may
-//      alias h0 as in the plain route).
+//      (segment 0 starts from a copy of h0 that its map walk wrote, so
+//      h_final may alias h0 as in the plain route).
 // The WY prep runs once; every walk reads the same workspace slots.  The
 // products in 2. are formed from bf16 splits of both fp32 operands
 // (x = hi + lo; A B ~ Ahi Bhi + Ahi Blo + Alo Bhi), about 16 bits of each.
@@ -1370,7 +1380,7 @@ struct CombineOps {
 // that every fragment load is one contiguous 1 KiB.
 
 __global__ void __launch_bounds__(64 * CMB_WAVES)
-gdn_segment_combine_kernel(SegWalk sw, const float* __restrict__ h0, int Hv)
+gdn_segment_combine_kernel(SegWalk sw, int Hv)
 {
     __shared__ __attribute__((aligned(16))) uint16_t sh[2][TILE_COLS][CMB_LD];
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1380,15 +1390,6 @@ gdn_segment_combine_kernel(SegWalk sw, const float* __restrict__ h0, int Hv)
     const size_t DD = (size_t)D * D;
     const int row = 16 * w + 4 * g;   // this lane's first accumulator row
     auto mat = [&](int j) { return ((size_t)b * sw.S + j) * Hv + vh; };
-    if (h0) {   // h0's tile into segment 0's start slot
-        const float* src = h0 + ((size_t)b * Hv + vh) * DD + c0;
-        float* dst = sw.starts + mat(0) * DD + c0;
-        for (int e = threadIdx.x; e < D * TILE_COLS / 4; e += 64 * CMB_WAVES) {
-            const int r = e / (TILE_COLS / 4), c4 = 4 * (e % (TILE_COLS / 4));
-            *reinterpret_cast<float4*>(dst + (size_t)r * D + c4) =
-                *reinterpret_cast<const float4*>(src + (size_t)r * D + c4);
-        }
-    }
     auto load = [&](CombineOps& o, int j) {
         const uint16_t* m = reinterpret_cast<const uint16_t*>(sw.maps + sw.map_m + mat(j) * DD);
         const float* nj = sw.maps + mat(j) * DD;
@@ -1600,7 +1601,7 @@ hipError_t launch_prefill_segmented(const PrefillArgs& a, SegmentCut sc, hipStre
     launch_spine(a, dim3(a.Hv * N_TILES, a.B * (2 * sc.S - 3)), a.h0, nullptr, tbs, pps, nullptr, nullptr, nc,
                  n_slots, sw, s);
     hipLaunchKernelGGL(gdn_segment_combine_kernel, dim3(a.Hv * N_TILES, a.B), dim3(64 * CMB_WAVES), 0, s, sw,
-                       a.h0, a.Hv);
+                       a.Hv);
     sw.phase = 2;
     launch_spine(a, dim3(a.Hv * N_TILES, a.B * sc.S), a.h0, a.h_final, tbs, pps, nullptr, nullptr, nc, n_slots,
                  sw, s);
