@@ -9,7 +9,8 @@ v-heads over 16 k-heads, d = 128, chunk 64, bf16 q/k/v, fp32 gates, an fp32
 initial state and fp32 final states.  Inputs rotate over enough copies
 (> 512 MB in total) that the 256 MB Infinity Cache cannot hold them between
 steps.  Prints one JSON line; the default run adds the K = 4 verify's and the
-fold's HBM rooflines as extra keys.  Other workloads: prefill_t1168,
+fold's HBM rooflines and the 6-v-head share of the layer (plain spine and
+segment scan) as extra keys.  Other workloads: prefill_t1168,
 varlen_b8 and prefill_t4576_hv6 (prefill, tokens/s; --segmented times
 gdn_chunk_prefill_segmented), verify_k4_b16, step_b16 and ba_gates_t4576
 (HBM-bound; metric GB/s).
@@ -556,6 +557,22 @@ def main():
                                            "algorithmic_bytes": f["algorithmic_bytes"],
                                            "kernel_ms": f["kernel_ms"], "spread": f["spread"]},
                               "na": f["na"]}
+            # one GPU's share of the layer (6 v-heads over 2 k-heads): the plain
+            # spine and the segment scan, timed the same way
+            import types
+            nw = synth.WORKLOADS["prefill_t4576_hv6"]
+            narrow = {}
+            for seg in (False, True):
+                a2 = types.SimpleNamespace(**{**vars(args), "no_cpu_baseline": True, "segmented": seg})
+                r2 = bench_prefill(nw, a2, torch)
+                narrow["segment_scan" if seg else "plain_spine"] = {
+                    "ms_per_call": r2["ms_per_step"], "tokens_per_s": r2["value"], "route": r2["route"],
+                    "spread": r2["roofline"]["spread"],
+                    "parity_max_rel_err_sampled_heads": r2["parity_max_rel_err_sampled_heads"]}
+            narrow["speedup"] = narrow["plain_spine"]["ms_per_call"] / narrow["segment_scan"]["ms_per_call"]
+            narrow["config"] = {"workload": nw.name, "seed": nw.seed, "B": nw.B, "T": nw.T, "Hk": nw.Hk,
+                                "Hv": nw.Hv, "dk": nw.dk, "dv": nw.dv, "chunk": nw.chunk, "h0": nw.h0}
+            rec["prefill_hv6"] = narrow
     elif w.kind == "decode_step":
         rec = bench_step(w, args, torch)
     else:

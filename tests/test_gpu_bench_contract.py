@@ -93,7 +93,8 @@ def test_ba_line():
 
 def test_default_line_carries_verify_and_fold():
     """The default run (what the driver times) prints one JSON line whose extra
-    keys hold the K = 4 verify's and the fold's HBM rooflines."""
+    keys hold the K = 4 verify's and the fold's HBM rooflines and the 6-v-head
+    layer share through the plain spine and the segment scan."""
     import os
     import subprocess
     import sys
@@ -111,3 +112,10 @@ def test_default_line_carries_verify_and_fold():
         assert rf["bound"] == "hbm" and rf["unit"] == "GB/s"
         assert 0 < rf["frac"] < 1 and rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
     assert rec["decode_verify_k4"]["parity_max_rel_err_out"] <= 2e-2
+    nar = rec["prefill_hv6"]
+    assert nar["config"]["Hv"] == 6 and nar["config"]["Hk"] == 2
+    assert "gdn_segment_combine_kernel" in nar["segment_scan"]["route"]
+    assert "segment" not in nar["plain_spine"]["route"].split(" ")[0]
+    assert nar["speedup"] == pytest.approx(nar["plain_spine"]["ms_per_call"] / nar["segment_scan"]["ms_per_call"])
+    for k in ("plain_spine", "segment_scan"):
+        assert nar[k]["parity_max_rel_err_sampled_heads"] <= 2e-2
