@@ -222,10 +222,9 @@ __device__ __forceinline__ s16x8 lds_read16(const unsigned char* p) {
 // rows in LDS once; each wave then forms, for its v-head,
 //   A = strict_lower(beta_r exp(G_r - G_s) (K K^T)_rs),   T = (I + A)^-1,
 // and writes T_b = T diag(beta) to the (chunk, v-head) slot as bf16 MFMA
-// fragments.  The ten 16 x 16 tiles of Q K^T are shared out over the group's
-// waves; the wave that forms a tile writes P = exp(G_r - G_s) (Q K^T)_rs
-// (lower, with the diagonal) of every v-head of the group for it.  The waves
-// never wait for each other after the staging.
+// fragments, and P = exp(G_r - G_s) (Q K^T)_rs (lower, with the diagonal)
+// into its own LDS fragments.  The waves never wait for each other after the
+// staging.
 //
 // Gram tiles are formed above the diagonal, tile (m, i) = K_m K_i^T and
 // K_m Q_i^T (16-row blocks, m <= i), so that lane (g, n) register s holds
@@ -387,65 +386,57 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         Gc[i] = f32x4{t4.x, t4.y, t4.z, t4.w};
     }
 
-    // Gram tiles by block column i: P tiles leave at once, A stays in
-    // registers.  Q K^T tile number i (i + 1) / 2 + m belongs to wave (that
-    // number) % nw of the group.
+    // Gram tiles by block column i, each wave for its own v-head: the decay
+    // factor of an entry is formed once and serves A and P alike; P tiles
+    // leave at once (as bf16, into the wave's P fragments), A stays in
+    // registers.  (Sharing the Q K^T tiles among the group's waves instead
+    // saves MFMAs but forms every P factor again per v-head, which costs
+    // more issue than the MFMAs.)
     unsigned char* dstT = tbs + ((size_t)x * Hv + vh) * SLOT_STRIDE;
     const bool live = h < G;
-    const int nlive = min(nw, G - (int)blockIdx.z * nw);   // live v-heads of the group
     s16x8 kf[4][4];
     f32x4 Aoff[6];   // A_im, m < i, index (i - 1) i / 2 + m
     f32x4 Adg[4];    // A_ii: register s = A_ii[n][4g + s]
+    if (live) {
+        unsigned char* sPw = sPall + w * SLOT_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        s16x8 qf[4];
+        for (int i = 0; i < 4; ++i) {
+            s16x8 qf[4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const unsigned char* fr = sKQ + (16 * i + n) * 256 + 16 * ((4 * kk + g) ^ (n & 7));
-            kf[i][kk] = lds_read16(fr);
-            qf[kk] = lds_read16(fr + C * D * 2);
-        }
+            for (int kk = 0; kk < 4; ++kk) {
+                const unsigned char* fr = sKQ + (16 * i + n) * 256 + 16 * ((4 * kk + g) ^ (n & 7));
+                kf[i][kk] = lds_read16(fr);
+                qf[kk] = lds_read16(fr + C * D * 2);
+            }
 #pragma unroll
-        for (int m = 0; m <= i; ++m) {
-            const bool mine = ((i * (i + 1) / 2 + m) % nw) == w;   // wave-uniform
-            f32x4 kk_acc = zero4(), kq_acc = zero4();
+            for (int m = 0; m <= i; ++m) {
+                f32x4 kk_acc = zero4(), kq_acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) kk_acc = mfma_bf16(kf[m][kk], kf[i][kk], kk_acc);
-            if (mine) {
+                for (int kk = 0; kk < 4; ++kk) kk_acc = mfma_bf16(kf[m][kk], kf[i][kk], kk_acc);
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) kq_acc = mfma_bf16(kf[m][kk], qf[kk], kq_acc);
-            }
-            f32x4 av;
+                f32x4 av, pv;
 #pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-                const float e = __builtin_amdgcn_exp2f(Gr[i] - Gc[m][s2]);
-                av[s2] = Bt[i] * e * kk_acc[s2];
-                if (m == i) av[s2] = (n > 4 * g + s2) ? av[s2] : 0.f;   // A strictly lower
-            }
-            if (m == i) Adg[i] = av;
-            else Aoff[(i - 1) * i / 2 + m] = av;
-            if (mine) {
-                // this lane's four entries: row rho = 16 i + n, columns c0 .. c0 + 3;
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const float e = __builtin_amdgcn_exp2f(Gr[i] - Gc[m][s2]);
+                    av[s2] = Bt[i] * e * kk_acc[s2];
+                    pv[s2] = e * kq_acc[s2];
+                    if (m == i) {
+                        av[s2] = (n > 4 * g + s2) ? av[s2] : 0.f;    // A strictly lower
+                        pv[s2] = (n >= 4 * g + s2) ? pv[s2] : 0.f;   // P lower with the diagonal
+                    }
+                }
+                if (m == i) Adg[i] = av;
+                else Aoff[(i - 1) * i / 2 + m] = av;
+                // this lane's four P entries: row rho = 16 i + n, columns c0 .. c0 + 3;
                 // rho = sig(cb, np), and the columns are half `hf` of lane
                 // (gp, np)'s granule in fragment (cb, kk)
                 const int rho = 16 * i + n, c0 = 16 * m + 4 * g;
                 const int cb = 2 * (rho >> 5) + ((rho >> 2) & 1), np = 4 * ((rho >> 3) & 3) + (rho & 3);
                 const int kk2 = c0 >> 5, gp = (c0 & 31) >> 3, hf = (c0 >> 2) & 1;
                 const uint32_t off = FRAG_BYTES * (kk2 == 0 ? cb : cb + 2) + 16u * (16 * gp + np) + 8u * hf;
-                for (int hh = 0; hh < nlive; ++hh) {   // every v-head of the group
-                    const float* sGh = prep_lds + prep_gb_base(nw) + hh * 2 * C;
-                    const float gr = sGh[16 * i + n];
-                    const float4 gc = *reinterpret_cast<const float4*>(sGh + 16 * m + 4 * g);
-                    const float gcv[4] = {gc.x, gc.y, gc.z, gc.w};
-                    f32x4 pv;
-#pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2) {
-                        pv[s2] = __builtin_amdgcn_exp2f(gr - gcv[s2]) * kq_acc[s2];
-                        if (m == i) pv[s2] = (n >= 4 * g + s2) ? pv[s2] : 0.f;   // P lower with the diagonal
-                    }
-                    *reinterpret_cast<s16x4*>(sPall + hh * SLOT_BYTES + off) =
-                        s16x4{bf16_bits(pv[0]), bf16_bits(pv[1]), bf16_bits(pv[2]), bf16_bits(pv[3])};
-                }
+                *reinterpret_cast<s16x4*>(sPw + off) =
+                    s16x4{bf16_bits(pv[0]), bf16_bits(pv[1]), bf16_bits(pv[2]), bf16_bits(pv[3])};
             }
         }
     }
