@@ -222,6 +222,22 @@ gdn_ba_partial_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict
         }
 }
 
+// The gating on the hardware's exp2, log2 and reciprocal (the IEEE division
+// and the library log1p take about 150 instructions a value, and a wave whose
+// lanes mix gates and betas runs both).  softplus(z) = max(z, 0) +
+// log1p(exp(-|z|)), with log1p(e) = log(1 + e) e / ((1 + e) - 1) (e itself
+// where 1 + e rounds to 1), which keeps its relative accuracy for small e.
+constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
+__device__ __forceinline__ float sigmoid(float y) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-y * LOG2E));
+}
+__device__ __forceinline__ float softplus(float z) {
+    const float e = __builtin_amdgcn_exp2f(-fabsf(z) * LOG2E);
+    const float u = 1.f + e;
+    const float l1p = u == 1.f ? e : __builtin_amdgcn_logf(u) * LN2 * (e * __builtin_amdgcn_rcpf(u - 1.f));
+    return fmaxf(z, 0.f) + l1p;
+}
+
 __global__ void __launch_bounds__(256)
 gdn_ba_gate_kernel(const float* __restrict__ partial, const float* __restrict__ a_log,
                    const float* __restrict__ dt_bias, float* __restrict__ out, int m, int n,
@@ -246,12 +262,10 @@ gdn_ba_gate_kernel(const float* __restrict__ partial, const float* __restrict__ 
     const int group = o / (2 * G), within = o % (2 * G);
     float* row = out + (size_t)t * gate_stride;
     if (within < G) {
-        row[nv + group * G + within] = 1.f / (1.f + __expf(-y));
+        row[nv + group * G + within] = sigmoid(y);
     } else {
         const int vh = group * G + (within - G);
-        const float z = y + dt_bias[vh];
-        const float sp = fmaxf(z, 0.f) + log1pf(__expf(-fabsf(z)));
-        row[vh] = -__expf(a_log[vh]) * sp;
+        row[vh] = -__expf(a_log[vh]) * softplus(y + dt_bias[vh]);
     }
 }
 
