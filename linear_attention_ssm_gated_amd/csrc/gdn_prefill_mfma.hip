@@ -11,8 +11,9 @@
 //     T_e = diag(el) T diag(beta),  el = exp(G_L - G)                  (per v-head)
 //     PT = (Gamma o lower_incl(Q K^T)) T diag(beta)                    (per v-head)
 //   K K^T, Q K^T and PT run on bf16 MFMA with fp32 accumulation; T is solved
-//   in fp32 (16x16 diagonal blocks by forward substitution on VALU, the blocks
-//   below them on fp32 MFMA); T_e and PT are stored as bf16 MFMA fragments in
+//   in 16x16 blocks: the diagonal ones by forward substitution in fp32 on VALU,
+//   the ones below them on bf16 MFMA with fp32 accumulation; T_e and PT are
+//   stored as bf16 MFMA fragments in
 //   the workspace, their granules above the diagonal left unwritten (they are
 //   zero, and the spine never reads them from memory), each followed by the
 //   chunk's per-row factors gm = exp(G).  Every decay factor formed is exp of
@@ -73,10 +74,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma_bf16(s16x8 a, s16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
@@ -233,9 +230,9 @@ __device__ __forceinline__ s16x8 lds_read16(const unsigned char* p) {
 // of one row, and an off-diagonal A tile is directly the A operand of an
 // fp32 MFMA whose k-slot of lane group g at step s is 4g + s.
 //
-// T is formed on 16 x 16 fp32 blocks: T_ii = (I + A_ii)^-1 by forward
-// substitution, then T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj by distance
-// i - j.  Block row r is stored at slot p(r) = 4 (r/4) + ((r + r/4) % 4) and
+// T is formed on 16 x 16 blocks: T_ii = (I + A_ii)^-1 by forward
+// substitution in fp32, then T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj by
+// distance i - j on bf16 products.  Block row r is stored at slot p(r) = 4 (r/4) + ((r + r/4) % 4) and
 // element c at c ^ 4 (r/4), so that the rows 4g + s that one MFMA operand or
 // accumulator register spans fall in four different 16-bank windows.  The
 // four diagonal blocks start at floats 272 i (four windows again), the six
@@ -478,45 +475,56 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
     wave_lds_sync();
 
-    // blocks below the diagonal, by distance: M = sum_m A_im T_mj with A_im
-    // from registers (k-slot 4g + s at step s), one accumulator per m; then
-    // T_ij = -T_ii M with M's registers as the B operand.
+    // blocks below the diagonal, by distance, on bf16 MFMA with fp32
+    // accumulation: M = sum_{m=j}^{i-1} A_im T_mj takes two blocks m per
+    // 32-wide k-step, k-slot 8g + t standing for column 4g + (t % 4) of the
+    // first (t < 4) or the second block, so that A_im's registers (row n,
+    // columns 4g .. 4g + 3) and T_mj's accumulator registers (rows 4g .. 4g + 3,
+    // column n) are the two operands as they are; then T_ij = -T_ii M with T_ii's
+    // row n from LDS as A and M's registers as B, the k-step's second half zero.
+    // The diagonal blocks come from LDS in accumulator order, the others from
+    // the registers of the distances before.  (The blocks enter T_e and PT as
+    // bf16 anyway; their bf16 products cost one MFMA per pair of blocks where
+    // the fp32 16x16x4 form took four per block at twice the cycles.)
     int boff[4], toff[4];
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
         boff[s2] = blk_elem(4 * g + s2, n);   // Y[4g + s][n]
         toff[s2] = blk_elem(n, 4 * g + s2);   // T_ii[n][4g + s]
     }
+    f32x4 Tdg[3];   // T_jj, j < 3: register s = T_jj[4g + s][n]
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) Tdg[j][s2] = lds[t_blk(j, j) + boff[s2]];
+    f32x4 Tlo[6];   // T_ij, i > j, index (i - 1) i / 2 + j: register s = T_ij[4g + s][n]
 #pragma unroll
     for (int d = 1; d < 4; ++d) {
-        f32x4 R[3];
 #pragma unroll
         for (int j = 0; j + d < 4; ++j) {
             const int i = j + d;
-            f32x4 Mp[3];
+            f32x4 M = zero4();
 #pragma unroll
-            for (int m = j; m < i; ++m) {
-                const float* Y = lds + t_blk(m, j);
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) acc = mfma_f32(Aoff[(i - 1) * i / 2 + m][s2], Y[boff[s2]], acc);
-                Mp[m - j] = acc;
+            for (int m = j; m < i; m += 2) {
+                const f32x4 t0 = m == j ? Tdg[j] : Tlo[(m - 1) * m / 2 + j];
+                const f32x4 a1 = m + 1 < i ? Aoff[(i - 1) * i / 2 + m + 1] : zero4();
+                const f32x4 t1 = m + 1 < i ? Tlo[m * (m + 1) / 2 + j] : zero4();
+                M = mfma_bf16(frag_b(Aoff[(i - 1) * i / 2 + m], a1), frag_b(t0, t1), M);
             }
-            f32x4 M = Mp[0];
+            f32x4 ti;
 #pragma unroll
-            for (int m = 1; m < d; ++m) M = M + Mp[m];
-            const float* Ti = lds + t_blk(i, i);
-            f32x4 t = zero4();
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) t = mfma_f32(Ti[toff[s2]], M[s2], t);
-            R[j] = t;
+            for (int s2 = 0; s2 < 4; ++s2) ti[s2] = lds[t_blk(i, i) + toff[s2]];
+            const f32x4 t = mfma_bf16(frag_b(ti, zero4()), frag_b(M, zero4()), zero4());
+            Tlo[(i - 1) * i / 2 + j] = -t;
         }
-#pragma unroll
-        for (int j = 0; j + d < 4; ++j)
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) lds[t_blk(j + d, j) + boff[s2]] = -R[j][s2];
-        wave_lds_sync();
     }
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < i; ++j)
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) lds[t_blk(i, j) + boff[s2]] = Tlo[(i - 1) * i / 2 + j][s2];
+    wave_lds_sync();
 
     // T_e = diag(el) T diag(beta), el = exp(G_L - G) per row -> workspace as
     // bf16 fragments: lane l of fragment f holds row sig(cb, l % 16), columns
