@@ -244,6 +244,7 @@ __host__ __device__ constexpr int t_blk(int i, int j) {
     return i == j ? 272 * i : 1088 + 256 * ((i - 1) * i / 2 + j);
 }
 constexpr int PREP_WAVE_FLOATS = 1088 + 6 * 256;          // per wave, over the K/Q staging
+constexpr int P_TILE_BYTES = 64 * 8;   // a P tile in LDS: each lane's four bf16
 constexpr int PREP_STAGE_BYTES = 2 * C * D * 2;           // K then Q, 256-byte rows
 // K/Q staging: granule q of row r at q ^ (r % 8), so that a fragment read (8
 // lanes, 8 consecutive rows, one granule) is free of bank conflicts.  After
@@ -359,12 +360,6 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             te_tail[16 * (m >> 2) + 4 * t + (m & 3)] = gm;
             if (lane == 0) te_tail[64] = __builtin_amdgcn_exp2f(GLl2);
             pt_tail[4 * m + t] = gm;
-            // granules of this v-head's P wholly above the diagonal, which no
-            // Gram tile writes, are zero (they enter P T_b as an operand)
-#pragma unroll
-            for (int f = 0; f < NFRAG; ++f)
-                if (2 * frag_kk(f) + (g >> 1) > (sig_row(frag_cb(f), n) >> 4))
-                    *reinterpret_cast<s16x8*>(sPall + w * SLOT_BYTES + FRAG_BYTES * f + 16 * lane) = s16x8{};
         }
     }
     // the DMA is inline assembly the compiler does not track: wait for it
@@ -425,14 +420,9 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                 }
                 if (m == i) Adg[i] = av;
                 else Aoff[(i - 1) * i / 2 + m] = av;
-                // this lane's four P entries: row rho = 16 i + n, columns c0 .. c0 + 3;
-                // rho = sig(cb, np), and the columns are half `hf` of lane
-                // (gp, np)'s granule in fragment (cb, kk)
-                const int rho = 16 * i + n, c0 = 16 * m + 4 * g;
-                const int cb = 2 * (rho >> 5) + ((rho >> 2) & 1), np = 4 * ((rho >> 3) & 3) + (rho & 3);
-                const int kk2 = c0 >> 5, gp = (c0 & 31) >> 3, hf = (c0 >> 2) & 1;
-                const uint32_t off = FRAG_BYTES * (kk2 == 0 ? cb : cb + 2) + 16u * (16 * gp + np) + 8u * hf;
-                *reinterpret_cast<s16x4*>(sPw + off) =
+                // this lane's four P entries (row 16 i + n, columns 16 m + 4 g ..
+                // + 3) in tile order, lane order within the tile
+                *reinterpret_cast<s16x4*>(sPw + P_TILE_BYTES * (i * (i + 1) / 2 + m) + 8 * lane) =
                     s16x4{bf16_bits(pv[0]), bf16_bits(pv[1]), bf16_bits(pv[2]), bf16_bits(pv[3])};
             }
         }
@@ -492,12 +482,17 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         boff[s2] = blk_elem(4 * g + s2, n);   // Y[4g + s][n]
         toff[s2] = blk_elem(n, 4 * g + s2);   // T_ii[n][4g + s]
     }
-    f32x4 Tdg[3];   // T_jj, j < 3: register s = T_jj[4g + s][n]
+    // Column n of every block scaled by beta_{16 j + n}: the blocks formed are
+    // those of T_b = T diag(beta) (the recursion is linear in a column
+    // scaling), which T_e and PT take.
+    f32x4 Tdg[4];   // T_b,jj: register s = T_jj[4g + s][n] beta_{16 j + n}
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+    for (int j = 0; j < 4; ++j) {
+        const float bj = sBt[16 * j + n];
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) Tdg[j][s2] = lds[t_blk(j, j) + boff[s2]];
-    f32x4 Tlo[6];   // T_ij, i > j, index (i - 1) i / 2 + j: register s = T_ij[4g + s][n]
+        for (int s2 = 0; s2 < 4; ++s2) Tdg[j][s2] = lds[t_blk(j, j) + boff[s2]] * bj;
+    }
+    f32x4 Tlo[6];   // T_b,ij, i > j, index (i - 1) i / 2 + j: register s = T_b,ij[4g + s][n]
 #pragma unroll
     for (int d = 1; d < 4; ++d) {
 #pragma unroll
@@ -518,15 +513,18 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             Tlo[(i - 1) * i / 2 + j] = -t;
         }
     }
+    // every read of the unscaled diagonal blocks is done: T_b into LDS
+    wave_lds_sync();
 #pragma unroll
-    for (int i = 1; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < i; ++j)
+        for (int j = 0; j <= i; ++j)
 #pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) lds[t_blk(i, j) + boff[s2]] = Tlo[(i - 1) * i / 2 + j][s2];
+            for (int s2 = 0; s2 < 4; ++s2)
+                lds[t_blk(i, j) + boff[s2]] = i == j ? Tdg[i][s2] : Tlo[(i - 1) * i / 2 + j][s2];
     wave_lds_sync();
 
-    // T_e = diag(el) T diag(beta), el = exp(G_L - G) per row -> workspace as
+    // T_e = diag(el) T_b, el = exp(G_L - G) per row -> workspace as
     // bf16 fragments: lane l of fragment f holds row sig(cb, l % 16), columns
     // c0 .. c0 + 7 (c0 = 32 kk + 8 (l / 16)), when that granule reaches the
     // diagonal
@@ -541,55 +539,50 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             const float* row = blk + 16 * prow(rr);
             const float4 a = *reinterpret_cast<const float4*>(row + 4 * (q4 ^ (rr >> 2)));
             const float4 e = *reinterpret_cast<const float4*>(row + 4 * ((q4 + 1) ^ (rr >> 2)));
-            const float4 b0 = *reinterpret_cast<const float4*>(sBt + c0);
-            const float4 b1 = *reinterpret_cast<const float4*>(sBt + c0 + 4);
             const float el = __builtin_amdgcn_exp2f(GL2 - sG[r]);
             *reinterpret_cast<s16x8*>(dstT + FRAG_BYTES * f + 16 * lane) =
-                s16x8{bf16_bits(el * (a.x * b0.x)), bf16_bits(el * (a.y * b0.y)), bf16_bits(el * (a.z * b0.z)),
-                      bf16_bits(el * (a.w * b0.w)), bf16_bits(el * (e.x * b1.x)), bf16_bits(el * (e.y * b1.y)),
-                      bf16_bits(el * (e.z * b1.z)), bf16_bits(el * (e.w * b1.w))};
+                s16x8{bf16_bits(el * a.x), bf16_bits(el * a.y), bf16_bits(el * a.z), bf16_bits(el * a.w),
+                      bf16_bits(el * e.x), bf16_bits(el * e.y), bf16_bits(el * e.z), bf16_bits(el * e.w)};
         }
     }
 
-    // PT = P T diag(beta), formed transposed (PT^T = (T diag(beta))^T P^T) so
-    // that lane (g, n) ends with four consecutive columns of one row.  Output
-    // tile (a, cb) covers columns 16 a .. 16 a + 15 and rows sig(cb, .); its
-    // k-steps q run over the rows s of T diag(beta) that can be nonzero for
-    // both factors.  A operand (a, q): lane (g, n) holds T[s][16 a + n] beta,
-    // s = 32 q + 8 g + i, gathered from the fp32 blocks (block row 2 q + g / 2;
-    // blocks above the diagonal are zero); B operand (cb, q): P fragment
-    // (cb, q) from LDS.  Granules wholly above the diagonal are not written.
+    // PT = P T_b, formed transposed (PT^T = T_b^T P^T): output tile (a, ip)
+    // covers columns 16 a .. + 15 and rows 16 ip .. + 15, and its k runs over
+    // the row blocks ib = a .. ip of T_b (T_b and P are lower triangular), two
+    // blocks per k-step, k-slot 8g + t standing for row 4g + (t % 4) of the
+    // first (t < 4) or the second block: the A operand is then T_b's
+    // accumulator registers (column 16 a + n, rows 4g .. 4g + 3) and the B
+    // operand P's tile registers as the Gram phase left them (row 16 ip + n,
+    // columns 4g .. 4g + 3), both as they are.  Lane (g, n) ends with
+    // PT[16 ip + n][16 a + 4g .. + 3], half of a workspace granule; granules
+    // wholly above the diagonal are not written.
     const unsigned char* sPw = sPall + w * SLOT_BYTES;
     unsigned char* dstP = pps + ((size_t)x * Hv + vh) * SLOT_STRIDE;
-    s16x8 ta[6];   // (a, q) = (0, 0) (0, 1) (1, 0) (1, 1) (2, 1) (3, 1)
+    auto tb = [&](int ib, int a) { return ib == a ? Tdg[a] : Tlo[(ib - 1) * ib / 2 + a]; };
+    auto ptile = [&](int ip, int ib) {
+        return *reinterpret_cast<const s16x4*>(sPw + P_TILE_BYTES * (ip * (ip + 1) / 2 + ib) + 8 * lane);
+    };
 #pragma unroll
-    for (int u = 0; u < 6; ++u) {
-        const int a = u < 4 ? u >> 1 : u - 2;
-        const int q = u < 4 ? u & 1 : 1;
-        const int ib = 2 * q + (g >> 1);
-        const float* blk = lds + (ib == a ? 272 * ib : 1088 + 256 * ((ib - 1) * ib / 2 + a));
-        const float bt = sBt[16 * a + n];
-        float v8[8];
+    for (int ip = 0; ip < 4; ++ip) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int rr = 8 * (g & 1) + i;
-            v8[i] = ib >= a ? blk[blk_elem(rr, n)] * bt : 0.f;
-        }
-        ta[u] = s16x8{bf16_bits(v8[0]), bf16_bits(v8[1]), bf16_bits(v8[2]), bf16_bits(v8[3]),
-                      bf16_bits(v8[4]), bf16_bits(v8[5]), bf16_bits(v8[6]), bf16_bits(v8[7])};
-    }
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        const s16x8 p0 = lds_read16(sPw + FRAG_BYTES * cb + 16 * lane);
-        const s16x8 p1 = cb >= 2 ? lds_read16(sPw + FRAG_BYTES * (cb + 2) + 16 * lane) : s16x8{};
-#pragma unroll
-        for (int a = 0; a < (cb < 2 ? 2 : 4); ++a) {
+        for (int a = 0; a <= ip; ++a) {
             f32x4 acc = zero4();
-            if (a < 2) acc = mfma_bf16(ta[2 * a], p0, acc);
-            if (cb >= 2) acc = mfma_bf16(ta[a < 2 ? 2 * a + 1 : a + 2], p1, acc);
-            const int f = a < 2 ? cb : cb + 2, gp = 2 * (a & 1) + (g >> 1);
-            if (frag_live(f, 16 * gp + n))
-                *reinterpret_cast<s16x4*>(dstP + FRAG_BYTES * f + 16 * (16 * gp + n) + 8 * (g & 1)) =
+#pragma unroll
+            for (int ib = a; ib <= ip; ib += 2) {
+                const bool two = ib + 1 <= ip;
+                const s16x4 p0 = ptile(ip, ib);
+                const s16x4 p1 = two ? ptile(ip, ib + 1) : s16x4{0, 0, 0, 0};
+                const s16x8 pb = s16x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+                acc = mfma_bf16(frag_b(tb(ib, a), two ? tb(ib + 1, a) : zero4()), pb, acc);
+            }
+            // row rho = sig(cb, np); columns 16 a + 4 g .. are half hf of lane
+            // (gp, np)'s granule in fragment (cb, kk)
+            const int rho = 16 * ip + n, c0 = 16 * a + 4 * g;
+            const int cb = 2 * (rho >> 5) + ((rho >> 2) & 1), np = 4 * ((rho >> 3) & 3) + (rho & 3);
+            const int kk2 = c0 >> 5, gp = (c0 & 31) >> 3, hf = (c0 >> 2) & 1;
+            const int f = kk2 == 0 ? cb : cb + 2;
+            if (8 * (c0 >> 3) <= rho)   // the granule reaches the diagonal
+                *reinterpret_cast<s16x4*>(dstP + FRAG_BYTES * f + 16 * (16 * gp + np) + 8 * hf) =
                     s16x4{bf16_bits(acc[0]), bf16_bits(acc[1]), bf16_bits(acc[2]), bf16_bits(acc[3])};
         }
     }
