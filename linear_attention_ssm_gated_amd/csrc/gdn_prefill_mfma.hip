@@ -562,29 +562,40 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     auto ptile = [&](int ip, int ib) {
         return *reinterpret_cast<const s16x4*>(sPw + P_TILE_BYTES * (ip * (ip + 1) / 2 + ib) + 8 * lane);
     };
+    auto pt_tile = [&](int ip, int a) {
+        f32x4 acc = zero4();
 #pragma unroll
-    for (int ip = 0; ip < 4; ++ip) {
-#pragma unroll
-        for (int a = 0; a <= ip; ++a) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int ib = a; ib <= ip; ib += 2) {
-                const bool two = ib + 1 <= ip;
-                const s16x4 p0 = ptile(ip, ib);
-                const s16x4 p1 = two ? ptile(ip, ib + 1) : s16x4{0, 0, 0, 0};
-                const s16x8 pb = s16x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-                acc = mfma_bf16(frag_b(tb(ib, a), two ? tb(ib + 1, a) : zero4()), pb, acc);
-            }
-            // row rho = sig(cb, np); columns 16 a + 4 g .. are half hf of lane
-            // (gp, np)'s granule in fragment (cb, kk)
-            const int rho = 16 * ip + n, c0 = 16 * a + 4 * g;
-            const int cb = 2 * (rho >> 5) + ((rho >> 2) & 1), np = 4 * ((rho >> 3) & 3) + (rho & 3);
-            const int kk2 = c0 >> 5, gp = (c0 & 31) >> 3, hf = (c0 >> 2) & 1;
-            const int f = kk2 == 0 ? cb : cb + 2;
-            if (8 * (c0 >> 3) <= rho)   // the granule reaches the diagonal
-                *reinterpret_cast<s16x4*>(dstP + FRAG_BYTES * f + 16 * (16 * gp + np) + 8 * hf) =
-                    s16x4{bf16_bits(acc[0]), bf16_bits(acc[1]), bf16_bits(acc[2]), bf16_bits(acc[3])};
+        for (int ib = a; ib <= ip; ib += 2) {
+            const bool two = ib + 1 <= ip;
+            const s16x4 p0 = ptile(ip, ib);
+            const s16x4 p1 = two ? ptile(ip, ib + 1) : s16x4{0, 0, 0, 0};
+            const s16x8 pb = s16x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            acc = mfma_bf16(frag_b(tb(ib, a), two ? tb(ib + 1, a) : zero4()), pb, acc);
         }
+        const s16x4 v = s16x4{bf16_bits(acc[0]), bf16_bits(acc[1]), bf16_bits(acc[2]), bf16_bits(acc[3])};
+        return __builtin_bit_cast(u32x2v, v);
+    };
+    // the ten output tiles in pairs: lane groups 2e and 2e + 1 hold the two
+    // halves of a granule, so one permlane16 swap per dword leaves the even
+    // group with the first tile's whole granules and the odd group with the
+    // second's, each stored as one 16-byte piece
+    constexpr int TIP[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3}, TA[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+    const int ge = g & ~1;   // the even group of the pair: the granule's first half
+#pragma unroll
+    for (int u = 0; u < 10; u += 2) {
+        const u32x2v v0 = pt_tile(TIP[u], TA[u]), v1 = pt_tile(TIP[u + 1], TA[u + 1]);
+        const auto s0 = __builtin_amdgcn_permlane16_swap(v0[0], v1[0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(v0[1], v1[1], false, false);
+        const u32x4v granule = u32x4v{s0[0], s1[0], s0[1], s1[1]};
+        const int ip = (g & 1) ? TIP[u + 1] : TIP[u], a = (g & 1) ? TA[u + 1] : TA[u];
+        // row rho = sig(cb, np); columns 16 a + 4 ge .. + 7 are lane (gp, np)'s
+        // granule in fragment (cb, kk)
+        const int rho = 16 * ip + n, c0 = 16 * a + 4 * ge;
+        const int cb = 2 * (rho >> 5) + ((rho >> 2) & 1), np = 4 * ((rho >> 3) & 3) + (rho & 3);
+        const int kk2 = c0 >> 5, gp = (c0 & 31) >> 3;
+        const int f = kk2 == 0 ? cb : cb + 2;
+        if (c0 <= rho)   // the granule reaches the diagonal
+            *reinterpret_cast<u32x4v*>(dstP + FRAG_BYTES * f + 16 * (16 * gp + np)) = granule;
     }
 }
 
