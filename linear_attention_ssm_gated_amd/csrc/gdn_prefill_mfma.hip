@@ -168,6 +168,8 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+// the nontemporal cache-policy bit of a gfx950 buffer access
+constexpr int CPOL_NT = 2;
 __device__ __forceinline__ s16x8 buffer_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
     const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
     return __builtin_bit_cast(s16x8, v);
@@ -1060,7 +1062,10 @@ static_assert(REC_READS_AFTER_EX >= 15, "the wait below then allows at most 15 o
 // transpose, so lane (g, n) register r of tile cb ends up holding
 // O[sig(cb, n)][4g + r] of its column half, four consecutive columns of one
 // row.  Each Q fragment serves both halves; the next k-step's fragments are
-// read while this one's products run.  `ro` covers exactly the chunk's rows.
+// read while this one's products run.  `ro` covers exactly the chunk's rows;
+// lane_off[u] is this lane's byte offset within a row: for fp32 outputs that
+// of its four columns of half u, for bf16 that of the eight columns it
+// stores after the lane swaps (both entries).
 template <bool kOutF32>
 __device__ __forceinline__ void out_step(const unsigned char* Qs, const unsigned char* Os, const unsigned char* E0,
                                          const unsigned char* E1, const FragOffsets& fo, rsrc_t ro,
@@ -1106,28 +1111,66 @@ __device__ __forceinline__ void out_step(const unsigned char* Qs, const unsigned
         }
         sched_fence();
     }
+    f32x4 O[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        f32x4 O[4];
-        O[0] = mfma_bf16(rb[u][0], pf[0], Y[u][0] * g4.x);
-        O[1] = mfma_bf16(rb[u][0], pf[1], Y[u][1] * g4.y);
-        O[2] = mfma_bf16(rb[u][0], pf[2], Y[u][2] * g4.z);
-        O[3] = mfma_bf16(rb[u][0], pf[3], Y[u][3] * g4.w);
-        O[2] = mfma_bf16(rb[u][1], pf[4], O[2]);
-        O[3] = mfma_bf16(rb[u][1], pf[5], O[3]);
-        // hardware RNE conversion; rows past a partial chunk fall outside `ro`
+        O[u][0] = mfma_bf16(rb[u][0], pf[0], Y[u][0] * g4.x);
+        O[u][1] = mfma_bf16(rb[u][0], pf[1], Y[u][1] * g4.y);
+        O[u][2] = mfma_bf16(rb[u][0], pf[2], Y[u][2] * g4.z);
+        O[u][3] = mfma_bf16(rb[u][0], pf[3], Y[u][3] * g4.w);
+        O[u][2] = mfma_bf16(rb[u][1], pf[4], O[u][2]);
+        O[u][3] = mfma_bf16(rb[u][1], pf[5], O[u][3]);
+    }
+    // Rows past a partial chunk fall outside `ro`.  Nothing here reads the
+    // outputs back: the stores are nontemporal.
+    if constexpr (kOutF32) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            const f32x4 v = O[cb];
-            if (kOutF32) {
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const f32x4 v = O[u][cb];
                 __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(v[0]), __float_as_uint(v[1]),
                                                               __float_as_uint(v[2]), __float_as_uint(v[3])},
-                                                       ro, lane_off[u], soff[cb], 0);
-            } else {
-                const uint32_t lo = (uint16_t)bf16_bits(v[0]) | ((uint32_t)(uint16_t)bf16_bits(v[1]) << 16);
-                const uint32_t hi = (uint16_t)bf16_bits(v[2]) | ((uint32_t)(uint16_t)bf16_bits(v[3]) << 16);
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2v{lo, hi}, ro, lane_off[u], soff[cb], 0);
+                                                       ro, lane_off[u], soff[cb], CPOL_NT);
             }
+    } else {
+        // bf16 (hardware RNE conversion): a lane holds 8 bytes of its row's 64
+        // (the workgroup's 32 columns).  Two rounds of permlane16 swaps put
+        // each row's 64 bytes into the lanes n, 16 + n, 32 + n, 48 + n: first
+        // between tiles 2p and 2p + 1 of one column half (the even lane group
+        // then holds 8 columns of tile 2p's row, the odd group the same
+        // columns of tile 2p + 1's), then between the two halves, after which
+        // lane group g holds columns 8 (g / 2) + 16 (g % 2) .. + 7 of one row,
+        // of tile 2p in the first register and of tile 2p + 1 in the second.
+        // Each store then writes 16 rows as 64-byte pieces: half the
+        // instructions, and half the pieces, of one 8-byte store per tile.
+        u32x2v pk[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const f32x4 v = O[u][cb];
+                pk[u][cb] = u32x2v{(uint32_t)(uint16_t)bf16_bits(v[0]) | ((uint32_t)(uint16_t)bf16_bits(v[1]) << 16),
+                                   (uint32_t)(uint16_t)bf16_bits(v[2]) | ((uint32_t)(uint16_t)bf16_bits(v[3]) << 16)};
+            }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            u32x4v half_rows[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const auto s0 = __builtin_amdgcn_permlane16_swap(pk[u][2 * p][0], pk[u][2 * p + 1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane16_swap(pk[u][2 * p][1], pk[u][2 * p + 1][1], false, false);
+                half_rows[u] = u32x4v{s0[0], s1[0], s0[1], s1[1]};
+            }
+            u32x4v r0, r1;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const auto t = __builtin_amdgcn_permlane16_swap(half_rows[0][d], half_rows[1][d], false, false);
+                r0[d] = t[0];
+                r1[d] = t[1];
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(r0, ro, lane_off[0], soff[2 * p], CPOL_NT);
+            __builtin_amdgcn_raw_buffer_store_b128(r1, ro, lane_off[0], soff[2 * p + 1], CPOL_NT);
         }
     }
 }
@@ -1243,7 +1286,8 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         uint32_t lane_off[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-            lane_off[u] = (uint32_t)(8 * (n >> 2) + (n & 3)) * rs + (uint32_t)(a.tile * TILE_COLS + 16 * u + 4 * g) * es;
+            lane_off[u] = (uint32_t)(8 * (n >> 2) + (n & 3)) * rs +
+                          (uint32_t)(a.tile * TILE_COLS + (kOutF32 ? 16 * u + 4 * g : 8 * (g >> 1) + 16 * (g & 1))) * es;
         uint32_t soff[4];
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) soff[cb] = (uint32_t)sig_tile(cb) * rs;
