@@ -195,7 +195,7 @@ gdn_ba_partial_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                        for (int j = 0; j < OTW; ++j) acc[rt][j] = mfma_bf16(af[rt], wb[u][s][j], acc[rt][j]);
+                        for (int j = 0; j < OTW; ++j) acc[rt][j] = mfma_bf16(wb[u][s][j], af[rt], acc[rt][j]);
                 }
                 if (b + WAHEAD < nb) {
 #pragma unroll
@@ -206,20 +206,33 @@ gdn_ba_partial_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict
             }
         }
     }
-    // partial[split][t][o]: lane (g, i) of tile (rt, j) holds tokens
-    // 16 rt + 4 g + r of output column o_row[j]
+    // partial[split][t][o].  The products are formed transposed (the weight
+    // fragment as the A operand, the activations as B), so lane (g, i) of
+    // tile (rt, j) holds outputs 16 (OTW wave + j) + 4 g .. + 3 of token
+    // 16 rt + i: one 16-byte store each, a token's 16 outputs of the tile in
+    // four neighbouring lanes.
     float* dst = partial + (size_t)split * m * n;
+    // rows of whole, aligned 16-byte granules
+    const bool vec = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(partial) & 15) == 0;
 #pragma unroll
-    for (int j = 0; j < OTW; ++j)
-        if (o_row[j] < n) {
+    for (int j = 0; j < OTW; ++j) {
+        const int o4 = 16 * (OTW * wave + j) + 4 * g;
+        if (o4 >= n) continue;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt) {
+            const int t = t0 + 16 * rt + i;
+            if (t >= m) continue;
+            float* p = dst + (size_t)t * n + o4;
+            const f32x4 v = acc[rt][j];
+            if (vec) {
+                *reinterpret_cast<f32x4*>(p) = v;
+            } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = t0 + 16 * rt + 4 * g + r;
-                    if (t < m) dst[(size_t)t * n + o_row[j]] = acc[rt][j][r];
-                }
+                for (int r = 0; r < 4; ++r)
+                    if (o4 + r < n) p[r] = v[r];
+            }
         }
+    }
 }
 
 // The gating on the hardware's exp2, log2 and reciprocal (the IEEE division
