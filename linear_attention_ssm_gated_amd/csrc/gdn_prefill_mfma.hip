@@ -83,6 +83,12 @@ __device__ __forceinline__ short bf16_bits(float x) {
 }
 
 // B operand from two accumulator tiles of consecutive k-blocks.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two floats rounded to bf16 (RNE) in one dword, the first in the low half
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
 __device__ __forceinline__ s16x8 frag_b(f32x4 lo, f32x4 hi) {
     return s16x8{bf16_bits(lo[0]), bf16_bits(lo[1]), bf16_bits(lo[2]), bf16_bits(lo[3]),
                  bf16_bits(hi[0]), bf16_bits(hi[1]), bf16_bits(hi[2]), bf16_bits(hi[3])};
@@ -1111,55 +1117,51 @@ __device__ __forceinline__ void out_step(const unsigned char* Qs, const unsigned
         }
         sched_fence();
     }
-    f32x4 O[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        O[u][0] = mfma_bf16(rb[u][0], pf[0], Y[u][0] * g4.x);
-        O[u][1] = mfma_bf16(rb[u][0], pf[1], Y[u][1] * g4.y);
-        O[u][2] = mfma_bf16(rb[u][0], pf[2], Y[u][2] * g4.z);
-        O[u][3] = mfma_bf16(rb[u][0], pf[3], Y[u][3] * g4.w);
-        O[u][2] = mfma_bf16(rb[u][1], pf[4], O[u][2]);
-        O[u][3] = mfma_bf16(rb[u][1], pf[5], O[u][3]);
-    }
-    // Rows past a partial chunk fall outside `ro`.  Nothing here reads the
+    // O = gm (Q h) + PT R by pairs of tiles (2p, 2p + 1), both column halves;
+    // rows past a partial chunk fall outside `ro`.  Nothing here reads the
     // outputs back: the stores are nontemporal.
-    if constexpr (kOutF32) {
+    const float gs[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        f32x4 O[2][2];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const f32x4 v = O[u][cb];
-                __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(v[0]), __float_as_uint(v[1]),
-                                                              __float_as_uint(v[2]), __float_as_uint(v[3])},
-                                                       ro, lane_off[u], soff[cb], CPOL_NT);
+            for (int e = 0; e < 2; ++e) {
+                const int cb = 2 * p + e;
+                O[u][e] = mfma_bf16(rb[u][0], pf[cb], Y[u][cb] * gs[cb]);
+                if (p == 1) O[u][e] = mfma_bf16(rb[u][1], pf[cb + 2], O[u][e]);
             }
-    } else {
-        // bf16 (hardware RNE conversion): a lane holds 8 bytes of its row's 64
-        // (the workgroup's 32 columns).  Two rounds of permlane16 swaps put
-        // each row's 64 bytes into the lanes n, 16 + n, 32 + n, 48 + n: first
-        // between tiles 2p and 2p + 1 of one column half (the even lane group
-        // then holds 8 columns of tile 2p's row, the odd group the same
-        // columns of tile 2p + 1's), then between the two halves, after which
-        // lane group g holds columns 8 (g / 2) + 16 (g % 2) .. + 7 of one row,
-        // of tile 2p in the first register and of tile 2p + 1 in the second.
-        // Each store then writes 16 rows as 64-byte pieces: half the
-        // instructions, and half the pieces, of one 8-byte store per tile.
-        u32x2v pk[2][4];
+        if constexpr (kOutF32) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const f32x4 v = O[u][cb];
-                pk[u][cb] = u32x2v{(uint32_t)(uint16_t)bf16_bits(v[0]) | ((uint32_t)(uint16_t)bf16_bits(v[1]) << 16),
-                                   (uint32_t)(uint16_t)bf16_bits(v[2]) | ((uint32_t)(uint16_t)bf16_bits(v[3]) << 16)};
-            }
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
+                for (int e = 0; e < 2; ++e) {
+                    const f32x4 v = O[u][e];
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                                  __float_as_uint(v[2]), __float_as_uint(v[3])},
+                                                           ro, lane_off[u], soff[2 * p + e], CPOL_NT);
+                }
+        } else {
+            // bf16 (hardware RNE conversion): a lane holds 8 bytes of its
+            // row's 64 (the workgroup's 32 columns).  Two rounds of permlane16
+            // swaps put each row's 64 bytes into the lanes n, 16 + n, 32 + n,
+            // 48 + n: first between the pair's tiles within one column half
+            // (the even lane group then holds 8 columns of tile 2p's row, the
+            // odd group the same columns of tile 2p + 1's), then between the
+            // halves, after which lane group g holds columns 8 (g / 2) +
+            // 16 (g % 2) .. + 7 of one row, of tile 2p in the first register
+            // and of tile 2p + 1 in the second.  Each store then writes 16 rows
+            // as 64-byte pieces: half the instructions, and half the pieces,
+            // of one 8-byte store per tile and half.
             u32x4v half_rows[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const auto s0 = __builtin_amdgcn_permlane16_swap(pk[u][2 * p][0], pk[u][2 * p + 1][0], false, false);
-                const auto s1 = __builtin_amdgcn_permlane16_swap(pk[u][2 * p][1], pk[u][2 * p + 1][1], false, false);
+                const f32x4 a = O[u][0], b = O[u][1];
+                const auto s0 = __builtin_amdgcn_permlane16_swap(bf16x2_bits(a[0], a[1]), bf16x2_bits(b[0], b[1]),
+                                                                 false, false);
+                const auto s1 = __builtin_amdgcn_permlane16_swap(bf16x2_bits(a[2], a[3]), bf16x2_bits(b[2], b[3]),
+                                                                 false, false);
                 half_rows[u] = u32x4v{s0[0], s1[0], s0[1], s1[1]};
             }
             u32x4v r0, r1;
