@@ -610,13 +610,16 @@ gdn_wy_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // The state spine.  One workgroup per (sequence, v-head, 32 dv columns), four
 // waves, one per SIMD (wave w runs on SIMD w):
-//   the loader (0): the workgroup's ring and output-slot traffic into LDS, by
-//     buffer->LDS DMA: in step c, chunk c + 3's ring stage and chunk c + 1's
-//     output slot, each filled two steps before it is read, which covers the
-//     memory latency.  A DMA holds the wave that issues it for about as long
-//     as its kilobyte takes to move, so one wave issuing everything sets the
-//     pace of the chunk: the recurrence waves issue chunk c's Q rows (half
-//     each) at the start of step c, read by the output wave in step c + 1.
+//   the loader (0): the workgroup's memory traffic into LDS, by buffer->LDS
+//     DMA: in step c, chunk c + 3's ring stage and chunk c + 1's output slot,
+//     each filled two steps before it is read, which covers the memory
+//     latency, and chunk c's Q rows, read by the output wave in step c + 1.
+//     A DMA holds the wave that issues it for as long as the compute unit's
+//     memory path takes to accept its lines.  With many workgroups in flight
+//     (Q_SPLIT_GRID or more) and the output stores on that path too, that
+//     makes the loader's DMAs the pace of the step, and the recurrence waves
+//     issue the Q rows instead (half each, at the start of step c); otherwise
+//     the recurrence chain sets the pace and the loader keeps them.
 //   the output wave (1): one chunk behind the recurrence, O = gm (Q h) + PT R
 //     for all 32 columns (PT R = P Delta).
 //   recurrence waves (2, 3): 16 columns each; the fp32 state h lives in MFMA
@@ -831,6 +834,19 @@ __device__ __forceinline__ void issue_out(unsigned char* slot, const LoadOffsets
     const Rsrc rp = make_dma_rsrc(a.pts + ((size_t)(a.slot0 + cc) * a.Hv + a.vh) * SLOT_STRIDE, SLOT_BYTES + 256);
     dma_x6(rp, lds_u32(slot) + OS_P, o.fv, o.fs);
     dma4(rp, slot + OS_GM, o.gmv);
+}
+
+// Workgroups in a launch from which the recurrence waves issue the Q rows.
+constexpr unsigned Q_SPLIT_GRID = 192;
+
+// Chunk cc's Q rows into a Q slot, laid out as K in the ring.
+__device__ __forceinline__ void issue_q(unsigned char* slot, const LoadOffsets& o, const SpineArgs& a, int cc) {
+    const ChunkRows cr = chunk_rows(a.row0, a.len, cc);
+    const uint32_t q_row = (uint32_t)a.Hk * D * 2u;
+    const Rsrc rq = make_dma_rsrc(a.q + (cr.r0 * a.Hk + a.kh) * D, cr.L * q_row);
+    const uint32_t base = lds_u32(slot);
+    dma_x8(rq, base, o.kv, &o.ks[0]);
+    dma_x8(rq, base + 8192, o.kv, &o.ks[8]);
 }
 
 // Half `half` of chunk cc's Q rows (rows 32 half .. + 31) into a Q slot, laid
@@ -1258,7 +1274,9 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const FragOffsets fo = frag_offsets(g, n, half);
     unsigned char* ex = lds + EX_BASE + 2 * half * EX_BYTES;   // this column half's exchange, parity 0
 
-    if (w == 0) {   // the loader: in step c, chunk c + 3's ring stage and chunk c + 1's output slot
+    // uniform over the workgroup
+    const bool q_split = gridDim.x * gridDim.y >= Q_SPLIT_GRID && !(flags & SPINE_NO_OUT);
+    if (w == 0) {   // the loader: in step c, chunk c's Q, chunk c + 3's ring stage and chunk c + 1's output slot
         const LoadOffsets o = load_offsets(lane, Hk, Hv);
         for (int cc = 0; cc < 2 && cc < nc; ++cc) issue_rec(ring, o, a, cc);
         __builtin_amdgcn_s_waitcnt(GDN_VMCNT(0));
@@ -1270,11 +1288,13 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             // stage c % 3 held chunk c, whose ring reads ended in step c - 1 (in
             // the prologue for chunk 0); slot (c + 1) % 3 held chunk c - 2, read
             // in step c - 1
+            // Q slot c % 2 held chunk c - 2, read in step c - 1
+            if (!q_split && c < nc) issue_q(lds + QS_BASE + (c & 1) * QS_BYTES, o, a, c);
             const bool rr = c + 3 < nc, oo = c + 1 < nc;
             if (rr) issue_rec(ring, o, a, c + 3);
             if (oo) issue_out(lds + OS_BASE + ((c + 1) % N_OS) * OS_BYTES, o, a, c + 1);
-            // what was issued before this step (chunk c + 2's stage, chunk c's
-            // slot) lands before the next barrier
+            // chunk c's Q and what was issued before this step (chunk c + 2's
+            // stage, chunk c's slot) land before the next barrier
             if (rr && oo) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_REC + DMA_OUT));
             else if (rr) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_REC));
             else if (oo) __builtin_amdgcn_s_waitcnt(GDN_VMCNT(DMA_OUT));
@@ -1355,22 +1375,22 @@ gdn_spine_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // the walk's own reads
     __builtin_amdgcn_s_waitcnt(0);
     ring_barrier();   // step 0
-    // Step c starts with this wave's half of chunk c's Q rows into Q slot
-    // c % 2 (chunk c - 2's, read by the output wave in step c - 1); the wave
-    // has no other vector-memory operation in the walk, so vmcnt(0) before the
-    // barrier that ends the step is exactly those pieces.
+    // With q_split, step c starts with this wave's half of chunk c's Q rows
+    // into Q slot c % 2 (chunk c - 2's, read by the output wave in step
+    // c - 1); the wave has no other vector-memory operation in the walk, so
+    // vmcnt(0) before the barrier that ends the step is exactly those pieces.
     const LoadOffsets lq = load_offsets(lane, Hk, Hv);
     uint32_t qs[8];   // the SGPR offsets of K pieces 8 half .. 8 half + 7
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         qs[j] = __builtin_amdgcn_readfirstlane((uint32_t)(4 * (8 * half + j)) * (uint32_t)Hk * D * 2u);
     for (int c = 0; c < nc; c += 2) {
-        issue_q_half(lds + QS_BASE, lq.kv, qs, a, c, half);
+        if (q_split) issue_q_half(lds + QS_BASE, lq.kv, qs, a, c, half);
         rec_step(h, oA, oB, ring + ((c + 1) % N_RS) * RS_BYTES, ex, fo, g, lane);
         __builtin_amdgcn_s_waitcnt(GDN_LGKMCNT(15) & GDN_VMCNT(0));
         ring_barrier();
         if (c + 1 >= nc) break;
-        issue_q_half(lds + QS_BASE + QS_BYTES, lq.kv, qs, a, c + 1, half);
+        if (q_split) issue_q_half(lds + QS_BASE + QS_BYTES, lq.kv, qs, a, c + 1, half);
         rec_step(h, oB, oA, ring + ((c + 2) % N_RS) * RS_BYTES, ex + EX_BYTES, fo, g, lane);
         __builtin_amdgcn_s_waitcnt(GDN_LGKMCNT(15) & GDN_VMCNT(0));
         ring_barrier();
