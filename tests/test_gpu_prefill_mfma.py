@@ -9,7 +9,9 @@ Edge cases: sequences of 1, 63, 64, 65 and 130 tokens, empty packed
 sequences, fp32 outputs, in-place states, and 1, 2, 4, 5 and 8 v-heads per
 k-head (the WY kernel runs one wave per v-head in groups of up to four, so 5
 leaves a partial last group).  Bitwise properties: repeated runs,
-a state carried across a chunk-aligned split, and packed vs separate runs.
+a state carried across a chunk-aligned split, packed vs separate runs, and
+the Q rows brought in by either wave (the recurrence waves in a launch of 192
+or more workgroups that writes outputs, the loader otherwise).
 """
 import numpy as np
 import pytest
@@ -184,6 +186,24 @@ def test_packed_equals_separate_bitwise():
         one["cu_seqlens"] = None
         o, h, _ = gpu_prefill(one, 64)
         assert torch.equal(_bits(o[0]), _bits(out[sl])), b
+        assert torch.equal(_bits(h[0]), _bits(hf[b])), b
+
+
+def test_q_rows_from_either_wave_bitwise():
+    """Two dense sequences of 24 v-heads in one call (grid 96 x 2 = 192
+    workgroups: the recurrence waves issue the Q rows) against each sequence
+    alone (96 workgroups: the loader issues them): the same bits."""
+    B, T, Hk, Hv = 2, 64 * 6 + 17, 8, 24
+    inp = synth.prefill_inputs(B, T, Hk, Hv, 128, 128, h0=True, seed=37)
+    say("Q rows by the recurrence waves vs by the loader")
+    out, hf, route = gpu_prefill(inp, 64)
+    assert route.startswith(f"{ROUTE} grid=[{Hv * 4},{B},1]"), route
+    check(inp, out, hf)
+    for b in range(B):
+        one = {k: (v[b : b + 1].contiguous() if torch.is_tensor(v) else v) for k, v in inp.items()}
+        o, h, r1 = gpu_prefill(one, 64)
+        assert r1.startswith(f"{ROUTE} grid=[{Hv * 4},1,1]"), r1
+        assert torch.equal(_bits(o[0]), _bits(out[b])), b
         assert torch.equal(_bits(h[0]), _bits(hf[b])), b
 
 
